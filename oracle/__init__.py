@@ -1,0 +1,176 @@
+"""CPU oracle for the Q8_0 weight-streaming path (ctypes over ``q8_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with the
+HIP library and never imports it.
+
+Every function takes and returns numpy arrays; the arithmetic lives in the C
+file, which cites the passages it follows.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q8_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+           "-Wall", "-shared", "-fPIC"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C, OpenMP); returns the library path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = C.CDLL(_LIB)
+        P = C.c_void_p
+        I64 = C.c_int64
+        L.oracle_set_threads.argtypes = [C.c_int]
+        L.oracle_get_threads.restype = C.c_int
+        L.oracle_half_to_double.argtypes = [C.c_uint16]
+        L.oracle_half_to_double.restype = C.c_double
+        L.oracle_half_from_double.argtypes = [C.c_double]
+        L.oracle_half_from_double.restype = C.c_uint16
+        L.oracle_rhaway.argtypes = [C.c_float]
+        L.oracle_rhaway.restype = C.c_double
+        L.oracle_rhaway_array.argtypes = [P, I64, P]
+        L.oracle_block_scale.argtypes = [C.c_float]
+        L.oracle_block_scale.restype = C.c_uint16
+        L.oracle_quantize_f32.argtypes = [P, I64, I64, P, P]
+        L.oracle_quantize_bf16.argtypes = [P, I64, I64, P, P]
+        L.oracle_w8a16.argtypes = [P, P, I64, I64, I64, P, P, I64, P]
+        L.oracle_block_dots.argtypes = [P, I64, I64, P, I64, P]
+        L.oracle_q8q8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, P]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return lib().oracle_get_threads()
+
+
+def half_to_float(h: int) -> float:
+    return lib().oracle_half_to_double(int(h))
+
+
+def half_from_float(v: float) -> int:
+    return lib().oracle_half_from_double(float(v))
+
+
+def rhaway(t: float) -> float:
+    return lib().oracle_rhaway(float(t))
+
+
+def rhaway_array(t: np.ndarray) -> np.ndarray:
+    t = np.ascontiguousarray(t, dtype=np.float32)
+    out = np.empty(t.shape, dtype=np.int32)
+    lib().oracle_rhaway_array(_p(t), t.size, _p(out))
+    return out
+
+
+def block_scale(amax: float) -> int:
+    return lib().oracle_block_scale(float(amax))
+
+
+def _check_k(k: int) -> None:
+    if k % 32 != 0 or k <= 0:
+        raise ValueError("k must be a positive multiple of 32")
+
+
+def quantize_f32(w: np.ndarray):
+    """fp32 [n][k] -> (codes int8 [n][k], binary16 scale bits uint16 [n][k/32])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    _check_k(k)
+    q = np.empty((n, k), dtype=np.int8)
+    d = np.empty((n, k // 32), dtype=np.uint16)
+    lib().oracle_quantize_f32(_p(w), n, k, _p(q), _p(d))
+    return q, d
+
+
+def quantize_bf16(x: np.ndarray):
+    """bf16 bits [m][k] -> (codes int8 [m][k], binary16 scale bits [m][k/32])."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    m, k = x.shape
+    _check_k(k)
+    q = np.empty((m, k), dtype=np.int8)
+    d = np.empty((m, k // 32), dtype=np.uint16)
+    lib().oracle_quantize_bf16(_p(x), m, k, _p(q), _p(d))
+    return q, d
+
+
+def _rows(rows, n):
+    if rows is None:
+        return None, n
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    if r.size and (r.min() < 0 or r.max() >= n):
+        raise IndexError("row index out of range")
+    return r, r.size
+
+
+def w8a16(wq, wd, x, rows=None) -> np.ndarray:
+    """fp64 y [m][len(rows) or n] = dequantized W (rows) times bf16 x."""
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    wd = np.ascontiguousarray(wd, dtype=np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    n, k = wq.shape
+    m = x.shape[0]
+    assert x.shape[1] == k and wd.shape == (n, k // 32)
+    r, nr = _rows(rows, n)
+    y = np.empty((m, nr), dtype=np.float64)
+    lib().oracle_w8a16(_p(wq), _p(wd), n, k, m, _p(x),
+                       None if r is None else _p(r), nr, _p(y))
+    return y
+
+
+def block_dots(wq, xq) -> np.ndarray:
+    """Exact int32 block sums isum [m][n][k/32]."""
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    n, k = wq.shape
+    m = xq.shape[0]
+    assert xq.shape[1] == k
+    out = np.empty((m, n, k // 32), dtype=np.int32)
+    lib().oracle_block_dots(_p(wq), n, k, _p(xq), m, _p(out))
+    return out
+
+
+def q8q8(wq, wd, xq, xd, rows=None) -> np.ndarray:
+    """fp64 y [m][len(rows) or n] = sum_b wd*xd*isum."""
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    wd = np.ascontiguousarray(wd, dtype=np.uint16)
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    xd = np.ascontiguousarray(xd, dtype=np.uint16)
+    n, k = wq.shape
+    m = xq.shape[0]
+    assert xq.shape[1] == k and wd.shape == (n, k // 32) and xd.shape == (m, k // 32)
+    r, nr = _rows(rows, n)
+    y = np.empty((m, nr), dtype=np.float64)
+    lib().oracle_q8q8(_p(wq), _p(wd), n, k, m, _p(xq), _p(xd),
+                      None if r is None else _p(r), nr, _p(y))
+    return y
