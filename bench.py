@@ -1,0 +1,410 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q8_0 weight-streaming hot path on one MI355X.
+
+Headline (one JSON line on stdout): the batch-1 W8A16 GEMV at the lm_head shape
+[262144 x 1536] -- weights already quantized and resident in HBM, two weight
+copies alternated so no call finds the previous call's bytes in cache -- timed
+over K steps after W warm-up steps.  `value` is algorithmic bytes per call
+(int8 codes + binary16 scales + bf16 x + fp32 y = 428,870,656 B) times K over
+the synchronized wall time of the timed region, in GB/s.  The same line carries
+the roofline of that kernel (HIP-event kernel durations on the launch stream),
+the measured HBM read peak, the CPU oracle timed on the host, and the other
+workloads: the 1536 x 1536 GEMV, the Mimir-shaped decode step (513 GEMVs,
+graph-replayed), the batch 2/4/8 skinny step and the P=256 prefill GEMMs.
+
+Inputs are synthetic and seeded (module ``workloads``).  The pages' own figures
+(338.7 GB/s for a bf16 GEMV of this shape on an RTX 3060; 46.7 tok/s int8
+decode) are other hardware and another precision: context only.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Q8 GEMV HBM GB/s (% of peak) at 1536x262144 b=1; Mimir-shape tok/s"
+HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+INT8_PEAK_TOPS = 5000.0         # MI355X published dense int8 MFMA rate
+Q8_BPW = 1.0625                 # bytes per weight: 1 code + 2/32 scale
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemv_bytes(n: int, k: int, m: int = 1) -> int:
+    """Algorithmic bytes of one call: codes + scales + bf16 activations + fp32 out."""
+    return n * k + n * (k // 32) * 2 + m * k * 2 + m * n * 4
+
+
+def prefill_bytes(n: int, k: int, p: int) -> int:
+    return n * k + n * (k // 32) * 2 + p * k + p * (k // 32) * 2 + p * n * 4
+
+
+def gpu_state() -> dict | None:
+    try:
+        r = subprocess.run(["rocm-smi", "--showtemp", "--showclocks", "--json"],
+                           capture_output=True, text=True, timeout=15)
+        data = json.loads(r.stdout)
+        card = next(iter(data.values()))
+        keep = {}
+        for key, val in card.items():
+            kl = key.lower()
+            if ("temperature" in kl and ("junction" in kl or "edge" in kl or "memory" in kl)) or \
+               kl.startswith("sclk") or kl.startswith("mclk"):
+                keep[key] = val
+        return keep or None
+    except Exception:
+        return None
+
+
+# ------------------------------------------------------------------ device helpers
+
+def to_dev(a, dev):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.uint16)
+    return torch.from_numpy(a).to(dev)
+
+
+def quantize_on_device(q8, w_np, dev):
+    import torch
+    w = to_dev(w_np, dev)
+    wq, wd = q8.quantize_weights(w)
+    torch.cuda.synchronize()
+    del w
+    return wq, wd
+
+
+def time_events(fn, iters: int) -> tuple[float, float]:
+    """(mean per-call kernel time from HIP events on the launch stream, wall s)."""
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(iters):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return float(np.mean(ms)), wall
+
+
+# ------------------------------------------------------------------ workloads
+
+def bench_read_probe(q8, dev, gib: float = 4.0, reps: int = 10) -> dict:
+    import torch
+    nbytes = int(gib * (1 << 30))
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+    sink = q8.probe_read(buf)
+    for _ in range(2):
+        q8.probe_read(buf, sink)
+    ms, _ = time_events(lambda i: q8.probe_read(buf, sink), reps)
+    del buf
+    return {"bytes": nbytes, "ms": ms, "GBps": nbytes / ms / 1e6}
+
+
+def bench_gemv_1536(q8, wl, dev, copies: int = 256, iters: int = 2000) -> dict:
+    """The 1536 x 1536 batch-1 GEMV: rotating 256 weight copies (640 MB) so the
+    figure is HBM-bound, and a single copy (cache-resident), both graph-replayed."""
+    import torch
+    cfg = wl.CONFIGS["gemv_1536x1536_b1"]
+    n, k = cfg["n"], cfg["k"]
+    wq, wd = quantize_on_device(q8, wl.normal_weights(cfg["w_seed"], n, k), dev)
+    x = to_dev(wl.normal_act_bf16(cfg["x_seed"], 1, k)[0], dev)
+    wqs = [wq.clone() for _ in range(copies)]
+    wds = [wd.clone() for _ in range(copies)]
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    out = {}
+    for label, nc in (("rotating", copies), ("single", 1)):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(8):
+                q8.gemv(wqs[i % nc], wds[i % nc], x, out=y)
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        per_graph = 500
+        with torch.cuda.graph(g):
+            for i in range(per_graph):
+                q8.gemv(wqs[i % nc], wds[i % nc], x, out=y)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, iters // per_graph)
+        ms, _ = time_events(lambda i: g.replay(), reps)
+        per_call_us = ms * 1e3 / per_graph
+        out[label] = {"us_per_gemv": per_call_us, "gemv_per_s": 1e6 / per_call_us,
+                      "GBps": gemv_bytes(n, k) / per_call_us / 1e3}
+    return out
+
+
+def load_mimir(q8, wl, dev) -> dict:
+    weights = {}
+    for blk in range(wl.N_BLOCKS):
+        for proj, (_, n, k) in enumerate(wl.BLOCK_SHAPES):
+            weights[(blk, proj)] = quantize_on_device(
+                q8, wl.normal_weights(wl.mimir_weight_seed(blk, proj), n, k), dev)
+    n, k = wl.LM_HEAD_SHAPE
+    weights["lm_head"] = quantize_on_device(q8, wl.normal_weights(wl.LM_HEAD_SEED, n, k), dev)
+    return weights
+
+
+def mimir_step_bytes(wl, m: int) -> int:
+    total = 0
+    for item in wl.mimir_step_order():
+        if item[0] == "lm_head":
+            n, k = wl.LM_HEAD_SHAPE
+        else:
+            _, n, k = wl.BLOCK_SHAPES[item[1]]
+        total += gemv_bytes(n, k, m)
+    return total
+
+
+def bench_mimir(q8, wl, dev, weights, m: int, replays: int = 20) -> dict:
+    """One decode token (m streams): 513 skinny products in recurrence order,
+    captured once into a graph and replayed; eager replay of the same launches
+    is timed too."""
+    import torch
+    xs = {k: [to_dev(wl.normal_act_bf16(9000 + 16 * m + 2 * i + (k == wl.INTER), m, k), dev)
+              for i in range(8)] for k in (wl.HIDDEN, wl.INTER)}
+    ys = {n: torch.empty((m, n), dtype=torch.float32, device=dev)
+          for n in {s[1] for s in wl.BLOCK_SHAPES} | {wl.LM_HEAD_SHAPE[0]}}
+    order = wl.mimir_step_order()
+
+    def step():
+        for i, item in enumerate(order):
+            if item[0] == "lm_head":
+                wq, wd = weights["lm_head"]
+                x = xs[wl.HIDDEN][0]
+            else:
+                wq, wd = weights[item]
+                x = xs[wq.shape[1]][i % 8]
+            q8.gemm_skinny(wq, wd, x, out=ys[wq.shape[0]])
+
+    step()
+    torch.cuda.synchronize()
+    eager_ms, _ = time_events(lambda i: step(), 3)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    ms, _ = time_events(lambda i: g.replay(), replays)
+    nbytes = mimir_step_bytes(wl, m)
+    return {"m": m, "ms_per_step": ms, "tok_per_s": m * 1e3 / ms, "eager_ms_per_step": eager_ms,
+            "eager_tok_per_s": m * 1e3 / eager_ms, "bytes_per_step": nbytes,
+            "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": m * HBM_PEAK_GBPS * 1e6 / nbytes}
+
+
+def bench_prefill(q8, wl, dev, weights, reps: int = 50) -> dict:
+    """P = 256: qkv and gate_up on [256, 1536], down on [256, 4096] (block 0
+    weights); activations quantized by q8_quantize_act (timed separately)."""
+    import torch
+    cfg = wl.CONFIGS["prefill_p256"]
+    xa = to_dev(wl.prefill_act_bf16(cfg["xa_seed"], 256, wl.HIDDEN), dev)
+    xb = to_dev(wl.prefill_act_bf16(cfg["xb_seed"], 256, wl.INTER), dev)
+    xaq, xad = q8.quantize_act(xa)
+    xbq, xbd = q8.quantize_act(xb)
+    gemms = []
+    for proj, (name, n, k) in enumerate(wl.BLOCK_SHAPES):
+        if name == "o":
+            continue
+        gemms.append((name, n, k, weights[(0, proj)],
+                      (xbq, xbd) if k == wl.INTER else (xaq, xad),
+                      torch.empty((256, n), dtype=torch.float32, device=dev)))
+
+    def run(i):
+        for name, n, k, (wq, wd), (xq, xd), y in gemms:
+            q8.gemm_prefill(wq, wd, xq, xd, out=y)
+
+    run(0)
+    ms, _ = time_events(run, reps)
+    ops = sum(2 * 256 * n * k for _, n, k, *_ in gemms)
+    per = {}
+    for name, n, k, (wq, wd), (xq, xd), y in gemms:
+        gms, _ = time_events(lambda i: q8.gemm_prefill(wq, wd, xq, xd, out=y), reps)
+        per[name] = {"us": gms * 1e3, "TOPS": 2 * 256 * n * k / gms / 1e9}
+    qms, _ = time_events(lambda i: (q8.quantize_act(xa, out=(xaq, xad)),
+                                    q8.quantize_act(xb, out=(xbq, xbd))), reps)
+    nbytes = sum(prefill_bytes(n, k, 256) for _, n, k, *_ in gemms)
+    tops = ops / ms / 1e9
+    return {"ms_three_gemms": ms, "int_ops": ops, "TOPS": tops,
+            "frac_int8_peak": tops / INT8_PEAK_TOPS, "bytes": nbytes,
+            "per_gemm": per, "quantize_act_us": qms * 1e3}
+
+
+def cpu_baseline(oracle, wl, oq, od, x, seconds: float = 10.0) -> dict:
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    oracle.set_threads(threads)
+    n, k = oq.shape
+    nbytes = gemv_bytes(n, k)
+    times = []
+    t_end = time.perf_counter() + seconds
+    while not times or (time.perf_counter() < t_end and len(times) < 20):
+        t0 = time.perf_counter()
+        oracle.w8a16(oq, od, x)
+        times.append(time.perf_counter() - t0)
+    best = min(times)
+    return {"value": nbytes / best / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle W8A16 GEMV over all {n} x {k} rows of the lm_head workload, "
+                      f"{len(times)} runs, best {best * 1e3:.1f} ms",
+            "host_cpus_visible": os.cpu_count()}
+
+
+# ------------------------------------------------------------------ main
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--metric-only", action="store_true",
+                    help="time only the headline GEMV (no other workloads, no CPU baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the weight-streaming products shard by output "
+              "rows with no collective, so a multi-GPU figure is N independent copies of this "
+              "one; run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import int8_weight_streaming_amd as q8
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    q8.load_library()
+    state_before = gpu_state()
+
+    # ---- headline: lm_head-shaped GEMV, batch 1
+    cfg = wl.CONFIGS["lm_head_gemv_262144x1536_b1"]
+    n, k = cfg["n"], cfg["k"]
+    log(f"generating lm_head weights {n}x{k}")
+    w_np = wl.normal_weights(cfg["w_seed"], n, k)
+    x_np = wl.rms_unit_act_bf16(cfg["x_seed"], k)
+    wq, wd = quantize_on_device(q8, w_np, dev)
+    copies = [(wq, wd), (wq.clone(), wd.clone())]
+    x = to_dev(x_np[0], dev)
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    nbytes = gemv_bytes(n, k)
+
+    def call(i):
+        cq, cd = copies[i & 1]
+        q8.gemv(cq, cd, x, out=y)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    kern_ms, wall = time_events(call, args.steps)
+    ms_per_step = wall * 1e3 / args.steps
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    log(f"lm_head gemv: {kern_ms * 1e3:.2f} us/kernel, {achieved:.1f} GB/s kernel, {value:.1f} GB/s wall")
+
+    # sampled parity on the timed output
+    import oracle
+    oracle.set_threads(max(1, min(16, len(os.sched_getaffinity(0)))))
+    oq, od = oracle.quantize_f32(w_np)
+    del w_np
+    rows = np.random.Generator(np.random.PCG64(77)).choice(n, size=4096, replace=False)
+    y_host = y.cpu().numpy()[rows].astype(np.float64)
+    y_ref = oracle.w8a16(oq, od, x_np, rows=rows)[0]
+    parity = {"rows_checked": int(rows.size),
+              "max_abs": float(np.max(np.abs(y_host - y_ref))),
+              "rel_l2": float(np.linalg.norm(y_host - y_ref) / np.linalg.norm(y_ref))}
+    parity["ok"] = parity["max_abs"] <= 2e-3 and parity["rel_l2"] <= 1e-5
+
+    extras = {}
+    probe = bench_read_probe(q8, dev)
+    log(f"read probe: {probe['GBps']:.1f} GB/s")
+    extras["read_probe"] = probe
+    measured_peak = probe["GBps"]
+
+    if not args.metric_only:
+        log("gemv 1536x1536")
+        extras["gemv_1536x1536_b1"] = bench_gemv_1536(q8, wl, dev)
+        log("loading Mimir weight set (32 blocks + lm_head)")
+        weights = load_mimir(q8, wl, dev)
+        for m in (1, 2, 4, 8):
+            log(f"mimir step m={m}")
+            extras[f"mimir_step_b{m}"] = bench_mimir(q8, wl, dev, weights, m)
+        log("prefill P=256")
+        extras["prefill_p256"] = bench_prefill(q8, wl, dev, weights)
+        del weights
+
+    cpu = None
+    if not args.metric_only and not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(oracle, wl, oq, od, x_np)
+
+    torch.cuda.synchronize()
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic_lm_head_gemv.json")
+    if os.path.exists(tfile):
+        try:
+            import hashlib
+            t = json.load(open(tfile))
+            src = open(os.path.join(ROOT, "int8_weight_streaming_amd", "csrc", "q8_skinny.hip"), "rb").read()
+            if t.get("source_sha256") == hashlib.sha256(src).hexdigest():
+                traffic = t.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 weights x bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) weights, unit-RMS N(0,1) bf16 activation)",
+        "config": {"workload": "lm_head_gemv_262144x1536_b1", "n": n, "k": k, "batch": 1,
+                   "format": "Q8_0: 32 int8 codes + binary16 scale per block",
+                   "bytes_per_call": nbytes, "weight_copies_alternated": 2},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel_us": round(kern_ms * 1e3, 3),
+                     "frac_of_measured_read_peak": round(achieved / measured_peak, 4)},
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+        "extras": extras,
+        "gpu_state": {"before": state_before, "after": gpu_state()},
+        "context": {"pages_gemv_bf16_rtx3060_GBps": 338.7, "pages_int8_decode_rtx3060_tok_s": 46.7,
+                    "pages_q8_decode_zen5_1t_ms_per_tok": 7.7, "pages_q8_prefill_slope_zen5_ms_per_tok": 0.346},
+    }
+    if "mimir_step_b1" in extras:
+        result["mimir_tok_s"] = round(extras["mimir_step_b1"]["tok_per_s"], 1)
+    print(json.dumps(result), flush=True)
+    return 0 if parity["ok"] else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

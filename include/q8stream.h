@@ -1,0 +1,148 @@
+/*
+ * q8stream.h -- C ABI of the Q8_0 weight-streaming library for MI355X (gfx950).
+ *
+ * The library computes the int8 weight-streaming hot path of LLM decode and
+ * prefill: block quantization of weights and activations, the batch-1..8
+ * matrix-vector / skinny products over int8 weights, and the Q8 x Q8 prefill
+ * product.  Every call is a hand-written HIP kernel enqueued on the caller's
+ * stream.
+ *
+ * Format (Q8_0) [fak MODEL-BASELINE-RESULTS, ACT 3, "How it was closed",
+ * item 1]: a row of K values (K % 32 == 0) is cut into K/32 blocks of 32
+ * consecutive elements along the reduction axis.  Each block stores 32 int8
+ * codes and one scale d = maxabs / 127.  The scale is stored as IEEE binary16
+ * (2 bytes, so 34 bytes per 32 weights = 1.0625 B/weight, the page's "~1.06
+ * B/weight").  d is the fp32 quotient maxabs / 127 rounded to binary16 (nearest,
+ * ties to even).  Codes are clamp(round_half_away(v / d), -127, 127), the
+ * quotient being the correctly rounded fp32 division by the STORED scale; a block
+ * whose stored scale is zero has all-zero codes [ACT 4, "Correctness": rounding
+ * equal to math.Round, never add-0.5-and-truncate].
+ *
+ * Conventions shared by every call:
+ *  - Pointers are device pointers on the current HIP device.  bf16 and binary16
+ *    values travel as uint16_t bit patterns.  Arrays are dense and row-major:
+ *      int8 codes  [rows][K]     (row pitch K bytes)
+ *      scales      [rows][K/32]  (row pitch K/16 bytes)
+ *      bf16 values [rows][K]     (row pitch 2K bytes)
+ *      fp32 output [m][N]        (row pitch 4N bytes)
+ *  - Every pointer passed for a non-empty call must be 16-byte aligned.
+ *  - Ownership: the caller allocates and frees every buffer.  The library never
+ *    allocates, frees or caches device memory and keeps no per-call state, so
+ *    calls may be made from several host threads and may be captured into a
+ *    HIP graph.  Outputs must not alias inputs.
+ *  - Asynchrony: a call validates its arguments, enqueues kernels on `stream`
+ *    (NULL = the current device's null stream) and returns.  Results are valid
+ *    once the stream has been synchronized.  Calls never synchronize.
+ *  - Errors: arguments are checked on the host before any HIP call; on a
+ *    validation error nothing is enqueued and no output is touched.  A failed
+ *    launch returns Q8_ERR_HIP (the HIP error code is kept per host thread, see
+ *    q8_last_hip_error()).  Faults inside kernels surface, as in HIP, at the next
+ *    synchronization.
+ *  - Empty calls: a zero row count (n, m or p == 0) is a valid no-op that
+ *    returns Q8_OK without touching any pointer.  K must be a positive multiple
+ *    of 32.
+ *  - Inputs must be finite.  Non-finite inputs give unspecified results.
+ *  - Determinism: identical inputs and shapes give bitwise identical outputs on
+ *    every call and on graph replay (fixed reduction order, no atomics).
+ */
+#ifndef Q8STREAM_H
+#define Q8STREAM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q8_ABI_VERSION 1
+
+/* Largest batch of the decode products. */
+#define Q8_MAX_BATCH 8
+
+typedef enum {
+    Q8_OK = 0,
+    Q8_ERR_NULL = 1,   /* a required pointer is NULL                              */
+    Q8_ERR_SHAPE = 2,  /* negative extent, K < 32, K % 32 != 0, size overflow     */
+    Q8_ERR_BATCH = 3,  /* m outside [0, Q8_MAX_BATCH] for gemv / skinny           */
+    Q8_ERR_ALIGN = 4,  /* a pointer is not 16-byte aligned                        */
+    Q8_ERR_ENUM = 5,   /* unknown q8_act, or xd given (or missing) against act    */
+    Q8_ERR_DEVICE = 6, /* no HIP device, device is not gfx950, or the stream
+                          belongs to another device than the current one          */
+    Q8_ERR_HIP = 7     /* a HIP launch failed; see q8_last_hip_error()            */
+} q8_status;
+
+typedef enum {
+    Q8_ACT_BF16 = 0,   /* activations are bf16 [m][K]: W8A16                      */
+    Q8_ACT_Q8 = 1      /* activations are Q8_0: int8 codes [m][K] + binary16 [m][K/32] */
+} q8_act;
+
+/* Version of this ABI (Q8_ABI_VERSION). */
+int q8_abi_version(void);
+
+/* Static, NUL-terminated name of a status code ("Q8_OK", ...); "unknown" for
+ * values outside the enum. */
+const char* q8_status_str(int status);
+
+/* The hipError_t behind the most recent Q8_ERR_HIP or Q8_ERR_DEVICE returned
+ * on this host thread; 0 when that failure was not a HIP error (wrong
+ * architecture, stream of another device) or when no such failure happened. */
+int q8_last_hip_error(void);
+
+/* Quantize fp32 weights W [n][k] into codes wq [n][k] and binary16 scales
+ * wd [n][k/32], following the Q8_0 rule above [fak MODEL-BASELINE-RESULTS,
+ * ACT 3 item 1; ACT 4 "Correctness"].  Offline work, done once per weight. */
+q8_status q8_quantize_weights(const float* w, int64_t n, int64_t k,
+                              int8_t* wq, uint16_t* wd, hipStream_t stream);
+
+/* Quantize bf16 activations X [m][k] into codes xq [m][k] and binary16 scales
+ * xd [m][k/32] with the same rule [fak MODEL-BASELINE-RESULTS, ACT 5 "What
+ * moved" item 3: the round-half-away activation quantizer, exact on zeros,
+ * denormals and exact halves].  Any m >= 0. */
+q8_status q8_quantize_act(const uint16_t* x, int64_t m, int64_t k,
+                          int8_t* xq, uint16_t* xd, hipStream_t stream);
+
+/* Batch-1 product y[n] = sum_b d[n][b] * sum_{i<32} q[n][32b+i] * x[32b+i],
+ * fp32 accumulation [Frigg README, "The machine": at batch 1 every decode GEMM
+ * is this matrix-vector shape, and its speed is bytes / bandwidth].
+ *   act == Q8_ACT_BF16: x is bf16 [k], xd must be NULL.
+ *   act == Q8_ACT_Q8:   x is int8 codes [k], xd is binary16 [k/32]; each block
+ *                       contributes wd * xd * (exact int32 sum of code products)
+ *                       [fak MODEL-BASELINE-RESULTS, ACT 3 item 3].
+ * y is fp32 [n].  Same as q8_gemm_skinny with m = 1. */
+q8_status q8_gemv(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k,
+                  int act, const void* x, const uint16_t* xd,
+                  float* y, hipStream_t stream);
+
+/* Skinny product for m = 0..8 activation rows, reading every weight byte once
+ * for all rows [Frigg README, Finding 8: looping the GEMV re-reads the weights
+ * per row; a batched kernel costs nearly the same at every batch size].
+ * x is bf16 [m][k] (act BF16) or int8 [m][k] with xd [m][k/32] (act Q8);
+ * y is fp32 [m][n]. */
+q8_status q8_gemm_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k,
+                         int64_t m, int act, const void* x, const uint16_t* xd,
+                         float* y, hipStream_t stream);
+
+/* Q8 x Q8 prefill product for p activation rows (any p >= 0):
+ * y[t][j] = sum_b wd[j][b] * xd[t][b] * sum_{i<32} wq[j][32b+i] * xq[t][32b+i],
+ * the int32 block sums taken on the int8 matrix cores, each block folded into an
+ * fp32 accumulator with its two scales [fak MODEL-BASELINE-RESULTS, ACT 4,
+ * "How the GEMM was closed": deferred per-block reduction, register-blocked
+ * output tile].  y is fp32 [p][n]. */
+q8_status q8_gemm_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k,
+                          int64_t p, const int8_t* xq, const uint16_t* xd,
+                          float* y, hipStream_t stream);
+
+/* The exact int32 block sums of the Q8 x Q8 product, exported so that they can
+ * be compared bit for bit: isum[t][j][b] = sum_{i<32} wq[j][32b+i] * xq[t][32b+i]
+ * for t < m (m = 0..8), j < n, b < k/32 [fak MODEL-BASELINE-RESULTS, ACT 3
+ * item 3: signed x signed int8 block dot].  Uses the same block-dot routine as
+ * the Q8-activation decode products.  isum is int32 [m][n][k/32]. */
+q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m,
+                        const int8_t* xq, int32_t* isum, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8STREAM_H */

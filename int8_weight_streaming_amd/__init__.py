@@ -1,0 +1,246 @@
+"""q8stream: Q8_0 int8 weight streaming on MI355X (gfx950) -- Python binding.
+
+A thin ctypes layer over ``libq8stream.so`` (the C ABI in ``include/q8stream.h``).
+It only checks tensor dtypes/devices/shapes, allocates outputs with
+``torch.empty`` and passes raw pointers plus the current torch stream; every
+step of the computation runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or the device is not a gfx950, calls raise.
+
+Names mirror the C entry points:
+
+    quantize_weights(w)            fp32 [n][k]            -> (wq int8 [n][k], wd uint16 [n][k/32])
+    quantize_act(x)                bf16 [m][k]            -> (xq int8 [m][k], xd uint16 [m][k/32])
+    gemv(wq, wd, x, xd=None)       x bf16 [k] or int8 [k] -> y fp32 [n]
+    gemm_skinny(wq, wd, x, xd=None) x [m][k], m <= 8      -> y fp32 [m][n]
+    gemm_prefill(wq, wd, xq, xd)   xq int8 [p][k]         -> y fp32 [p][n]
+    block_dots(wq, xq)             xq int8 [m][k]         -> isum int32 [m][n][k/32]
+
+Binary16 scales travel as torch.uint16 tensors holding the bit patterns
+(``wd.view(torch.float16)`` gives the values).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq8stream.so")
+
+Q8_OK = 0
+Q8_ACT_BF16 = 0
+Q8_ACT_Q8 = 1
+MAX_BATCH = 8
+
+EXPORTED = (
+    "q8_abi_version", "q8_status_str", "q8_last_hip_error",
+    "q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
+    "q8_gemm_prefill", "q8_block_dots",
+)
+PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words")
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str, hip_error: int):
+        super().__init__(f"{fn} failed: {text} (status {status}, hip error {hip_error})")
+        self.status = status
+        self.hip_error = hip_error
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> C.CDLL:
+    """Load the in-tree library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with int8_weight_streaming_amd/build.py")
+    L = C.CDLL(path)
+    P, I64, I = C.c_void_p, C.c_int64, C.c_int
+    L.q8_abi_version.restype = I
+    L.q8_status_str.argtypes = [I]
+    L.q8_status_str.restype = C.c_char_p
+    L.q8_last_hip_error.restype = I
+    L.q8_quantize_weights.argtypes = [P, I64, I64, P, P, P]
+    L.q8_quantize_act.argtypes = [P, I64, I64, P, P, P]
+    L.q8_gemv.argtypes = [P, P, I64, I64, I, P, P, P, P]
+    L.q8_gemm_skinny.argtypes = [P, P, I64, I64, I64, I, P, P, P, P]
+    L.q8_gemm_prefill.argtypes = [P, P, I64, I64, I64, P, P, P, P]
+    L.q8_block_dots.argtypes = [P, I64, I64, I64, P, P, P]
+    L.q8_probe_read.argtypes = [P, I64, P, P]
+    L.q8_probe_read.restype = I
+    L.q8_probe_sink_words.restype = I64
+    for name in ("q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
+                 "q8_gemm_prefill", "q8_block_dots"):
+        getattr(L, name).restype = I
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return load_library().q8_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != Q8_OK:
+        L = load_library()
+        raise Q8Error(fn, status, status_str(status), L.q8_last_hip_error())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _as_bits16(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.uint16)
+    return t
+
+
+# ------------------------------------------------------------------ quantizers
+
+def quantize_weights(w: torch.Tensor, out=None):
+    """fp32 [n][k] -> (codes int8 [n][k], binary16 scale bits uint16 [n][k/32])."""
+    _need(w, "w", torch.float32, 2)
+    n, k = w.shape
+    if out is None:
+        wq = torch.empty((n, k), dtype=torch.int8, device=w.device)
+        wd = torch.empty((n, k // 32), dtype=torch.uint16, device=w.device)
+    else:
+        wq, wd = out
+    _check("q8_quantize_weights", load_library().q8_quantize_weights(
+        _ptr(w), n, k, _ptr(wq), _ptr(wd), _stream()))
+    return wq, wd
+
+
+def quantize_act(x: torch.Tensor, out=None):
+    """bf16 [m][k] (torch.bfloat16 or uint16 bits) -> (int8 [m][k], uint16 [m][k/32])."""
+    x = _as_bits16(x)
+    _need(x, "x", torch.uint16, 2)
+    m, k = x.shape
+    if out is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+        xd = torch.empty((m, k // 32), dtype=torch.uint16, device=x.device)
+    else:
+        xq, xd = out
+    _check("q8_quantize_act", load_library().q8_quantize_act(
+        _ptr(x), m, k, _ptr(xq), _ptr(xd), _stream()))
+    return xq, xd
+
+
+# ------------------------------------------------------------------ products
+
+def _weights(wq, wd):
+    _need(wq, "wq", torch.int8, 2)
+    wd = _as_bits16(wd)
+    _need(wd, "wd", torch.uint16, 2)
+    n, k = wq.shape
+    if tuple(wd.shape) != (n, k // 32):
+        raise ValueError(f"wd must be [{n}][{k // 32}], got {tuple(wd.shape)}")
+    return wd, n, k
+
+
+def gemm_skinny(wq, wd, x, xd=None, out=None):
+    """y fp32 [m][n] for m = x.shape[0] <= 8; x bf16 [m][k] or int8 codes with xd."""
+    wd, n, k = _weights(wq, wd)
+    if xd is None:
+        x = _as_bits16(x)
+        _need(x, "x", torch.uint16, 2)
+        act = Q8_ACT_BF16
+    else:
+        _need(x, "x", torch.int8, 2)
+        xd = _as_bits16(xd)
+        _need(xd, "xd", torch.uint16, 2)
+        if tuple(xd.shape) != (x.shape[0], k // 32):
+            raise ValueError("xd must be [m][k/32]")
+        act = Q8_ACT_Q8
+    m = x.shape[0]
+    if x.shape[1] != k:
+        raise ValueError(f"x must have {k} columns, got {x.shape[1]}")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=wq.device)
+    _check("q8_gemm_skinny", load_library().q8_gemm_skinny(
+        _ptr(wq), _ptr(wd), n, k, m, act, _ptr(x), _ptr(xd), _ptr(y), _stream()))
+    return y
+
+
+def gemv(wq, wd, x, xd=None, out=None):
+    """y fp32 [n] from one activation vector x [k] (bf16, or int8 codes with xd [k/32])."""
+    wd, n, k = _weights(wq, wd)
+    if xd is None:
+        x = _as_bits16(x)
+        _need(x, "x", torch.uint16, 1)
+        act = Q8_ACT_BF16
+    else:
+        _need(x, "x", torch.int8, 1)
+        xd = _as_bits16(xd)
+        _need(xd, "xd", torch.uint16, 1)
+        act = Q8_ACT_Q8
+    if x.shape[0] != k:
+        raise ValueError(f"x must have {k} elements, got {x.shape[0]}")
+    y = out if out is not None else torch.empty((n,), dtype=torch.float32, device=wq.device)
+    _check("q8_gemv", load_library().q8_gemv(
+        _ptr(wq), _ptr(wd), n, k, act, _ptr(x), _ptr(xd), _ptr(y), _stream()))
+    return y
+
+
+def gemm_prefill(wq, wd, xq, xd, out=None):
+    """y fp32 [p][n] = Q8 x Q8 product of p activation rows."""
+    wd, n, k = _weights(wq, wd)
+    _need(xq, "xq", torch.int8, 2)
+    xd = _as_bits16(xd)
+    _need(xd, "xd", torch.uint16, 2)
+    p = xq.shape[0]
+    if xq.shape[1] != k or tuple(xd.shape) != (p, k // 32):
+        raise ValueError("xq must be [p][k] and xd [p][k/32]")
+    y = out if out is not None else torch.empty((p, n), dtype=torch.float32, device=wq.device)
+    _check("q8_gemm_prefill", load_library().q8_gemm_prefill(
+        _ptr(wq), _ptr(wd), n, k, p, _ptr(xq), _ptr(xd), _ptr(y), _stream()))
+    return y
+
+
+def block_dots(wq, xq, out=None):
+    """Exact int32 block sums isum [m][n][k/32] (m <= 8)."""
+    _need(wq, "wq", torch.int8, 2)
+    _need(xq, "xq", torch.int8, 2)
+    n, k = wq.shape
+    m = xq.shape[0]
+    if xq.shape[1] != k:
+        raise ValueError("xq must be [m][k]")
+    isum = out if out is not None else torch.empty((m, n, k // 32), dtype=torch.int32, device=wq.device)
+    _check("q8_block_dots", load_library().q8_block_dots(
+        _ptr(wq), n, k, m, _ptr(xq), _ptr(isum), _stream()))
+    return isum
+
+
+# ------------------------------------------------------------------ measurement utility
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Stream every byte of `buf` (read-only) with the library's HBM read probe."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    L = load_library()
+    if sink is None:
+        sink = torch.empty((max(1, L.q8_probe_sink_words()),), dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check("q8_probe_read", L.q8_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream()))
+    return sink

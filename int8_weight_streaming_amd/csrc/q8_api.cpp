@@ -1,0 +1,207 @@
+// q8_api.cpp -- the extern "C" boundary of q8stream.
+//
+// Every entry point first checks its arguments without touching HIP (so a
+// rejected call enqueues nothing and leaves every output untouched), then checks
+// the device (a gfx950 device that owns the stream), then hands the validated
+// arguments to the kernel launchers.
+#include "q8stream.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "q8_internal.hpp"
+
+namespace {
+
+thread_local int t_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+int g_dev_state[kMaxDevices];          // 0 unknown, 1 gfx950, -1 unsupported
+q8::DeviceInfo g_dev_info[kMaxDevices];
+
+constexpr int64_t kMaxExtent = (int64_t)1 << 31;   // per-dimension limit
+constexpr int64_t kMaxElems = (int64_t)1 << 46;    // n * k limit (64 TiB of codes)
+constexpr int64_t kMaxPrefillRows = (int64_t)65535 * 64;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+q8_status check_k(int64_t k) {
+    if (k < 32 || k % 32 != 0 || k >= kMaxExtent) return Q8_ERR_SHAPE;
+    return Q8_OK;
+}
+
+q8_status check_rows(int64_t rows, int64_t k) {
+    if (rows < 0 || rows >= kMaxExtent) return Q8_ERR_SHAPE;
+    if (rows > 0 && rows > kMaxElems / k) return Q8_ERR_SHAPE;
+    return Q8_OK;
+}
+
+q8_status hip_fail(hipError_t e) {
+    t_last_hip_error = (int)e;
+    return Q8_ERR_HIP;
+}
+
+// The device that will run the call: the current device, which must be a gfx950
+// and must own `stream`.
+q8_status device_for(hipStream_t stream, const q8::DeviceInfo** info) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        t_last_hip_error = (int)e;
+        return Q8_ERR_DEVICE;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        if (g_dev_state[dev] == 0) {
+            hipDeviceProp_t prop;
+            e = hipGetDeviceProperties(&prop, dev);
+            if (e != hipSuccess) {
+                t_last_hip_error = (int)e;
+                return Q8_ERR_DEVICE;
+            }
+            const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                            (prop.gcnArchName[6] == 0 || prop.gcnArchName[6] == ':');
+            g_dev_state[dev] = ok ? 1 : -1;
+            g_dev_info[dev].cu_count = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+        }
+        if (g_dev_state[dev] != 1) {
+            t_last_hip_error = 0;
+            return Q8_ERR_DEVICE;
+        }
+    }
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) {
+            t_last_hip_error = (int)e;
+            return Q8_ERR_DEVICE;
+        }
+        if ((int)sdev != dev) {
+            t_last_hip_error = 0;
+            return Q8_ERR_DEVICE;
+        }
+    }
+    *info = &g_dev_info[dev];
+    return Q8_OK;
+}
+
+#define Q8_TRY(expr)                       \
+    do {                                   \
+        const q8_status st_ = (expr);      \
+        if (st_ != Q8_OK) return st_;      \
+    } while (0)
+
+q8_status finish(hipError_t e) {
+    if (e != hipSuccess) return hip_fail(e);
+    return Q8_OK;
+}
+
+q8_status check_act(int act, const void* xd) {
+    if (act != Q8_ACT_BF16 && act != Q8_ACT_Q8) return Q8_ERR_ENUM;
+    if (act == Q8_ACT_BF16 && xd != nullptr) return Q8_ERR_ENUM;
+    if (act == Q8_ACT_Q8 && xd == nullptr) return Q8_ERR_ENUM;
+    return Q8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q8_abi_version(void) { return Q8_ABI_VERSION; }
+
+const char* q8_status_str(int status) {
+    switch (status) {
+        case Q8_OK: return "Q8_OK";
+        case Q8_ERR_NULL: return "Q8_ERR_NULL";
+        case Q8_ERR_SHAPE: return "Q8_ERR_SHAPE";
+        case Q8_ERR_BATCH: return "Q8_ERR_BATCH";
+        case Q8_ERR_ALIGN: return "Q8_ERR_ALIGN";
+        case Q8_ERR_ENUM: return "Q8_ERR_ENUM";
+        case Q8_ERR_DEVICE: return "Q8_ERR_DEVICE";
+        case Q8_ERR_HIP: return "Q8_ERR_HIP";
+        default: return "unknown";
+    }
+}
+
+int q8_last_hip_error(void) { return t_last_hip_error; }
+
+q8_status q8_quantize_weights(const float* w, int64_t n, int64_t k, int8_t* wq, uint16_t* wd,
+                              hipStream_t stream) {
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(n, k));
+    if (n == 0) return Q8_OK;
+    if (!w || !wq || !wd) return Q8_ERR_NULL;
+    if (!aligned16(w) || !aligned16(wq) || !aligned16(wd)) return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_quantize_f32(w, n * (k / 32), wq, wd, *dev, stream));
+}
+
+q8_status q8_quantize_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd,
+                          hipStream_t stream) {
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(m, k));
+    if (m == 0) return Q8_OK;
+    if (!x || !xq || !xd) return Q8_ERR_NULL;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(xd)) return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_quantize_bf16(x, m * (k / 32), xq, xd, *dev, stream));
+}
+
+q8_status q8_gemm_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t m,
+                         int act, const void* x, const uint16_t* xd, float* y,
+                         hipStream_t stream) {
+    Q8_TRY(check_act(act, xd));
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(n, k));
+    if (m < 0 || m > Q8_MAX_BATCH) return Q8_ERR_BATCH;
+    if (n == 0 || m == 0) return Q8_OK;
+    if (!wq || !wd || !x || !y) return Q8_ERR_NULL;
+    if (!aligned16(wq) || !aligned16(wd) || !aligned16(x) || !aligned16(y) ||
+        (xd && !aligned16(xd)))
+        return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_skinny(wq, wd, n, k, (int)m, act, x, xd, y, *dev, stream));
+}
+
+q8_status q8_gemv(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int act,
+                  const void* x, const uint16_t* xd, float* y, hipStream_t stream) {
+    return q8_gemm_skinny(wq, wd, n, k, 1, act, x, xd, y, stream);
+}
+
+q8_status q8_gemm_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t p,
+                          const int8_t* xq, const uint16_t* xd, float* y, hipStream_t stream) {
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(n, k));
+    Q8_TRY(check_rows(p, k));
+    if (p > kMaxPrefillRows) return Q8_ERR_SHAPE;
+    if (n == 0 || p == 0) return Q8_OK;
+    if (!wq || !wd || !xq || !xd || !y) return Q8_ERR_NULL;
+    if (!aligned16(wq) || !aligned16(wd) || !aligned16(xq) || !aligned16(xd) || !aligned16(y))
+        return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_prefill(wq, wd, n, k, p, xq, xd, y, *dev, stream));
+}
+
+q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m, const int8_t* xq,
+                        int32_t* isum, hipStream_t stream) {
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(n, k));
+    if (m < 0 || m > Q8_MAX_BATCH) return Q8_ERR_BATCH;
+    if (n == 0 || m == 0) return Q8_OK;
+    if (!wq || !xq || !isum) return Q8_ERR_NULL;
+    if (!aligned16(wq) || !aligned16(xq) || !aligned16(isum)) return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_block_dots(wq, n, k, (int)m, xq, isum, *dev, stream));
+}
+
+}  // extern "C"

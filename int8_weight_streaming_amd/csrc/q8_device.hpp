@@ -1,0 +1,103 @@
+// q8_device.hpp -- device-side building blocks shared by the q8stream kernels.
+//
+// Everything here is gfx950 (CDNA4) code: wave64, DPP row operations, the
+// packed bf16 dot (v_dot2_f32_bf16), the signed int8 dot (v_dot4_i32_i8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// Q8_0 block scale from the block's largest magnitude: the fp32 quotient
+// amax / 127 (IEEE division, correctly rounded) rounded to binary16 with the
+// hardware's round-to-nearest-even conversion
+// [fak MODEL-BASELINE-RESULTS, ACT 3, "How it was closed", item 1: d = maxabs/127].
+__device__ __forceinline__ uint16_t block_scale_bits(float amax) {
+    const float d = amax / 127.0f;
+    return __builtin_bit_cast(uint16_t, (_Float16)d);
+}
+
+// One code: round half away from zero of the correctly rounded fp32 quotient
+// v / s by the stored scale, clamped to [-127, 127]; zero scale gives zero
+// [fak MODEL-BASELINE-RESULTS, ACT 4, "Correctness": math.Round semantics,
+// never add-0.5-and-truncate].  roundf() is half-away-from-zero.
+__device__ __forceinline__ int block_code(float v, float s) {
+    if (s == 0.0f) return 0;
+    float r = roundf(v / s);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// ---------------------------------------------------------------- conversions
+
+// Four int8 codes (one dword) -> two dwords of packed bf16 pairs.  Codes are
+// small integers, exact in fp32 and in bf16, so taking the upper half of the
+// fp32 pattern is an exact conversion.
+__device__ __forceinline__ void i8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    const float f0 = (float)(int)(int8_t)(w);
+    const float f1 = (float)(int)(int8_t)(w >> 8);
+    const float f2 = (float)(int)(int8_t)(w >> 16);
+    const float f3 = (float)((int)w >> 24);
+    lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                          __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Exact int32 dot of one 32-element Q8 block (8 dwords of codes on each side)
+// [fak MODEL-BASELINE-RESULTS, ACT 3 item 3: signed x signed int8 block dot].
+// |sum| <= 32 * 127 * 127 = 516,128, far inside int32.
+__device__ __forceinline__ int block_dot_i8(const uint32_t w[8], const uint32_t x[8]) {
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        s = __builtin_amdgcn_sdot4((int)w[i], (int)x[i], s, false);
+    return s;
+}
+
+// ---------------------------------------------------------------- reductions
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each row of 16 lanes with a fixed DPP tree (xor 1, xor 2, half-row
+// mirror, row mirror).  Every lane of the row ends with the same bits: each step
+// adds a pair of values in both orders, and fp32 addition is commutative.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);   // row_half_mirror
+    v += dpp_f<0x140>(v);   // row_mirror
+    return v;
+}
+
+// Sum over groups of G lanes (G = 16, 32 or 64), same fixed order everywhere.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    v = row16_sum(v);
+    if (G >= 32) v += __shfl_xor(v, 16);
+    if (G >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+}  // namespace q8

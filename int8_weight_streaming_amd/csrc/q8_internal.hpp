@@ -1,0 +1,31 @@
+// q8_internal.hpp -- host-side launchers shared between the C ABI layer and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+struct DeviceInfo {
+    int cu_count;
+};
+
+// Each launcher enqueues on `stream` and returns the launch's hipError_t.
+hipError_t launch_quantize_f32(const float* w, int64_t nblocks, int8_t* q, uint16_t* d,
+                               const DeviceInfo& dev, hipStream_t stream);
+hipError_t launch_quantize_bf16(const uint16_t* x, int64_t nblocks, int8_t* q, uint16_t* d,
+                                const DeviceInfo& dev, hipStream_t stream);
+
+hipError_t launch_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int m,
+                         int act, const void* x, const uint16_t* xd, float* y,
+                         const DeviceInfo& dev, hipStream_t stream);
+
+hipError_t launch_block_dots(const int8_t* wq, int64_t n, int64_t k, int m, const int8_t* xq,
+                             int32_t* isum, const DeviceInfo& dev, hipStream_t stream);
+
+hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t p,
+                          const int8_t* xq, const uint16_t* xd, float* y,
+                          const DeviceInfo& dev, hipStream_t stream);
+
+}  // namespace q8

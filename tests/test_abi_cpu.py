@@ -1,0 +1,127 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/q8stream.h declares, and rejects bad arguments on the host before any HIP
+call (so nothing is enqueued and no pointer is touched -- the pointers used here
+are fake addresses that would fault if dereferenced)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import int8_weight_streaming_amd as q8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8stream.h")
+
+OK, NULL, SHAPE, BATCH, ALIGN, ENUM, DEVICE = 0, 1, 2, 3, 4, 5, 6
+A = 0x100000          # fake, 16-byte aligned "device" addresses (never dereferenced)
+B = 0x200000
+MIS = 0x300004        # misaligned
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return q8.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(q8.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+    probe = declared_functions(os.path.join(ROOT, "include", "q8probe.h"))
+    assert set(probe) == set(q8.PROBE_EXPORTED)
+    for name in probe:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.q8_abi_version() == 1
+    assert [q8.status_str(s) for s in range(8)] == [
+        "Q8_OK", "Q8_ERR_NULL", "Q8_ERR_SHAPE", "Q8_ERR_BATCH", "Q8_ERR_ALIGN",
+        "Q8_ERR_ENUM", "Q8_ERR_DEVICE", "Q8_ERR_HIP"]
+    assert q8.status_str(99) == "unknown"
+    assert q8.status_str(-1) == "unknown"
+
+
+def test_quantize_validation(lib):
+    f = lib.q8_quantize_weights
+    assert f(A, 4, 0, A, B, None) == SHAPE
+    assert f(A, 4, 48, A, B, None) == SHAPE
+    assert f(A, 4, 16, A, B, None) == SHAPE
+    assert f(A, -1, 64, A, B, None) == SHAPE
+    assert f(A, 1 << 31, 64, A, B, None) == SHAPE
+    assert f(A, (1 << 30), 1 << 20, A, B, None) == SHAPE      # n*k overflow limit
+    assert f(None, 4, 64, A, B, None) == NULL
+    assert f(A, 4, 64, None, B, None) == NULL
+    assert f(A, 4, 64, A, None, None) == NULL
+    assert f(MIS, 4, 64, A, B, None) == ALIGN
+    assert f(A, 4, 64, MIS, B, None) == ALIGN
+    assert f(A, 4, 64, A, MIS, None) == ALIGN
+    assert f(None, 0, 64, None, None, None) == OK              # empty: no pointer touched
+    g = lib.q8_quantize_act
+    assert g(A, 3, 33, A, B, None) == SHAPE
+    assert g(None, 3, 64, A, B, None) == NULL
+    assert g(A, 3, 64, A, MIS, None) == ALIGN
+    assert g(None, 0, 64, None, None, None) == OK
+
+
+def test_skinny_validation(lib):
+    f = lib.q8_gemm_skinny
+    # act enum and the xd / act agreement come first
+    assert f(A, B, 8, 64, 1, 2, A, None, A, None) == ENUM
+    assert f(A, B, 8, 64, 1, -1, A, None, A, None) == ENUM
+    assert f(A, B, 8, 64, 1, 0, A, B, A, None) == ENUM         # bf16 with xd
+    assert f(A, B, 8, 64, 1, 1, A, None, A, None) == ENUM      # q8 without xd
+    assert f(A, B, 8, 40, 1, 0, A, None, A, None) == SHAPE
+    assert f(A, B, -2, 64, 1, 0, A, None, A, None) == SHAPE
+    assert f(A, B, 8, 64, 9, 0, A, None, A, None) == BATCH
+    assert f(A, B, 8, 64, -1, 0, A, None, A, None) == BATCH
+    assert f(None, B, 8, 64, 1, 0, A, None, A, None) == NULL
+    assert f(A, None, 8, 64, 1, 0, A, None, A, None) == NULL
+    assert f(A, B, 8, 64, 1, 0, None, None, A, None) == NULL
+    assert f(A, B, 8, 64, 1, 0, A, None, None, None) == NULL
+    assert f(MIS, B, 8, 64, 1, 0, A, None, A, None) == ALIGN
+    assert f(A, B, 8, 64, 1, 0, MIS, None, A, None) == ALIGN
+    assert f(A, B, 8, 64, 1, 0, A, None, MIS, None) == ALIGN
+    assert f(A, B, 8, 64, 1, 1, A, MIS, A, None) == ALIGN
+    assert f(None, None, 0, 64, 3, 0, None, None, None, None) == OK
+    assert f(None, None, 5, 64, 0, 0, None, None, None, None) == OK
+    g = lib.q8_gemv
+    assert g(A, B, 8, 64, 7, A, None, A, None) == ENUM
+    assert g(A, B, 8, 31, 0, A, None, A, None) == SHAPE
+    assert g(None, B, 8, 64, 0, A, None, A, None) == NULL
+    assert g(None, None, 0, 64, 0, None, None, None, None) == OK
+
+
+def test_prefill_and_block_dots_validation(lib):
+    f = lib.q8_gemm_prefill
+    assert f(A, B, 8, 48, 4, A, B, A, None) == SHAPE
+    assert f(A, B, 8, 64, 65535 * 64 + 1, A, B, A, None) == SHAPE
+    assert f(A, B, 8, 64, 4, None, B, A, None) == NULL
+    assert f(A, B, 8, 64, 4, A, None, A, None) == NULL
+    assert f(A, B, 8, 64, 4, A, B, MIS, None) == ALIGN
+    assert f(None, None, 8, 64, 0, None, None, None, None) == OK
+    assert f(None, None, 0, 64, 9, None, None, None, None) == OK
+    g = lib.q8_block_dots
+    assert g(A, 8, 64, 9, A, A, None) == BATCH
+    assert g(A, 8, 50, 1, A, A, None) == SHAPE
+    assert g(A, 8, 64, 1, None, A, None) == NULL
+    assert g(A, 8, 64, 1, A, MIS, None) == ALIGN
+    assert g(None, 0, 64, 1, None, None, None) == OK
+
+
+def test_valid_arguments_without_gpu_report_device(lib):
+    """With valid arguments the call reaches the device check; with no usable
+    gfx950 it refuses with Q8_ERR_DEVICE instead of launching anything."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib.q8_gemm_skinny(A, B, 8, 64, 1, 0, A, None, A, None) == DEVICE
+    assert lib.q8_quantize_weights(A, 4, 64, A, B, None) == DEVICE

@@ -1,0 +1,396 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle on
+identical seeded inputs.
+
+Integer outputs (codes, scales, int32 block sums) must match bit for bit; fp32
+outputs must be within max-abs 2e-3 and relative L2 1e-5 of the fp64 oracle, and
+equal it bit for bit where the construction makes every fp32 step exact."""
+import numpy as np
+import pytest
+import torch
+
+import int8_weight_streaming_amd as q8
+import oracle
+import workloads as wl
+from gpu_helpers import DEV, assert_close, log, oracle_threads, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q8.load_library()
+    oracle.set_threads(oracle_threads())
+    yield
+    torch.cuda.synchronize()
+
+
+def mixed_weights(seed, n, k):
+    """fp32 rows mixing N(0, 0.02) blocks with zero, negative-zero, tiny
+    (binary16-subnormal or zero scale), wide-range and exact-half blocks."""
+    g = wl.rng(seed)
+    w = (g.standard_normal((n, k)) * 0.02).astype(np.float32)
+    blocks = w.reshape(-1, 32)
+    nbt = blocks.shape[0]
+    kinds = g.integers(0, 8, size=nbt)
+    for i in np.nonzero(kinds == 1)[0]:
+        blocks[i] = 0.0
+    for i in np.nonzero(kinds == 2)[0]:
+        blocks[i] = -0.0
+    for i in np.nonzero(kinds == 3)[0]:
+        blocks[i] = (g.standard_normal(32) * 10.0 ** g.integers(-9, -3)).astype(np.float32)
+    for i in np.nonzero(kinds == 4)[0]:
+        blocks[i] = (g.standard_normal(32) * np.exp2(g.integers(-30, 8, size=32))).astype(np.float32)
+    for i in np.nonzero(kinds == 5)[0]:
+        e = int(g.integers(-8, 3))
+        v = (g.integers(0, 127, size=32) + 0.5) * 2.0 ** e * np.where(g.integers(0, 2, size=32) == 0, -1, 1)
+        v[int(g.integers(0, 32))] = 127 * 2.0 ** e
+        blocks[i] = v.astype(np.float32)
+    return w
+
+
+# ------------------------------------------------------------------ quantizers
+
+def _check_quant_w(w):
+    log(f"quantize_weights {w.shape}")
+    wq, wd = q8.quantize_weights(to_dev(w))
+    torch.cuda.synchronize()
+    oq, od = oracle.quantize_f32(w)
+    gq, gd = to_host(wq), to_host(wd)
+    assert np.array_equal(gd, od), f"scales differ at {np.argwhere(gd != od)[:5]}"
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+
+
+@pytest.mark.parametrize("n,k", [(1, 32), (3, 64), (7, 96), (33, 160), (129, 1536), (1000, 4096)])
+def test_quantize_weights_mixed(n, k):
+    _check_quant_w(mixed_weights(1000 + n + k, n, k))
+
+
+def test_quantize_weights_gemv_1536():
+    cfg = wl.CONFIGS["gemv_1536x1536_b1"]
+    _check_quant_w(wl.normal_weights(cfg["w_seed"], cfg["n"], cfg["k"]))
+
+
+def test_quantize_weights_lm_head_full():
+    cfg = wl.CONFIGS["lm_head_gemv_262144x1536_b1"]
+    _check_quant_w(wl.normal_weights(cfg["w_seed"], cfg["n"], cfg["k"]))
+
+
+@pytest.mark.parametrize("block", [0, 31])
+def test_quantize_weights_mimir_block(block):
+    for proj, (_, n, k) in enumerate(wl.BLOCK_SHAPES):
+        _check_quant_w(wl.normal_weights(wl.mimir_weight_seed(block, proj), n, k))
+
+
+def _check_quant_x(x_bits):
+    log(f"quantize_act {x_bits.shape}")
+    xq, xd = q8.quantize_act(to_dev(x_bits))
+    torch.cuda.synchronize()
+    oq, od = oracle.quantize_bf16(x_bits)
+    assert np.array_equal(to_host(xd), od)
+    assert np.array_equal(to_host(xq), oq)
+
+
+def test_quantize_act_special_and_prefill_rows():
+    _check_quant_x(wl.f32_to_bf16_bits(wl.special_rows_f32(3, 1536)))
+    _check_quant_x(wl.prefill_act_bf16(wl.CONFIGS["prefill_p256"]["xa_seed"], 256, 1536))
+    _check_quant_x(wl.prefill_act_bf16(wl.CONFIGS["prefill_p256"]["xb_seed"], 256, 4096))
+    _check_quant_x(wl.normal_act_bf16(7, 8, 96))
+
+
+def test_quantize_act_all_bf16_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = wl.bf16_bits_to_f32(bits)
+    keep = bits[np.isfinite(vals) & (np.abs(vals) <= np.float32(8e6))]
+    keep = keep[np.argsort(np.abs(wl.bf16_bits_to_f32(keep)), kind="stable")]
+    pad = (-keep.size) % 1024
+    x = np.concatenate([keep, np.zeros(pad, dtype=np.uint16)]).reshape(-1, 1024)
+    _check_quant_x(x)
+    g = wl.rng(12)
+    _check_quant_x(x[:, g.permutation(1024)])
+
+
+# ------------------------------------------------------------------ decode products
+
+def _w8a16_case(n, k, m, seed, mixed=False):
+    w = mixed_weights(seed, n, k) if mixed else wl.normal_weights(seed, n, k)
+    wq, wd = oracle.quantize_f32(w)
+    x = wl.normal_act_bf16(seed + 1, m, k)
+    return wq, wd, x
+
+
+def _run_skinny(wq, wd, x, xq=None, xd=None):
+    dq, dd = to_dev(wq), to_dev(wd)
+    if xq is None:
+        y = q8.gemm_skinny(dq, dd, to_dev(x))
+    else:
+        y = q8.gemm_skinny(dq, dd, to_dev(xq), to_dev(xd))
+    torch.cuda.synchronize()
+    return to_host(y)
+
+
+SMALL_SHAPES = [(1, 32), (5, 64), (63, 96), (64, 1536), (65, 1536), (1000, 4096),
+                (4097, 160), (1536, 4096), (300, 20480)]
+
+
+@pytest.mark.parametrize("n,k", SMALL_SHAPES)
+@pytest.mark.parametrize("m", [1, 2, 3, 8])
+def test_skinny_bf16_small(n, k, m):
+    log(f"skinny bf16 n={n} k={k} m={m}")
+    wq, wd, x = _w8a16_case(n, k, m, 2000 + n + k, mixed=True)
+    y = _run_skinny(wq, wd, x)
+    assert_close(y, oracle.w8a16(wq, wd, x), f"bf16 n={n} k={k} m={m}")
+
+
+@pytest.mark.parametrize("n,k", SMALL_SHAPES)
+@pytest.mark.parametrize("m", [1, 4, 5, 8])
+def test_skinny_q8_small(n, k, m):
+    log(f"skinny q8 n={n} k={k} m={m}")
+    wq, wd, x = _w8a16_case(n, k, m, 3000 + n + k, mixed=True)
+    xq, xd = oracle.quantize_bf16(x)
+    y = _run_skinny(wq, wd, x, xq, xd)
+    assert_close(y, oracle.q8q8(wq, wd, xq, xd), f"q8 n={n} k={k} m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 6, 7, 8])
+def test_skinny_large_rows_ragged(m):
+    """Enough rows for the 16-lane-group layout, with a ragged last tile."""
+    n, k = 33000, 1536
+    log(f"skinny large ragged m={m}")
+    wq, wd, x = _w8a16_case(n, k, m, 4000 + m)
+    assert_close(_run_skinny(wq, wd, x), oracle.w8a16(wq, wd, x), f"bf16 large m={m}")
+    xq, xd = oracle.quantize_bf16(x)
+    assert_close(_run_skinny(wq, wd, x, xq, xd), oracle.q8q8(wq, wd, xq, xd), f"q8 large m={m}")
+
+
+def test_gemv_1536_config():
+    cfg = wl.CONFIGS["gemv_1536x1536_b1"]
+    w = wl.normal_weights(cfg["w_seed"], cfg["n"], cfg["k"])
+    x = wl.normal_act_bf16(cfg["x_seed"], 1, cfg["k"])
+    wq, wd = q8.quantize_weights(to_dev(w))
+    y = q8.gemv(wq, wd, to_dev(x[0]))
+    torch.cuda.synchronize()
+    oq, od = oracle.quantize_f32(w)
+    assert np.array_equal(to_host(wq), oq) and np.array_equal(to_host(wd), od)
+    assert_close(to_host(y)[None, :], oracle.w8a16(oq, od, x), "gemv 1536")
+
+
+def test_gemv_lm_head_config_full():
+    cfg = wl.CONFIGS["lm_head_gemv_262144x1536_b1"]
+    log("lm_head gemv: generating 262144 x 1536")
+    w = wl.normal_weights(cfg["w_seed"], cfg["n"], cfg["k"])
+    x = wl.rms_unit_act_bf16(cfg["x_seed"], cfg["k"])
+    wq, wd = q8.quantize_weights(to_dev(w))
+    y = q8.gemv(wq, wd, to_dev(x[0]))
+    torch.cuda.synchronize()
+    oq, od = oracle.quantize_f32(w)
+    del w
+    assert np.array_equal(to_host(wq), oq) and np.array_equal(to_host(wd), od)
+    assert_close(to_host(y)[None, :], oracle.w8a16(oq, od, x), "lm_head gemv")
+    # the Q8-activation form on the same weights
+    xq, xd = oracle.quantize_bf16(x)
+    yq = q8.gemv(wq, wd, to_dev(xq[0]), to_dev(xd[0]))
+    torch.cuda.synchronize()
+    assert_close(to_host(yq)[None, :], oracle.q8q8(oq, od, xq, xd), "lm_head gemv q8")
+
+
+@pytest.mark.parametrize("m", [2, 4, 8])
+def test_skinny_mimir_shapes(m):
+    for proj, (name, n, k) in enumerate(wl.BLOCK_SHAPES):
+        log(f"mimir {name} m={m}")
+        w = wl.normal_weights(wl.mimir_weight_seed(0, proj), n, k)
+        wq, wd = oracle.quantize_f32(w)
+        x = wl.normal_act_bf16(7000 + proj, m, k)
+        assert_close(_run_skinny(wq, wd, x), oracle.w8a16(wq, wd, x), f"{name} m={m}")
+
+
+# ------------------------------------------------------------------ block dots
+
+@pytest.mark.parametrize("n,k,m", [(1, 32, 1), (77, 1536, 8), (1536, 4096, 3)])
+def test_block_dots_bit_exact(n, k, m):
+    w = mixed_weights(5000 + n, n, k)
+    wq, _ = oracle.quantize_f32(w)
+    xq, _ = oracle.quantize_bf16(wl.normal_act_bf16(5001, m, k))
+    got = to_host(q8.block_dots(to_dev(wq), to_dev(xq)))
+    assert np.array_equal(got, oracle.block_dots(wq, xq))
+
+
+def test_block_dots_extremes():
+    k = 64
+    wq = np.full((2, k), 127, dtype=np.int8)
+    wq[1] = -127
+    xq = np.full((1, k), -127, dtype=np.int8)
+    got = to_host(q8.block_dots(to_dev(wq), to_dev(xq)))
+    assert np.all(got[0, 0] == -516128) and np.all(got[0, 1] == 516128)
+
+
+# ------------------------------------------------------------------ prefill
+
+def _prefill_case(n, k, p, seed):
+    w = mixed_weights(seed, n, k)
+    wq, wd = oracle.quantize_f32(w)
+    xq, xd = oracle.quantize_bf16(wl.prefill_act_bf16(seed + 1, p, k))
+    return wq, wd, xq, xd
+
+
+@pytest.mark.parametrize("n,k,p", [(1, 32, 1), (64, 64, 64), (100, 96, 11), (65, 2080, 100),
+                                   (300, 4096, 256), (33, 1536, 257)])
+def test_prefill_small(n, k, p):
+    log(f"prefill n={n} k={k} p={p}")
+    wq, wd, xq, xd = _prefill_case(n, k, p, 6000 + n + k + p)
+    y = q8.gemm_prefill(to_dev(wq), to_dev(wd), to_dev(xq), to_dev(xd))
+    torch.cuda.synchronize()
+    assert_close(to_host(y), oracle.q8q8(wq, wd, xq, xd), f"prefill n={n} k={k} p={p}")
+
+
+def test_prefill_p256_config():
+    cfg = wl.CONFIGS["prefill_p256"]
+    xa = wl.prefill_act_bf16(cfg["xa_seed"], 256, wl.HIDDEN)
+    xb = wl.prefill_act_bf16(cfg["xb_seed"], 256, wl.INTER)
+    for proj, (name, n, k) in enumerate(wl.BLOCK_SHAPES):
+        if name == "o":
+            continue
+        log(f"prefill p256 {name}")
+        w = wl.normal_weights(wl.mimir_weight_seed(0, proj), n, k)
+        x = xb if k == wl.INTER else xa
+        dxq, dxd = q8.quantize_act(to_dev(x))
+        dwq, dwd = q8.quantize_weights(to_dev(w))
+        y = q8.gemm_prefill(dwq, dwd, dxq, dxd)
+        torch.cuda.synchronize()
+        wq, wd = oracle.quantize_f32(w)
+        xq, xd = oracle.quantize_bf16(x)
+        assert np.array_equal(to_host(dxq), xq) and np.array_equal(to_host(dxd), xd)
+        assert_close(to_host(y), oracle.q8q8(wq, wd, xq, xd), f"prefill {name}")
+
+
+# ------------------------------------------------------------------ exact constructions
+
+def _pow2_q8(seed, n, k, m):
+    """Codes in [-127, 127] with one |127| per block and power-of-two scales, so
+    the scales are exactly 2^e and every product and partial sum is exact."""
+    g = wl.rng(seed)
+    nb = k // 32
+    def make(rows, sign):
+        v = g.integers(-127, 128, size=(rows, k)).astype(np.float32)
+        v.reshape(rows, nb, 32)[:, :, 3] = sign * 127
+        e = g.integers(-6, 2, size=(rows, nb))
+        return (v.reshape(rows, nb, 32) * np.exp2(e)[:, :, None]).reshape(rows, k).astype(np.float32)
+    return make(n, 1), make(m, -1)
+
+
+def test_exact_pow2_scales_bitwise():
+    n, k, m = 200, 512, 8
+    w, x = _pow2_q8(8000, n, k, m)
+    wq, wd = oracle.quantize_f32(w)
+    xb = wl.f32_to_bf16_bits(x)
+    xq, xd = oracle.quantize_bf16(xb)
+    # Q8 x Q8: every block term is an exact dyadic number; sums stay < 2^24 ulps
+    y = _run_skinny(wq, wd, xb, xq, xd)
+    assert np.array_equal(y, oracle.q8q8(wq, wd, xq, xd).astype(np.float32))
+    yp = to_host(q8.gemm_prefill(to_dev(wq), to_dev(wd), to_dev(xq), to_dev(xd)))
+    assert np.array_equal(yp, oracle.q8q8(wq, wd, xq, xd).astype(np.float32))
+    # W8A16 with integer activations: exact as well
+    xi = wl.f32_to_bf16_bits(wl.rng(8001).integers(-100, 101, size=(m, k)).astype(np.float32))
+    yw = _run_skinny(wq, wd, xi)
+    assert np.array_equal(yw, oracle.w8a16(wq, wd, xi).astype(np.float32))
+
+
+def test_one_hot_gives_scaled_code():
+    n, k = 70, 256
+    wq, wd, _ = _w8a16_case(n, k, 1, 8100)
+    s = wd.view(np.float16).astype(np.float32)
+    x = np.zeros((8, k), dtype=np.uint16)
+    cols = [0, 31, 32, 100, 200, 255, 17, 64]
+    for i, c in enumerate(cols):
+        x[i, c] = 0x3F80
+    y = _run_skinny(wq, wd, x)
+    for i, c in enumerate(cols):
+        assert np.array_equal(y[i], wq[:, c].astype(np.float32) * s[:, c // 32])
+    assert np.all(_run_skinny(wq, wd, np.zeros((3, k), dtype=np.uint16)) == 0)
+
+
+# ------------------------------------------------------------------ determinism, batching, guards
+
+def test_identical_rows_identical_outputs():
+    n, k = 40000, 1536
+    wq, wd, x1 = _w8a16_case(n, k, 1, 8200)
+    y = _run_skinny(wq, wd, np.repeat(x1, 8, axis=0))
+    assert all(np.array_equal(y[0], y[i]) for i in range(1, 8))
+    xq, xd = oracle.quantize_bf16(np.repeat(x1, 8, axis=0))
+    yq = _run_skinny(wq, wd, None, xq, xd)
+    assert all(np.array_equal(yq[0], yq[i]) for i in range(1, 8))
+
+
+def test_repeat_and_graph_replay_bitwise():
+    n, k = 8192, 1536
+    wq, wd, x = _w8a16_case(n, k, 4, 8300)
+    dq, dd, dx = to_dev(wq), to_dev(wd), to_dev(x)
+    xq, xd = oracle.quantize_bf16(x)
+    dxq, dxd = to_dev(xq), to_dev(xd)
+    ref = q8.gemm_skinny(dq, dd, dx).clone()
+    refp = q8.gemm_prefill(dq, dd, dxq, dxd).clone()
+    for _ in range(3):
+        assert torch.equal(q8.gemm_skinny(dq, dd, dx), ref)
+        assert torch.equal(q8.gemm_prefill(dq, dd, dxq, dxd), refp)
+    out = torch.empty_like(ref)
+    outp = torch.empty_like(refp)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        q8.gemm_skinny(dq, dd, dx, out=out)
+        q8.gemm_prefill(dq, dd, dxq, dxd, out=outp)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q8.gemm_skinny(dq, dd, dx, out=out)
+        q8.gemm_prefill(dq, dd, dxq, dxd, out=outp)
+    for _ in range(4):
+        out.fill_(float("nan"))
+        outp.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(outp, refp)
+        # eager work between replays
+        q8.gemm_skinny(dq, dd, dx)
+        torch.cuda.synchronize()
+
+
+def test_outputs_leave_guard_bands_untouched():
+    n, k, m, p = 100, 96, 3, 5
+    w = mixed_weights(8400, n, k)
+    guard = 4096
+    wq_buf = torch.full((n * k + guard,), 0x5A, dtype=torch.int8, device=DEV)
+    wd_buf = torch.full((n * k // 32 + guard,), 0x1234, dtype=torch.int16, device=DEV)
+    wq = wq_buf[: n * k].view(n, k)
+    wd = wd_buf[: n * k // 32].view(torch.uint16).view(n, k // 32)
+    q8.quantize_weights(to_dev(w), out=(wq, wd))
+    y_buf = torch.full((m * n + guard,), 7.0, dtype=torch.float32, device=DEV)
+    y = y_buf[: m * n].view(m, n)
+    x = to_dev(wl.normal_act_bf16(8401, m, k))
+    q8.gemm_skinny(wq, wd, x, out=y)
+    xq, xd = q8.quantize_act(to_dev(wl.prefill_act_bf16(8402, p, k)))
+    yp_buf = torch.full((p * n + guard,), 7.0, dtype=torch.float32, device=DEV)
+    q8.gemm_prefill(wq, wd, xq, xd, out=yp_buf[: p * n].view(p, n))
+    torch.cuda.synchronize()
+    assert torch.all(wq_buf[n * k:] == 0x5A)
+    assert torch.all(wd_buf[n * k // 32:] == 0x1234)
+    assert torch.all(y_buf[m * n:] == 7.0)
+    assert torch.all(yp_buf[p * n:] == 7.0)
+
+
+def test_empty_calls_are_noops():
+    z = torch.empty((0, 64), dtype=torch.float32, device=DEV)
+    wq, wd = q8.quantize_weights(z)
+    assert wq.shape == (0, 64) and wd.shape == (0, 2)
+    y = q8.gemm_skinny(torch.empty((0, 64), dtype=torch.int8, device=DEV),
+                       torch.empty((0, 2), dtype=torch.uint16, device=DEV),
+                       torch.zeros((2, 64), dtype=torch.uint16, device=DEV))
+    assert y.shape == (2, 0)
+
+
+def test_rejects_bad_batch_loudly():
+    wq = torch.zeros((4, 64), dtype=torch.int8, device=DEV)
+    wd = torch.zeros((4, 2), dtype=torch.uint16, device=DEV)
+    with pytest.raises(q8.Q8Error):
+        q8.gemm_skinny(wq, wd, torch.zeros((9, 64), dtype=torch.uint16, device=DEV))
