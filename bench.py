@@ -211,7 +211,7 @@ def bench_mimir(q8, wl, dev, weights, m: int, replays: int = 20) -> dict:
     nbytes = mimir_step_bytes(wl, m)
     return {"m": m, "ms_per_step": ms, "tok_per_s": m * 1e3 / ms, "eager_ms_per_step": eager_ms,
             "eager_tok_per_s": m * 1e3 / eager_ms, "bytes_per_step": nbytes,
-            "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": m * HBM_PEAK_GBPS * 1e6 / nbytes}
+            "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": m * HBM_PEAK_GBPS * 1e9 / nbytes}
 
 
 def bench_prefill(q8, wl, dev, weights, reps: int = 50) -> dict:

@@ -50,6 +50,42 @@ def mixed_weights(seed, n, k):
     return w
 
 
+def edge_weights(seed, n, k):
+    """N(0, 0.02) rows with the quantizer's edge cases at realistic magnitude:
+    zero and negative-zero blocks, tiny blocks (binary16-subnormal or zero
+    scale), wide dynamic range below 2^-4, and exact halves of 2^-8..2^-6."""
+    g = wl.rng(seed)
+    w = (g.standard_normal((n, k)) * 0.02).astype(np.float32)
+    blocks = w.reshape(-1, 32)
+    kinds = g.integers(0, 8, size=blocks.shape[0])
+    for i in np.nonzero(kinds == 1)[0]:
+        blocks[i] = 0.0
+    for i in np.nonzero(kinds == 2)[0]:
+        blocks[i] = -0.0
+    for i in np.nonzero(kinds == 3)[0]:
+        blocks[i] = (g.standard_normal(32) * 10.0 ** g.integers(-9, -3)).astype(np.float32)
+    for i in np.nonzero(kinds == 4)[0]:
+        blocks[i] = (g.standard_normal(32) * np.exp2(g.integers(-30, -4, size=32))).astype(np.float32)
+    for i in np.nonzero(kinds == 5)[0]:
+        e = int(g.integers(-8, -5))
+        v = (g.integers(0, 127, size=32) + 0.5) * 2.0 ** e * np.where(g.integers(0, 2, size=32) == 0, -1, 1)
+        v[int(g.integers(0, 32))] = 127 * 2.0 ** e
+        blocks[i] = v.astype(np.float32)
+    return w
+
+
+def assert_within_summation_bound(y, wq, wd, x, what=""):
+    """Inputs of any magnitude: |y - y64| <= (K + 2) * 2^-24 * sum_k |q s x|,
+    the classical bound for fp32 summation of K exact products in any order
+    plus one rounding of the block scale product."""
+    k = wq.shape[1]
+    s = np.repeat(wd.view(np.float16).astype(np.float64), 32, axis=1)
+    absum = np.abs(wl.bf16_bits_to_f32(x).astype(np.float64)) @ (np.abs(wq.astype(np.float64)) * s).T
+    err = np.abs(np.asarray(y, dtype=np.float64) - oracle.w8a16(wq, wd, x))
+    bound = (k + 2) * 2.0 ** -24 * absum
+    assert np.all(err <= bound), f"{what}: worst err/bound {np.max(err / np.maximum(bound, 1e-300)):.3f}"
+
+
 # ------------------------------------------------------------------ quantizers
 
 def _check_quant_w(w):
@@ -114,7 +150,7 @@ def test_quantize_act_all_bf16_patterns():
 # ------------------------------------------------------------------ decode products
 
 def _w8a16_case(n, k, m, seed, mixed=False):
-    w = mixed_weights(seed, n, k) if mixed else wl.normal_weights(seed, n, k)
+    w = edge_weights(seed, n, k) if mixed else wl.normal_weights(seed, n, k)
     wq, wd = oracle.quantize_f32(w)
     x = wl.normal_act_bf16(seed + 1, m, k)
     return wq, wd, x
@@ -151,6 +187,17 @@ def test_skinny_q8_small(n, k, m):
     xq, xd = oracle.quantize_bf16(x)
     y = _run_skinny(wq, wd, x, xq, xd)
     assert_close(y, oracle.q8q8(wq, wd, xq, xd), f"q8 n={n} k={k} m={m}")
+
+
+@pytest.mark.parametrize("n,k,m", [(77, 1536, 1), (300, 20480, 2), (4097, 4096, 8), (40000, 1536, 3)])
+def test_skinny_extreme_range_summation_bound(n, k, m):
+    """Weights up to 2^8 in magnitude: the fixed 2e-3 bound does not scale, so
+    the product is held to the summation error bound instead."""
+    log(f"skinny extreme n={n} k={k} m={m}")
+    w = mixed_weights(2500 + n + k, n, k)
+    wq, wd = oracle.quantize_f32(w)
+    x = wl.normal_act_bf16(2501 + n, m, k)
+    assert_within_summation_bound(_run_skinny(wq, wd, x), wq, wd, x, f"extreme n={n} k={k} m={m}")
 
 
 @pytest.mark.parametrize("m", [1, 2, 4, 6, 7, 8])
@@ -228,7 +275,7 @@ def test_block_dots_extremes():
 # ------------------------------------------------------------------ prefill
 
 def _prefill_case(n, k, p, seed):
-    w = mixed_weights(seed, n, k)
+    w = edge_weights(seed, n, k)
     wq, wd = oracle.quantize_f32(w)
     xq, xd = oracle.quantize_bf16(wl.prefill_act_bf16(seed + 1, p, k))
     return wq, wd, xq, xd
@@ -267,16 +314,22 @@ def test_prefill_p256_config():
 # ------------------------------------------------------------------ exact constructions
 
 def _pow2_q8(seed, n, k, m):
-    """Codes in [-127, 127] with one |127| per block and power-of-two scales, so
-    the scales are exactly 2^e and every product and partial sum is exact."""
+    """Codes in [-127, 127] with one |127| per block and scales 2^0 or 2^-1, so
+    the stored scales are exactly 2^e and every block term is a multiple of 2^-2."""
     g = wl.rng(seed)
     nb = k // 32
     def make(rows, sign):
         v = g.integers(-127, 128, size=(rows, k)).astype(np.float32)
         v.reshape(rows, nb, 32)[:, :, 3] = sign * 127
-        e = g.integers(-6, 2, size=(rows, nb))
+        e = g.integers(-1, 1, size=(rows, nb))
         return (v.reshape(rows, nb, 32) * np.exp2(e)[:, :, None]).reshape(rows, k).astype(np.float32)
     return make(n, 1), make(m, -1)
+
+
+def _assert_exact_regime(terms_abs_sum, quantum):
+    """Every partial sum of terms that are multiples of `quantum` is exact in
+    fp32 when the sum of their magnitudes stays below 2^24 quanta."""
+    assert np.all(terms_abs_sum < 2.0 ** 24 * quantum), "construction left the exact regime"
 
 
 def test_exact_pow2_scales_bitwise():
@@ -285,15 +338,22 @@ def test_exact_pow2_scales_bitwise():
     wq, wd = oracle.quantize_f32(w)
     xb = wl.f32_to_bf16_bits(x)
     xq, xd = oracle.quantize_bf16(xb)
-    # Q8 x Q8: every block term is an exact dyadic number; sums stay < 2^24 ulps
-    y = _run_skinny(wq, wd, xb, xq, xd)
-    assert np.array_equal(y, oracle.q8q8(wq, wd, xq, xd).astype(np.float32))
+    sw = wd.view(np.float16).astype(np.float64)
+    sx = xd.view(np.float16).astype(np.float64)
+    assert set(np.unique(sw)) <= {0.5, 1.0} and set(np.unique(sx)) <= {0.5, 1.0}
+    isum = oracle.block_dots(wq, xq).astype(np.float64)          # [m][n][nb]
+    _assert_exact_regime((np.abs(isum) * sw[None] * sx[:, None]).sum(axis=2), 0.25)
+    ref = oracle.q8q8(wq, wd, xq, xd).astype(np.float32)
+    assert np.array_equal(_run_skinny(wq, wd, xb, xq, xd), ref)
     yp = to_host(q8.gemm_prefill(to_dev(wq), to_dev(wd), to_dev(xq), to_dev(xd)))
-    assert np.array_equal(yp, oracle.q8q8(wq, wd, xq, xd).astype(np.float32))
-    # W8A16 with integer activations: exact as well
-    xi = wl.f32_to_bf16_bits(wl.rng(8001).integers(-100, 101, size=(m, k)).astype(np.float32))
-    yw = _run_skinny(wq, wd, xi)
-    assert np.array_equal(yw, oracle.w8a16(wq, wd, xi).astype(np.float32))
+    assert np.array_equal(yp, ref)
+    # W8A16 with integer activations: every product and partial sum is an
+    # integer times 2^-1
+    xi_f = wl.rng(8001).integers(-100, 101, size=(m, k)).astype(np.float32)
+    xi = wl.f32_to_bf16_bits(xi_f)
+    absum = np.abs(xi_f.astype(np.float64)) @ (np.abs(wq.astype(np.float64)) * np.repeat(sw, 32, axis=1)).T
+    _assert_exact_regime(absum, 0.5)
+    assert np.array_equal(_run_skinny(wq, wd, xi), oracle.w8a16(wq, wd, xi).astype(np.float32))
 
 
 def test_one_hot_gives_scaled_code():
@@ -358,7 +418,7 @@ def test_repeat_and_graph_replay_bitwise():
 
 def test_outputs_leave_guard_bands_untouched():
     n, k, m, p = 100, 96, 3, 5
-    w = mixed_weights(8400, n, k)
+    w = edge_weights(8400, n, k)
     guard = 4096
     wq_buf = torch.full((n * k + guard,), 0x5A, dtype=torch.int8, device=DEV)
     wd_buf = torch.full((n * k // 32 + guard,), 0x1234, dtype=torch.int16, device=DEV)
