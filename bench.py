@@ -51,20 +51,27 @@ def prefill_bytes(n: int, k: int, p: int) -> int:
 
 
 def gpu_state() -> dict | None:
+    """GPU temperatures and current clock levels read from sysfs (plain file
+    reads: no child process, which a profiled process must not exec)."""
+    import glob
+    out = {}
     try:
-        r = subprocess.run(["rocm-smi", "--showtemp", "--showclocks", "--json"],
-                           capture_output=True, text=True, timeout=15)
-        data = json.loads(r.stdout)
-        card = next(iter(data.values()))
-        keep = {}
-        for key, val in card.items():
-            kl = key.lower()
-            if ("temperature" in kl and ("junction" in kl or "edge" in kl or "memory" in kl)) or \
-               kl.startswith("sclk") or kl.startswith("mclk"):
-                keep[key] = val
-        return keep or None
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            if not os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+                continue
+            for hw in glob.glob(os.path.join(dev, "hwmon", "hwmon*")):
+                for t in sorted(glob.glob(os.path.join(hw, "temp*_input"))):
+                    lab = t.replace("_input", "_label")
+                    name = open(lab).read().strip() if os.path.exists(lab) else os.path.basename(t)
+                    out[f"temp_{name}_C"] = int(open(t).read().strip()) / 1000.0
+            for clk in ("pp_dpm_sclk", "pp_dpm_mclk"):
+                for line in open(os.path.join(dev, clk)):
+                    if "*" in line:
+                        out[clk[7:]] = line.split(":", 1)[1].replace("*", "").strip()
+            break
     except Exception:
-        return None
+        return out or None
+    return out or None
 
 
 # ------------------------------------------------------------------ device helpers
@@ -84,6 +91,23 @@ def quantize_on_device(q8, w_np, dev):
     torch.cuda.synchronize()
     del w
     return wq, wd
+
+
+def time_region(fn, iters: int) -> tuple[float, float]:
+    """(mean per-call time from one pair of HIP events around `iters` back-to-back
+    calls on the launch stream, wall s)."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(iters):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / iters, wall
 
 
 def time_events(fn, iters: int) -> tuple[float, float]:
@@ -115,6 +139,20 @@ def bench_read_probe(q8, dev, gib: float = 4.0, reps: int = 10) -> dict:
     ms, _ = time_events(lambda i: q8.probe_read(buf, sink), reps)
     del buf
     return {"bytes": nbytes, "ms": ms, "GBps": nbytes / ms / 1e6}
+
+
+def bench_copy_probe(dev, gib: float = 1.0, reps: int = 10) -> dict:
+    """Device-to-device copy of a known size: a second peak probe, and the
+    reference that scales the HBM byte counters (it reads and writes `bytes`)."""
+    import torch
+    nbytes = int(gib * (1 << 30))
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(3)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    ms, _ = time_events(lambda i: b.copy_(a), reps)
+    del a, b
+    return {"bytes_each_way": nbytes, "ms": ms, "GBps_read_plus_write": 2 * nbytes / ms / 1e6}
 
 
 def bench_gemv_1536(q8, wl, dev, copies: int = 256, iters: int = 2000) -> dict:
@@ -317,7 +355,7 @@ def main() -> int:
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
-    kern_ms, wall = time_events(call, args.steps)
+    kern_ms, wall = time_region(call, args.steps)
     ms_per_step = wall * 1e3 / args.steps
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
@@ -341,6 +379,8 @@ def main() -> int:
     log(f"read probe: {probe['GBps']:.1f} GB/s")
     extras["read_probe"] = probe
     measured_peak = probe["GBps"]
+    extras["copy_probe"] = bench_copy_probe(dev)
+    log(f"copy probe: {extras['copy_probe']['GBps_read_plus_write']:.1f} GB/s (read + write)")
 
     if not args.metric_only:
         log("gemv 1536x1536")

@@ -1,8 +1,10 @@
 // q8_probe.hip -- HBM read-bandwidth probe (measurement utility).
 //
-// Each lane streams 16-byte non-temporal loads over a grid-stride loop, four
-// loads in flight per lane, and folds them into an xor checksum; one word per
-// workgroup is written so the loads stay live.
+// Each workgroup streams one contiguous span of the buffer with 16-byte
+// non-temporal loads, four in flight per lane, and folds them into an xor
+// checksum; one word per workgroup is written so the loads stay live.
+// Contiguous spans per workgroup keep each DRAM page's reads together, which
+// measured faster on MI355X than a grid-stride walk over the whole buffer.
 #include "q8probe.h"
 #include "q8_device.hpp"
 
@@ -10,21 +12,23 @@
 
 namespace {
 
-constexpr int kProbeBlocksPerCu = 8;
+constexpr int kProbeBlocksPerCu = 16;
 
 __global__ __launch_bounds__(256) void probe_read_kernel(const q8::u32x4* __restrict__ src,
                                                          int64_t n16, uint32_t* __restrict__ sink) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = (int64_t)blockIdx.x * per;
+    const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
     q8::u32x4 acc = {0u, 0u, 0u, 0u};
-    for (; i + 3 * stride < n16; i += 4 * stride) {
+    int64_t i = b0 + threadIdx.x;
+    for (; i + 3 * 256 < b1; i += 4 * 256) {
         const q8::u32x4 a = __builtin_nontemporal_load(src + i);
-        const q8::u32x4 b = __builtin_nontemporal_load(src + i + stride);
-        const q8::u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-        const q8::u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+        const q8::u32x4 b = __builtin_nontemporal_load(src + i + 256);
+        const q8::u32x4 c = __builtin_nontemporal_load(src + i + 512);
+        const q8::u32x4 d = __builtin_nontemporal_load(src + i + 768);
         acc ^= a ^ b ^ c ^ d;
     }
-    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+    for (; i < b1; i += 256) acc ^= __builtin_nontemporal_load(src + i);
     uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
     __shared__ uint32_t red[256];
     red[threadIdx.x] = v;
@@ -35,7 +39,6 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const q8::u32x4* __rest
         sink[blockIdx.x] = s;
     }
 }
-
 int cu_count_current() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
