@@ -123,7 +123,9 @@ q8_status q8_gemm_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_
                          int64_t m, int act, const void* x, const uint16_t* xd,
                          float* y, hipStream_t stream);
 
-/* Q8 x Q8 prefill product for p activation rows (any p >= 0):
+/* Q8 x Q8 prefill product for p activation rows (0 <= p <= 4,194,240) and
+ * K <= 7104 (the scales of a workgroup's rows are staged whole in LDS; larger K
+ * returns Q8_ERR_SHAPE):
  * y[t][j] = sum_b wd[j][b] * xd[t][b] * sum_{i<32} wq[j][32b+i] * xq[t][32b+i],
  * the int32 block sums taken on the int8 matrix cores, each block folded into an
  * fp32 accumulator with its two scales [fak MODEL-BASELINE-RESULTS, ACT 4,

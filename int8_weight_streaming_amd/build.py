@@ -23,9 +23,12 @@ ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
           "-I", INCLUDE, "-I", CSRC]
-# Packed fp32 VALU instructions are kept off for all device code.
+# Packed fp32 VALU instructions are kept off for all device code.  Matrix-core
+# results are written to ordinary VGPRs (no copies out of accumulation
+# registers before the fp32 fold).
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=true"]
 
 
 def _compile(src: str) -> str:

@@ -182,6 +182,7 @@ q8_status q8_gemm_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
     Q8_TRY(check_rows(n, k));
     Q8_TRY(check_rows(p, k));
     if (p > kMaxPrefillRows) return Q8_ERR_SHAPE;
+    if (q8::prefill_lds_bytes(k) > q8::kPrefillMaxLds) return Q8_ERR_SHAPE;
     if (n == 0 || p == 0) return Q8_OK;
     if (!wq || !wd || !xq || !xd || !y) return Q8_ERR_NULL;
     if (!aligned16(wq) || !aligned16(wd) || !aligned16(xq) || !aligned16(xd) || !aligned16(y))

@@ -8,19 +8,43 @@
 // convert + scale step, register-block the output tile so every weight block
 // serves several tokens and every activation block several rows.]
 //
-// On gfx950 a single v_mfma_i32_32x32x32_i8 covers exactly one 32-wide Q8 block
-// of a 32 x 32 output tile, so the per-block int32 sums come straight out of the
-// matrix core and are folded into fp32 accumulators by the vector ALUs.  Both
-// operands are K-contiguous (codes [rows][K]), so each lane reads its 16-byte
-// operand slice directly.  Workgroup tile: 64 activation rows x 64 weight rows,
-// one 32 x 32 tile per wave; the K/32 scales of the tile are staged in LDS as
-// fp32.
+// On gfx950 one v_mfma_i32_32x32x32_i8 covers exactly one 32-wide Q8 block of
+// a 32 x 32 output tile, so every block sum comes straight from the matrix core
+// as an exact int32.  The per-(t, j) scale product wd*xd of the same block is a
+// rank-1 outer product: a v_mfma_f32_32x32x2_f32 with a single non-zero k term
+// produces it in the same register layout, exactly (every binary16 value,
+// subnormals included, is a normal fp32 number, and a product of two of them
+// needs at most 22 significant bits).  The vector ALUs then only convert and
+// accumulate: two operations per output and block.
+//
+// Work layout.  A workgroup computes one 32 x 32 output tile; its four waves
+// take contiguous quarters of the K blocks (more waves in flight), and the four
+// partial tiles are added through LDS in a fixed order, so results are bitwise
+// reproducible.  Operands are K-contiguous (codes [rows][K]).  Each wave copies
+// its 32 activation rows and 32 weight rows, four blocks (128 bytes) per row at
+// a time, into its own LDS slice with full-cache-line 16-byte loads (eight
+// lanes per row), prefetching the next four blocks into registers; the MFMA
+// operand slices are then read from LDS (row pitch padded to 144 bytes so the
+// 16-byte reads of 32 rows are bank-conflict free).  Gathering the operand
+// slices straight from global memory touches 32 cache lines per instruction
+// and measured 5-8x slower.  The workgroup's binary16 scales for the whole K
+// range are staged once.  Workgroups that share a weight tile get ids that land
+// on the same XCD (ids are dealt round-robin to the 8 XCDs), so its L2 fetches
+// each weight tile from HBM once.
 #include "q8_device.hpp"
 #include "q8_internal.hpp"
 
 namespace q8 {
 
-constexpr int kPrefillKt = 64;   // blocks of scales staged per K tile
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kGroup = 4;                      // blocks per pipeline step (128 B per row)
+constexpr int kPitch = 144;                    // LDS bytes per staged row (128 + 16 pad)
+constexpr int kWaveSlice = 2 * 32 * kPitch;    // A and B rows of one wave: 9216 B
+
+// Odd number of dwords per staged scale row: 32 lanes reading one scale of
+// 32 different rows hit 32 different banks.
+__host__ __device__ constexpr int scale_pitch_dw(int nb) { return ((nb + 1) / 2) | 1; }
 
 __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__ wq,
                                                       const uint16_t* __restrict__ wd, int64_t n,
@@ -28,62 +52,136 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
                                                       const int8_t* __restrict__ xq,
                                                       const uint16_t* __restrict__ xd,
                                                       float* __restrict__ y) {
-    __shared__ float xs_l[kPrefillKt * 64];
-    __shared__ float ws_l[kPrefillKt * 64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wp = wave & 1, wn = wave >> 1;
-    const int64_t p0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
-    const int i = lane & 31, h = lane >> 5;
-    const int64_t k = (int64_t)nb * 32;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int ntn = (int)((n + 31) / 32), ntp = (int)((p + 31) / 32);
+    // id = xcd + 8 * (tp + ntp * c)  ->  weight tile tn = 8c + xcd, activation tile tp
+    const int id = blockIdx.x;
+    const int xcd = id & 7, rest = id >> 3;
+    const int tp = rest % ntp, tn = 8 * (rest / ntp) + xcd;
+    if (tn >= ntn) return;                             // whole padding workgroup leaves
 
-    // The 32x32 result layout gives lane (i, h) rows 8*(r/4) + 4*h + r%4,
-    // r = 0..15.  Operand row i is loaded from activation row pl(i) so that the
-    // lane's 16 results are the 16 consecutive activation rows 16*h + r.
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t p0 = (int64_t)tp * 32, n0 = (int64_t)tn * 32;
+    const int64_t k = (int64_t)nb * 32;
+    const int spw = scale_pitch_dw(nb);
+    uint32_t* sA = reinterpret_cast<uint32_t*>(lds + 4 * kWaveSlice);   // [32][spw] dwords
+    uint32_t* sB = sA + 32 * spw;
+
+    // ---- stage every scale of the tile's 32 activation and 32 weight rows
+    {
+        const int per_row = (nb + 1) / 2;              // dwords of binary16 pairs
+        for (int t = threadIdx.x; t < 64 * per_row; t += 256) {
+            const int row = t / per_row, d = t % per_row;
+            const bool isb = row >= 32;
+            const int r = row & 31;
+            const int64_t gr = isb ? (n0 + r < n ? n0 + r : n - 1) : (p0 + r < p ? p0 + r : p - 1);
+            const uint16_t* src = (isb ? wd : xd) + gr * nb;
+            const uint32_t lo = src[2 * d];
+            const uint32_t hi = 2 * d + 1 < nb ? src[2 * d + 1] : 0u;
+            (isb ? sB : sA)[r * spw + d] = lo | (hi << 16);
+        }
+    }
+    __syncthreads();
+
+    // ---- this wave's K range and LDS slice
+    const int b_lo = (int)((int64_t)nb * wave / 4), b_hi = (int)((int64_t)nb * (wave + 1) / 4);
+    const int nblk = b_hi - b_lo;
+    unsigned char* slA = lds + wave * kWaveSlice;      // [32 rows][kPitch]
+    unsigned char* slB = slA + 32 * kPitch;
+
+    // copy lanes: lane l moves bytes 16*(l%8) of row 8*j + l/8 (j = 0..3)
+    const int cr = lane >> 3, cb = (lane & 7) * 16;
+    const int8_t* ga[4];
+    const int8_t* gb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 8 * j + cr;
+        const int64_t pr = p0 + r < p ? p0 + r : p - 1;
+        const int64_t nr = n0 + r < n ? n0 + r : n - 1;
+        ga[j] = xq + pr * k;
+        gb[j] = wq + nr * k;
+    }
+
+    // MFMA lanes: the 32x32 result layout gives lane (i, h) rows
+    // 8*(r/4) + 4*h + r%4, r = 0..15; operand row i is taken from tile row pl(i)
+    // so that the lane's 16 results are the 16 consecutive tile rows 16*h + r.
+    const int i = lane & 31, h = lane >> 5;
     const int pl = 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
-    const int64_t pa = p0 + 32 * wp + pl < p ? p0 + 32 * wp + pl : p - 1;
-    const int64_t nbw = n0 + 32 * wn + i < n ? n0 + 32 * wn + i : n - 1;
-    const int8_t* arow = xq + pa * k + 16 * h;
-    const int8_t* brow = wq + nbw * k + 16 * h;
+    const bool lo_half = h == 0;
 
     float acc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    const i32x16 zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-    for (int b0 = 0; b0 < nb; b0 += kPrefillKt) {
-        const int nblk = nb - b0 < kPrefillKt ? nb - b0 : kPrefillKt;
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < 64 * nblk; idx += 256) {
-            const int row = idx & 63, blk = idx >> 6;
-            const int64_t pr = p0 + row < p ? p0 + row : p - 1;
-            const int64_t nr = n0 + row < n ? n0 + row : n - 1;
-            xs_l[blk * 64 + row] = half_bits_to_float(xd[pr * nb + b0 + blk]);
-            ws_l[blk * 64 + row] = half_bits_to_float(wd[nr * nb + b0 + blk]);
-        }
-        __syncthreads();
-        for (int bl = 0; bl < nblk; ++bl) {
-            const int64_t off = (int64_t)(b0 + bl) * 32;
-            const i32x4 A = *reinterpret_cast<const i32x4*>(arow + off);
-            const i32x4 B = *reinterpret_cast<const i32x4*>(brow + off);
-            const i32x16 c = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, zero, 0, 0, 0);
-            const float wsc = ws_l[bl * 64 + 32 * wn + i];
-            const float4* xs4 = reinterpret_cast<const float4*>(&xs_l[bl * 64 + 32 * wp + 16 * h]);
-            const float4 s0 = xs4[0], s1 = xs4[1], s2 = xs4[2], s3 = xs4[3];
-            const float xsv[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
-                                   s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+    const int ngroups = (nblk + kGroup - 1) / kGroup;
+    i32x4 ra[4], rb[4];
+    auto fetch = [&](int g) {
+        // 128 bytes of each row starting at block b_lo + 4g; the byte offset is
+        // clamped to the row so the last group never reads past it
+        int64_t off = (int64_t)(b_lo + kGroup * g) * 32 + cb;
+        off = off < k - 16 ? off : k - 16;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = fmaf((float)c[r], xsv[r] * wsc, acc[r]);
+        for (int j = 0; j < 4; ++j) {
+            ra[j] = *reinterpret_cast<const i32x4*>(ga[j] + off);
+            rb[j] = *reinterpret_cast<const i32x4*>(gb[j] + off);
+        }
+    };
+    const i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const f32x16 zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+    if (ngroups > 0) fetch(0);
+    for (int g = 0; g < ngroups; ++g) {
+        // registers -> this wave's LDS slice (LDS operations of one wave stay in
+        // order, so the reads of the previous group are done before this write)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<i32x4*>(slA + (8 * j + cr) * kPitch + cb) = ra[j];
+            *reinterpret_cast<i32x4*>(slB + (8 * j + cr) * kPitch + cb) = rb[j];
+        }
+        if (g + 1 < ngroups) fetch(g + 1);
+        const int nu = nblk - kGroup * g < kGroup ? nblk - kGroup * g : kGroup;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            if (u >= nu) break;                        // uniform across the wave
+            const i32x4 a = *reinterpret_cast<const i32x4*>(slA + pl * kPitch + u * 32 + 16 * h);
+            const i32x4 b = *reinterpret_cast<const i32x4*>(slB + i * kPitch + u * 32 + 16 * h);
+            const i32x16 c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zi, 0, 0, 0);
+            const int blk = b_lo + kGroup * g + u;
+            const uint32_t wa = sA[pl * spw + (blk >> 1)];
+            const uint32_t wb = sB[i * spw + (blk >> 1)];
+            const uint16_t ha = (uint16_t)((blk & 1) ? (wa >> 16) : (wa & 0xFFFFu));
+            const uint16_t hb = (uint16_t)((blk & 1) ? (wb >> 16) : (wb & 0xFFFFu));
+            // scale outer product: lanes 0..31 carry k = 0, lanes 32..63 the zero k = 1
+            const float xs = lo_half ? half_bits_to_float(ha) : 0.0f;
+            const float ws = lo_half ? half_bits_to_float(hb) : 0.0f;
+            const f32x16 t = __builtin_amdgcn_mfma_f32_32x32x2f32(xs, ws, zf, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = fmaf((float)c[r], t[r], acc[r]);
         }
     }
 
-    const int64_t nout = n0 + 32 * wn + i;
-    if (nout < n) {
+    // ---- combine the four partial tiles in a fixed order (wave 0 + 1 + 2 + 3)
+    __syncthreads();                                   // every wave is done with its slice
+    float* part = reinterpret_cast<float*>(lds);       // [3][16][64], reuses the slices
+    if (wave > 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part[((wave - 1) * 16 + r) * 64 + lane] = acc[r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int64_t nout = n0 + i;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int64_t pout = p0 + 32 * wp + 16 * h + r;
-            if (pout < p) y[pout * n + nout] = acc[r];
+            const float v = ((acc[r] + part[r * 64 + lane]) + part[(16 + r) * 64 + lane]) +
+                            part[(32 + r) * 64 + lane];
+            const int64_t pout = p0 + 16 * h + r;
+            if (nout < n && pout < p) y[pout * n + nout] = v;
         }
     }
+}
+
+size_t prefill_lds_bytes(int64_t k) {
+    return 4 * (size_t)kWaveSlice + 2 * 32 * (size_t)scale_pitch_dw((int)(k / 32)) * 4;
 }
 
 hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t p,
@@ -91,9 +189,11 @@ hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
                           const DeviceInfo& dev, hipStream_t stream) {
     (void)dev;
     const int nb = (int)(k / 32);
-    const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((p + 63) / 64));
+    const int64_t ntn = (n + 31) / 32, ntp = (p + 31) / 32;
+    const int64_t grid = 8 * ntp * ((ntn + 7) / 8);
+    const size_t lds = prefill_lds_bytes(k);
     (void)hipGetLastError();
-    prefill_kernel<<<grid, 256, 0, stream>>>(wq, wd, n, nb, p, xq, xd, y);
+    prefill_kernel<<<(unsigned)grid, 256, lds, stream>>>(wq, wd, n, nb, p, xq, xd, y);
     return hipGetLastError();
 }
 

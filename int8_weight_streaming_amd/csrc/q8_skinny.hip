@@ -8,8 +8,8 @@
 // weight bytes / bandwidth].
 //
 // Work layout (wave64):
-//  * A lane group of G lanes (G = 16 for tall matrices, 64 for short ones)
-//    owns R weight rows.  The rows are cut into 16-byte chunks (half a Q8
+//  * A lane group of G lanes (G = 16 for tall matrices, 32 or 64 for short
+//    ones) owns R weight rows.  The rows are cut into 16-byte chunks (half a Q8
 //    block); lane g takes chunks g, g+G, g+2G, ..., so one load instruction of a
 //    group reads G*16 contiguous bytes of a row.  Weight loads are non-temporal
 //    (streamed once, kept out of the caches) and are issued before the
@@ -268,15 +268,22 @@ static hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int 
                            const void* x, const uint16_t* xd, float* y,
                            const DeviceInfo& dev, hipStream_t stream) {
     (void)hipGetLastError();
-    // Tall matrices: 16-lane groups, 2 rows per group (4 from batch 4 up, so
-    // each activation chunk read from LDS serves more rows), 6 chunks per lane
-    // per K tile (K = 1536 in one tile).  Short matrices: one wave per row so
-    // the workgroups still cover every compute unit.
+    // Tall matrices: 16-lane groups, 2 rows per group (4 from batch 4 up, so each
+    // activation chunk read from LDS serves more rows), 6 chunks per lane per K
+    // tile (K = 1536 in one tile).  Shorter matrices need smaller row tiles to
+    // cover every compute unit: 32-lane groups, one row each, with the K tile
+    // sized to K at batch 1-2 (measured per Mimir shape under graph replay), and
+    // one wave per row for larger batches.
     constexpr int RB = M >= 4 ? 4 : 2;
     const int64_t tall_wgs = (n + 16 * RB - 1) / (16 * RB);
-    if (tall_wgs >= 2 * (int64_t)dev.cu_count)
+    if (tall_wgs >= (int64_t)dev.cu_count)
         return launch_cfg<M, ACT, 16, RB, 6>(wq, wd, n, nb, x, xd, y, stream);
-    return launch_cfg<M, ACT, 64, 1, 2>(wq, wd, n, nb, x, xd, y, stream);
+    if constexpr (M <= 2) {
+        if (nb <= 48) return launch_cfg<M, ACT, 32, 1, 3>(wq, wd, n, nb, x, xd, y, stream);
+        return launch_cfg<M, ACT, 32, 1, 8>(wq, wd, n, nb, x, xd, y, stream);
+    } else {
+        return launch_cfg<M, ACT, 64, 1, 2>(wq, wd, n, nb, x, xd, y, stream);
+    }
 }
 
 template <int ACT>

@@ -282,7 +282,7 @@ def _prefill_case(n, k, p, seed):
 
 
 @pytest.mark.parametrize("n,k,p", [(1, 32, 1), (64, 64, 64), (100, 96, 11), (65, 2080, 100),
-                                   (300, 4096, 256), (33, 1536, 257)])
+                                   (300, 4096, 256), (33, 1536, 257), (40, 7104, 37), (257, 160, 300)])
 def test_prefill_small(n, k, p):
     log(f"prefill n={n} k={k} p={p}")
     wq, wd, xq, xd = _prefill_case(n, k, p, 6000 + n + k + p)
