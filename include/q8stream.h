@@ -123,9 +123,11 @@ q8_status q8_gemm_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_
                          int64_t m, int act, const void* x, const uint16_t* xd,
                          float* y, hipStream_t stream);
 
-/* Q8 x Q8 prefill product for p activation rows (0 <= p <= 4,194,240) and
- * K <= 7104 (the scales of a workgroup's rows are staged whole in LDS; larger K
- * returns Q8_ERR_SHAPE):
+/* Q8 x Q8 prefill product for p activation rows (0 <= p <= 4,194,240).  A
+ * workgroup keeps the binary16 scales of its rows for the whole of K in LDS:
+ * 36 KiB + 128 bytes per 32-element block must fit the device's per-workgroup
+ * LDS (K <= 7168 with 64 KiB, K <= 31744 with 160 KiB); a larger K returns
+ * Q8_ERR_SHAPE, checked after the device check, with nothing enqueued.
  * y[t][j] = sum_b wd[j][b] * xd[t][b] * sum_{i<32} wq[j][32b+i] * xq[t][32b+i],
  * the int32 block sums taken on the int8 matrix cores, each block folded into an
  * fp32 accumulator with its two scales [fak MODEL-BASELINE-RESULTS, ACT 4,

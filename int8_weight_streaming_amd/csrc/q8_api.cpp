@@ -66,8 +66,14 @@ q8_status device_for(hipStream_t stream, const q8::DeviceInfo** info) {
             }
             const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
                             (prop.gcnArchName[6] == 0 || prop.gcnArchName[6] == ':');
-            g_dev_state[dev] = ok ? 1 : -1;
             g_dev_info[dev].cu_count = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+            g_dev_info[dev].max_lds = prop.sharedMemPerBlock > 0 ? (size_t)prop.sharedMemPerBlock : 65536;
+            if (ok && g_dev_info[dev].max_lds > 65536 &&
+                q8::prefill_prepare(g_dev_info[dev]) != hipSuccess) {
+                (void)hipGetLastError();
+                g_dev_info[dev].max_lds = 65536;   // the default every kernel may use
+            }
+            g_dev_state[dev] = ok ? 1 : -1;
         }
         if (g_dev_state[dev] != 1) {
             t_last_hip_error = 0;
@@ -182,13 +188,13 @@ q8_status q8_gemm_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
     Q8_TRY(check_rows(n, k));
     Q8_TRY(check_rows(p, k));
     if (p > kMaxPrefillRows) return Q8_ERR_SHAPE;
-    if (q8::prefill_lds_bytes(k) > q8::kPrefillMaxLds) return Q8_ERR_SHAPE;
     if (n == 0 || p == 0) return Q8_OK;
     if (!wq || !wd || !xq || !xd || !y) return Q8_ERR_NULL;
     if (!aligned16(wq) || !aligned16(wd) || !aligned16(xq) || !aligned16(xd) || !aligned16(y))
         return Q8_ERR_ALIGN;
     const q8::DeviceInfo* dev = nullptr;
     Q8_TRY(device_for(stream, &dev));
+    if (q8::prefill_lds_bytes(k) > dev->max_lds) return Q8_ERR_SHAPE;
     return finish(q8::launch_prefill(wq, wd, n, k, p, xq, xd, y, *dev, stream));
 }
 

@@ -9,6 +9,7 @@ namespace q8 {
 
 struct DeviceInfo {
     int cu_count;
+    size_t max_lds;   // largest LDS allocation of one workgroup, bytes
 };
 
 // Each launcher enqueues on `stream` and returns the launch's hipError_t.
@@ -24,10 +25,10 @@ hipError_t launch_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_
 hipError_t launch_block_dots(const int8_t* wq, int64_t n, int64_t k, int m, const int8_t* xq,
                              int32_t* isum, const DeviceInfo& dev, hipStream_t stream);
 
-// Dynamic LDS of the prefill kernel for a given K; calls whose K would need more
-// than kPrefillMaxLds are refused before any launch.
+// LDS the prefill kernel needs for a given K, and the one-time per-device setup
+// that lets it use up to dev.max_lds.
 size_t prefill_lds_bytes(int64_t k);
-constexpr size_t kPrefillMaxLds = 65536;
+hipError_t prefill_prepare(const DeviceInfo& dev);
 
 hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t p,
                           const int8_t* xq, const uint16_t* xd, float* y,

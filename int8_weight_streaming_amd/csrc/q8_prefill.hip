@@ -27,8 +27,11 @@
 // operand slices are then read from LDS (row pitch padded to 144 bytes so the
 // 16-byte reads of 32 rows are bank-conflict free).  Gathering the operand
 // slices straight from global memory touches 32 cache lines per instruction
-// and measured 5-8x slower.  The workgroup's binary16 scales for the whole K
-// range are staged once.  Workgroups that share a weight tile get ids that land
+// and measured 5-8x slower.  The next step is fetched into registers while the
+// current one is multiplied.  The binary16 scales of the tile's rows (one
+// contiguous range per operand) are copied to LDS once, coalesced, while the
+// first step is in flight.
+// Workgroups that share a weight tile get ids that land
 // on the same XCD (ids are dealt round-robin to the 8 XCDs), so its L2 fetches
 // each weight tile from HBM once.
 #include "q8_device.hpp"
@@ -42,9 +45,11 @@ constexpr int kGroup = 4;                      // blocks per pipeline step (128 
 constexpr int kPitch = 144;                    // LDS bytes per staged row (128 + 16 pad)
 constexpr int kWaveSlice = 2 * 32 * kPitch;    // A and B rows of one wave: 9216 B
 
-// Odd number of dwords per staged scale row: 32 lanes reading one scale of
-// 32 different rows hit 32 different banks.
-__host__ __device__ constexpr int scale_pitch_dw(int nb) { return ((nb + 1) / 2) | 1; }
+// One pipeline step of one wave: 16 bytes of each of 4 + 4 copied rows.
+struct Stage {
+    i32x4 a[4], b[4];
+};
+constexpr int kScaleBatch = 16;                // binary16 scales copied per thread per batch
 
 __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__ wq,
                                                       const uint16_t* __restrict__ wd, int64_t n,
@@ -63,25 +68,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t p0 = (int64_t)tp * 32, n0 = (int64_t)tn * 32;
     const int64_t k = (int64_t)nb * 32;
-    const int spw = scale_pitch_dw(nb);
-    uint32_t* sA = reinterpret_cast<uint32_t*>(lds + 4 * kWaveSlice);   // [32][spw] dwords
-    uint32_t* sB = sA + 32 * spw;
-
-    // ---- stage every scale of the tile's 32 activation and 32 weight rows
-    {
-        const int per_row = (nb + 1) / 2;              // dwords of binary16 pairs
-        for (int t = threadIdx.x; t < 64 * per_row; t += 256) {
-            const int row = t / per_row, d = t % per_row;
-            const bool isb = row >= 32;
-            const int r = row & 31;
-            const int64_t gr = isb ? (n0 + r < n ? n0 + r : n - 1) : (p0 + r < p ? p0 + r : p - 1);
-            const uint16_t* src = (isb ? wd : xd) + gr * nb;
-            const uint32_t lo = src[2 * d];
-            const uint32_t hi = 2 * d + 1 < nb ? src[2 * d + 1] : 0u;
-            (isb ? sB : sA)[r * spw + d] = lo | (hi << 16);
-        }
-    }
-    __syncthreads();
 
     // ---- this wave's K range and LDS slice
     const int b_lo = (int)((int64_t)nb * wave / 4), b_hi = (int)((int64_t)nb * (wave + 1) / 4);
@@ -108,37 +94,71 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
     const int i = lane & 31, h = lane >> 5;
     const int pl = 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
     const bool lo_half = h == 0;
+    // binary16 scales of the tile's 32 activation rows and 32 weight rows,
+    // [row][nb] each, behind the four wave slices
+    uint16_t* sA = reinterpret_cast<uint16_t*>(lds + 4 * kWaveSlice);
+    uint16_t* sB = sA + 32 * nb;
 
     float acc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
     const int ngroups = (nblk + kGroup - 1) / kGroup;
-    i32x4 ra[4], rb[4];
-    auto fetch = [&](int g) {
-        // 128 bytes of each row starting at block b_lo + 4g; the byte offset is
-        // clamped to the row so the last group never reads past it
+    auto fetch = [&](Stage& st, int g) {
+        // 128 bytes of each copied row from block b_lo + 4g on; the offset is
+        // clamped to the row so the last step never reads past it
         int64_t off = (int64_t)(b_lo + kGroup * g) * 32 + cb;
         off = off < k - 16 ? off : k - 16;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            ra[j] = *reinterpret_cast<const i32x4*>(ga[j] + off);
-            rb[j] = *reinterpret_cast<const i32x4*>(gb[j] + off);
+            st.a[j] = *reinterpret_cast<const i32x4*>(ga[j] + off);
+            st.b[j] = *reinterpret_cast<const i32x4*>(gb[j] + off);
         }
     };
     const i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     const f32x16 zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-    if (ngroups > 0) fetch(0);
+    // Step g: copy the staged step into the LDS slice, keep its scales, refill
+    // the stage with step g + 1 (unconditionally: addresses are clamped in
+    // bounds, so the compiler counts outstanding loads exactly), then multiply
+    // step g (nothing past the wave's blocks).  LDS operations of one wave stay
+    // in order, so the previous step's reads are done before this write.
+    Stage st;
+    fetch(st, 0);                                      // first step in flight ...
+    {
+        // ... while the scales are copied: the 32 rows of a tile are one
+        // contiguous range of the scale array, so consecutive lanes read
+        // consecutive scales; rows past the matrix get scale 0.
+        const int64_t na = (int64_t)((p0 + 32 < p ? p0 + 32 : p) - p0) * nb;
+        const int64_t nbv = (int64_t)((n0 + 32 < n ? n0 + 32 : n) - n0) * nb;
+        const uint16_t* srcA = xd + p0 * nb;
+        const uint16_t* srcB = wd + n0 * nb;
+        const int total = 64 * nb;                     // A then B
+        for (int e0 = 0; e0 < total; e0 += 256 * kScaleBatch) {
+            uint16_t v[kScaleBatch];
+#pragma unroll
+            for (int q = 0; q < kScaleBatch; ++q) {
+                const int e = e0 + q * 256 + (int)threadIdx.x;
+                const bool isb = e >= 32 * nb;
+                const int64_t f = isb ? e - 32 * nb : e;
+                v[q] = 0;
+                if (e < total && f < (isb ? nbv : na)) v[q] = (isb ? srcB : srcA)[f];
+            }
+#pragma unroll
+            for (int q = 0; q < kScaleBatch; ++q) {
+                const int e = e0 + q * 256 + (int)threadIdx.x;
+                if (e < total) sA[e] = v[q];           // sB follows sA
+            }
+        }
+    }
+    __syncthreads();
     for (int g = 0; g < ngroups; ++g) {
-        // registers -> this wave's LDS slice (LDS operations of one wave stay in
-        // order, so the reads of the previous group are done before this write)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<i32x4*>(slA + (8 * j + cr) * kPitch + cb) = ra[j];
-            *reinterpret_cast<i32x4*>(slB + (8 * j + cr) * kPitch + cb) = rb[j];
+            *reinterpret_cast<i32x4*>(slA + (8 * j + cr) * kPitch + cb) = st.a[j];
+            *reinterpret_cast<i32x4*>(slB + (8 * j + cr) * kPitch + cb) = st.b[j];
         }
-        if (g + 1 < ngroups) fetch(g + 1);
+        fetch(st, g + 1);
         const int nu = nblk - kGroup * g < kGroup ? nblk - kGroup * g : kGroup;
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
@@ -146,14 +166,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
             const i32x4 a = *reinterpret_cast<const i32x4*>(slA + pl * kPitch + u * 32 + 16 * h);
             const i32x4 b = *reinterpret_cast<const i32x4*>(slB + i * kPitch + u * 32 + 16 * h);
             const i32x16 c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zi, 0, 0, 0);
-            const int blk = b_lo + kGroup * g + u;
-            const uint32_t wa = sA[pl * spw + (blk >> 1)];
-            const uint32_t wb = sB[i * spw + (blk >> 1)];
-            const uint16_t ha = (uint16_t)((blk & 1) ? (wa >> 16) : (wa & 0xFFFFu));
-            const uint16_t hb = (uint16_t)((blk & 1) ? (wb >> 16) : (wb & 0xFFFFu));
             // scale outer product: lanes 0..31 carry k = 0, lanes 32..63 the zero k = 1
-            const float xs = lo_half ? half_bits_to_float(ha) : 0.0f;
-            const float ws = lo_half ? half_bits_to_float(hb) : 0.0f;
+            const int blk = b_lo + kGroup * g + u;
+            const float xs = lo_half ? half_bits_to_float(sA[pl * nb + blk]) : 0.0f;
+            const float ws = lo_half ? half_bits_to_float(sB[i * nb + blk]) : 0.0f;
             const f32x16 t = __builtin_amdgcn_mfma_f32_32x32x2f32(xs, ws, zf, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = fmaf((float)c[r], t[r], acc[r]);
@@ -181,7 +197,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
 }
 
 size_t prefill_lds_bytes(int64_t k) {
-    return 4 * (size_t)kWaveSlice + 2 * 32 * (size_t)scale_pitch_dw((int)(k / 32)) * 4;
+    return 4 * (size_t)kWaveSlice + 2 * 32 * (size_t)(k / 32) * 2;
+}
+
+hipError_t prefill_prepare(const DeviceInfo& dev) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
 }
 
 hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t p,
@@ -191,8 +212,8 @@ hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
     const int nb = (int)(k / 32);
     const int64_t ntn = (n + 31) / 32, ntp = (p + 31) / 32;
     const int64_t grid = 8 * ntp * ((ntn + 7) / 8);
-    const size_t lds = prefill_lds_bytes(k);
     (void)hipGetLastError();
+    const size_t lds = prefill_lds_bytes(k);
     prefill_kernel<<<(unsigned)grid, 256, lds, stream>>>(wq, wd, n, nb, p, xq, xd, y);
     return hipGetLastError();
 }

@@ -282,13 +282,27 @@ def _prefill_case(n, k, p, seed):
 
 
 @pytest.mark.parametrize("n,k,p", [(1, 32, 1), (64, 64, 64), (100, 96, 11), (65, 2080, 100),
-                                   (300, 4096, 256), (33, 1536, 257), (40, 7104, 37), (257, 160, 300)])
+                                   (300, 4096, 256), (33, 1536, 257), (40, 7168, 37), (257, 160, 300)])
 def test_prefill_small(n, k, p):
     log(f"prefill n={n} k={k} p={p}")
     wq, wd, xq, xd = _prefill_case(n, k, p, 6000 + n + k + p)
     y = q8.gemm_prefill(to_dev(wq), to_dev(wd), to_dev(xq), to_dev(xd))
     torch.cuda.synchronize()
     assert_close(to_host(y), oracle.q8q8(wq, wd, xq, xd), f"prefill n={n} k={k} p={p}")
+
+
+def test_prefill_long_k_exact_or_refused():
+    """K beyond the 64 KiB-LDS bound: either computed correctly (devices with a
+    larger per-workgroup LDS) or refused with Q8_ERR_SHAPE -- never wrong."""
+    n, k, p = 70, 8224, 40
+    wq, wd, xq, xd = _prefill_case(n, k, p, 6100)
+    try:
+        y = q8.gemm_prefill(to_dev(wq), to_dev(wd), to_dev(xq), to_dev(xd))
+    except q8.Q8Error as e:
+        assert e.status == 2
+        return
+    torch.cuda.synchronize()
+    assert_close(to_host(y), oracle.q8q8(wq, wd, xq, xd), "prefill long K")
 
 
 def test_prefill_p256_config():
