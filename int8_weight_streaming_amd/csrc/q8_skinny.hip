@@ -268,18 +268,18 @@ static hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int 
                            const void* x, const uint16_t* xd, float* y,
                            const DeviceInfo& dev, hipStream_t stream) {
     (void)hipGetLastError();
-    // Tall matrices: 16-lane groups, 2 rows per group (4 from batch 4 up, so each
-    // activation chunk read from LDS serves more rows), 6 chunks per lane per K
-    // tile (K = 1536 in one tile).  Shorter matrices need smaller row tiles to
-    // cover every compute unit: 32-lane groups, one row each, with the K tile
-    // sized to K at batch 1-2 (measured per Mimir shape under graph replay), and
-    // one wave per row for larger batches.
-    constexpr int RB = M >= 4 ? 4 : 2;
-    const int64_t tall_wgs = (n + 16 * RB - 1) / (16 * RB);
+    // Configurations measured per Mimir shape (graph replay, batch 1 and 8):
+    //  * tall matrices (>= 32 rows per compute unit): 16-lane groups, 2 rows per
+    //    group, 6 chunks per lane per K tile (K = 1536 in one tile);
+    //  * shorter matrices need smaller row tiles to cover every compute unit:
+    //    32-lane groups, one row each, K tile = 96 chunks (K = 1536 in one tile);
+    //    for longer K, 32-lane groups with a 256-chunk tile at batch 1-2
+    //    (activations in registers) and one wave per row above that.
+    const int64_t tall_wgs = (n + 31) / 32;
     if (tall_wgs >= (int64_t)dev.cu_count)
-        return launch_cfg<M, ACT, 16, RB, 6>(wq, wd, n, nb, x, xd, y, stream);
+        return launch_cfg<M, ACT, 16, 2, 6>(wq, wd, n, nb, x, xd, y, stream);
+    if (nb <= 48) return launch_cfg<M, ACT, 32, 1, 3>(wq, wd, n, nb, x, xd, y, stream);
     if constexpr (M <= 2) {
-        if (nb <= 48) return launch_cfg<M, ACT, 32, 1, 3>(wq, wd, n, nb, x, xd, y, stream);
         return launch_cfg<M, ACT, 32, 1, 8>(wq, wd, n, nb, x, xd, y, stream);
     } else {
         return launch_cfg<M, ACT, 64, 1, 2>(wq, wd, n, nb, x, xd, y, stream);
