@@ -133,21 +133,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
         const int64_t nbv = (int64_t)((n0 + 32 < n ? n0 + 32 : n) - n0) * nb;
         const uint16_t* srcA = xd + p0 * nb;
         const uint16_t* srcB = wd + n0 * nb;
-        const int total = 64 * nb;                     // A then B
-        for (int e0 = 0; e0 < total; e0 += 256 * kScaleBatch) {
+        const int total = 64 * nb;
+        const int total_pad = (total + 255) & ~255;    // uniform trip counts, no masked lanes
+        for (int e0 = 0; e0 < total_pad; e0 += 256 * kScaleBatch) {
             uint16_t v[kScaleBatch];
 #pragma unroll
             for (int q = 0; q < kScaleBatch; ++q) {
                 const int e = e0 + q * 256 + (int)threadIdx.x;
                 const bool isb = e >= 32 * nb;
                 const int64_t f = isb ? e - 32 * nb : e;
-                v[q] = 0;
-                if (e < total && f < (isb ? nbv : na)) v[q] = (isb ? srcB : srcA)[f];
+                const bool valid = e < total && f < (isb ? nbv : na);
+                const uint16_t val = (isb ? srcB : srcA)[valid ? f : 0];   // index 0: row p0 / n0
+                v[q] = valid ? val : (uint16_t)0;
             }
 #pragma unroll
             for (int q = 0; q < kScaleBatch; ++q) {
                 const int e = e0 + q * 256 + (int)threadIdx.x;
-                if (e < total) sA[e] = v[q];           // sB follows sA
+                sA[e < total_pad ? e : total_pad] = v[q];   // slot total_pad is scratch
             }
         }
     }
@@ -197,7 +199,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
 }
 
 size_t prefill_lds_bytes(int64_t k) {
-    return 4 * (size_t)kWaveSlice + 2 * 32 * (size_t)(k / 32) * 2;
+    const size_t total_pad = ((size_t)64 * (size_t)(k / 32) + 255) & ~(size_t)255;
+    return 4 * (size_t)kWaveSlice + (total_pad + 2) * 2;
 }
 
 hipError_t prefill_prepare(const DeviceInfo& dev) {
