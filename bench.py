@@ -317,6 +317,8 @@ def main() -> int:
     ap.add_argument("--metric-only", action="store_true",
                     help="time only the headline GEMV (no other workloads, no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the P=256 prefill GEMMs (for hardware-counter passes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the weight-streaming products shard by output "
@@ -335,6 +337,15 @@ def main() -> int:
     torch.cuda.set_device(0)
     q8.load_library()
     state_before = gpu_state()
+
+    if args.prefill_only:
+        weights = {}
+        for proj, (name, n_, k_) in enumerate(wl.BLOCK_SHAPES):
+            if name != "o":
+                weights[(0, proj)] = quantize_on_device(
+                    q8, wl.normal_weights(wl.mimir_weight_seed(0, proj), n_, k_), dev)
+        print(json.dumps({"prefill_p256": bench_prefill(q8, wl, dev, weights, reps=10)}), flush=True)
+        return 0
 
     # ---- headline: lm_head-shaped GEMV, batch 1
     cfg = wl.CONFIGS["lm_head_gemv_262144x1536_b1"]
