@@ -11,29 +11,41 @@
 // On gfx950 one v_mfma_i32_32x32x32_i8 covers exactly one 32-wide Q8 block of
 // a 32 x 32 output tile, so every block sum comes straight from the matrix core
 // as an exact int32.  The per-(t, j) scale product wd*xd of the same block is a
-// rank-1 outer product: a v_mfma_f32_32x32x2_f32 with a single non-zero k term
-// produces it in the same register layout, exactly (every binary16 value,
-// subnormals included, is a normal fp32 number, and a product of two of them
-// needs at most 22 significant bits).  The vector ALUs then only convert and
+// rank-1 outer product, produced exactly by a matrix-core instruction with a
+// single non-zero k term in the same register layout (a product of two
+// binary16 numbers, subnormals included, needs at most 22 significant bits and
+// lies in fp32's normal range).  The vector ALUs then only convert and
 // accumulate: two operations per output and block.
 //
-// Work layout.  A workgroup computes one 32 x 32 output tile; its four waves
-// take contiguous quarters of the K blocks (more waves in flight), and the four
-// partial tiles are added through LDS in a fixed order, so results are bitwise
-// reproducible.  Operands are K-contiguous (codes [rows][K]).  Each wave copies
-// its 32 activation rows and 32 weight rows, four blocks (128 bytes) per row at
-// a time, into its own LDS slice with full-cache-line 16-byte loads (eight
-// lanes per row), prefetching the next four blocks into registers; the MFMA
-// operand slices are then read from LDS (row pitch padded to 144 bytes so the
-// 16-byte reads of 32 rows are bank-conflict free).  Gathering the operand
-// slices straight from global memory touches 32 cache lines per instruction
-// and measured 5-8x slower.  The next step is fetched into registers while the
-// current one is multiplied.  The binary16 scales of the tile's rows (one
-// contiguous range per operand) are copied to LDS once, coalesced, while the
-// first step is in flight.
-// Workgroups that share a weight tile get ids that land
-// on the same XCD (ids are dealt round-robin to the 8 XCDs), so its L2 fetches
-// each weight tile from HBM once.
+// Work layout (both kernels).  A 32 x 32 output tile is computed by the four
+// waves of a workgroup, each over a contiguous quarter of the K blocks, and the
+// four partial tiles are added through LDS in a fixed order (wave 0 + 1 + 2 +
+// 3), so results are bitwise reproducible and identical between the kernels.
+// Operands are K-contiguous (codes [rows][K]); each wave copies its 32
+// activation rows and 32 weight rows four blocks (128 bytes per row) at a time
+// into its own LDS slice with full-cache-line 16-byte loads (eight lanes per
+// row) and reads the MFMA operand slices from there (row pitch padded to 144
+// bytes, so the 16-byte reads of 32 rows are bank-conflict free).  Gathering
+// the operand slices straight from global memory touches 32 cache lines per
+// instruction and measured 5-8x slower.
+//
+// prefill_stream_kernel (K a multiple of 512, every shape the model uses) is
+// persistent: three workgroups per CU each walk a list of tiles, and the copy
+// of the next four-block step (possibly the next tile's first) is in flight
+// while the current one is multiplied, so the pipeline never drains between
+// tiles.  Loads go through buffer descriptors built in scalar registers: the
+// per-step advance is scalar arithmetic, rows past the matrix fall outside the
+// descriptor's range and read as zero, and a step past the wave's last tile
+// has an empty range and touches no memory.  The scale outer product is a
+// v_mfma_f32_32x32x16_f16 on the raw binary16 scales, and the int8 product of
+// the next block is issued before the fold of the current one, so the matrix
+// core and the vector ALUs overlap.  Tiles are dealt so that the workgroups of
+// one XCD (ids are dealt round-robin to the 8 XCDs) share its weight rows, so
+// its L2 fetches each weight tile from HBM once.
+//
+// prefill_kernel (any other K) computes one tile per workgroup, copies the
+// tile's scales to LDS once, and uses v_mfma_f32_32x32x2_f32 for the outer
+// product.
 #include "q8_device.hpp"
 #include "q8_internal.hpp"
 
@@ -198,7 +210,207 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
     }
 }
 
+// ------------------------------------------------------------------ streaming
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kStreamSlice = 2 * 32 * kPitch + 64 * 16;   // operand rows + per-lane scales
+constexpr int kStreamLds = 4 * kStreamSlice;              // 40,960 B: three workgroups per CU
+constexpr int kStreamWgPerCu = 3;
+constexpr int64_t kStreamMaxK = int64_t(1) << 24;         // 32-bit buffer offsets
+// raw buffer descriptor word 3 for gfx9-family targets: untyped 32-bit data
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Buffer descriptor over [base, base + bytes); offsets at or past `bytes` read
+// as zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             bytes > 0 ? (int)bytes : 0, kRsrcWord3);
+}
+
+// One four-block step of one wave: 16 bytes of each of 4 + 4 copied rows, and
+// the four binary16 scales of the lane's activation row and weight row.
+struct StreamStage {
+    i32x4 a[4], b[4];
+    i32x2 sa, sb;
+};
+
+// gx workgroups per XCD; XCD x owns the weight tiles [ntn*x/8, ntn*(x+1)/8)
+// and all activation tiles; workgroup j of an XCD takes its local tiles j,
+// j + gx, j + 2 gx, ...  Requires nb % 16 == 0 (whole steps per wave).
+__global__ __launch_bounds__(256) void prefill_stream_kernel(const int8_t* __restrict__ wq,
+                                                             const uint16_t* __restrict__ wd,
+                                                             int64_t n, int nb, int64_t p,
+                                                             const int8_t* __restrict__ xq,
+                                                             const uint16_t* __restrict__ xd,
+                                                             float* __restrict__ y, int gx) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int ntn = (int)((n + 31) / 32), ntp = (int)((p + 31) / 32);
+    const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3;
+    const int tn_lo = (int)((int64_t)ntn * xcd / 8), tn_hi = (int)((int64_t)ntn * (xcd + 1) / 8);
+    const int L = (tn_hi - tn_lo) * ntp;               // tiles of this XCD
+    if (jw >= L) return;                               // whole workgroup leaves
+    const int T = (L - jw + gx - 1) / gx;              // tiles of this workgroup
+    const int S = nb / 16;                             // steps per wave and tile
+    const int Q = T * S;
+    const int64_t k = (int64_t)nb * 32;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    // MFMA lanes: the 32x32 result layout gives lane (i, h) rows
+    // 8*(r/4) + 4*h + r%4, r = 0..15; operand row i is taken from tile row pl(i)
+    // so that the lane's 16 results are the 16 consecutive tile rows 16*h + r.
+    const int i = lane & 31, h = lane >> 5;
+    const int pl = 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+    // copy lanes: lane l moves bytes 16*(l%8) of rows 8*j + l/8 (j = 0..3)
+    const int cr = lane >> 3, cb = (lane & 7) * 16;
+    unsigned char* slA = lds + wave * kStreamSlice;    // [32 rows][kPitch]
+    unsigned char* slB = slA + 32 * kPitch;
+    unsigned char* slS = slB + 32 * kPitch;            // [64 lanes][xd 8 B, wd 8 B]
+
+    int voff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) voff[j] = (8 * j + cr) * (int)k + cb;
+    const int soffA = pl * nb * 2, soffB = i * nb * 2;
+
+    // fetch cursor: the step whose loads are issued next (wave-uniform)
+    int fs = 0, ft = 0, fm = jw;
+    int fp0 = (fm % ntp) * 32, fn0 = (tn_lo + fm / ntp) * 32;
+    auto issue = [&](StreamStage& st) {
+        const bool live = ft < T;
+        const int blk0 = wave * 4 * S + 4 * fs;
+        const int64_t adv = (int64_t)blk0 * 32;
+        const int64_t pv = p - fp0 < 32 ? p - fp0 : 32;
+        const int64_t nv = n - fn0 < 32 ? n - fn0 : 32;
+        const int64_t ra = live ? (int64_t)fp0 * k + adv : 0, rb = live ? (int64_t)fn0 * k + adv : 0;
+        const int64_t rsa = live ? (int64_t)fp0 * nb + blk0 : 0, rsb = live ? (int64_t)fn0 * nb + blk0 : 0;
+        const auto rA = range_rsrc(xq + ra, live ? pv * k - adv : 0);
+        const auto rB = range_rsrc(wq + rb, live ? nv * k - adv : 0);
+        const auto rsA = range_rsrc(xd + rsa, live ? (pv * nb - blk0) * 2 : 0);
+        const auto rsB = range_rsrc(wd + rsb, live ? (nv * nb - blk0) * 2 : 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            st.a[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff[j], 0, 0));
+            st.b[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, voff[j], 0, 0));
+        }
+        st.sa = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rsA, soffA, 0, 0));
+        st.sb = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rsB, soffB, 0, 0));
+        if (++fs == S) {
+            fs = 0;
+            ++ft;
+            fm += gx;
+            fp0 = (fm % ntp) * 32;
+            fn0 = (tn_lo + fm / ntp) * 32;
+        }
+    };
+
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    const i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const f32x16 zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int cs = 0, cm = jw;                               // compute cursor
+
+    // Step q: copy the staged step into the LDS slice, refill the stage with
+    // step q + 1 (scheduling barriers keep every load in issue order, so the
+    // compiler's counted waits stay exact), then multiply step q.  LDS
+    // operations of one wave stay in order, so the previous step's reads are
+    // done before this write.
+    StreamStage st;
+    issue(st);
+    for (int q = 0; q < Q; ++q) {
+        __builtin_amdgcn_sched_barrier(0);
+        *reinterpret_cast<i32x2*>(slS + lane * 16) = st.sa;
+        *reinterpret_cast<i32x2*>(slS + lane * 16 + 8) = st.sb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<i32x4*>(slA + (8 * j + cr) * kPitch + cb) = st.a[j];
+            *reinterpret_cast<i32x4*>(slB + (8 * j + cr) * kPitch + cb) = st.b[j];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue(st);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // scales of the four blocks; lanes 32..63 carry the zero k = 8 term
+        const i32x4 sc = *reinterpret_cast<const i32x4*>(slS + lane * 16);
+        const unsigned sa0 = h ? 0u : (unsigned)sc[0], sa1 = h ? 0u : (unsigned)sc[1];
+        const unsigned sb0 = (unsigned)sc[2], sb1 = (unsigned)sc[3];
+        i32x4 av[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            av[u] = *reinterpret_cast<const i32x4*>(slA + pl * kPitch + u * 32 + 16 * h);
+            bv[u] = *reinterpret_cast<const i32x4*>(slB + i * kPitch + u * 32 + 16 * h);
+        }
+        auto mm = [&](int u, i32x16& c, f32x16& t) {
+            const unsigned wa = (u >> 1) ? sa1 : sa0, wb = (u >> 1) ? sb1 : sb0;
+            const i32x4 va = {(int)((u & 1) ? wa >> 16 : wa & 0xFFFFu), 0, 0, 0};
+            const i32x4 vb = {(int)((u & 1) ? wb >> 16 : wb & 0xFFFFu), 0, 0, 0};
+            c = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[u], bv[u], zi, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va),
+                                                        __builtin_bit_cast(f16x8, vb), zf, 0, 0, 0);
+        };
+        auto fold = [&](const i32x16& c, const f32x16& t) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = fmaf((float)c[r], t[r], acc[r]);
+        };
+        // blocks 0..3, the matrix products of block u + 1 in flight while
+        // block u is folded
+        i32x16 c0, c1;
+        f32x16 t0, t1;
+        mm(0, c0, t0);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(1, c1, t1);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(c0, t0);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(2, c0, t0);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(c1, t1);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(3, c1, t1);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(c0, t0);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(c1, t1);
+
+        if (++cs == S) {
+            // tile done: the four partial tiles go through the waves' own
+            // slices (their operand data is consumed), each wave adds and
+            // stores four of the sixteen result rows, wave 0 + 1 + 2 + 3
+            cs = 0;
+            float* mine = reinterpret_cast<float*>(slA);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = acc[r];
+            __syncthreads();
+            const int64_t p0 = (int64_t)(cm % ntp) * 32, n0 = (int64_t)(tn_lo + cm / ntp) * 32;
+            const int64_t nout = n0 + i;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = 4 * wave + rr;
+                float v = reinterpret_cast<const float*>(lds)[r * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < 4; ++w)
+                    v += reinterpret_cast<const float*>(lds + w * kStreamSlice)[r * 64 + lane];
+                const int64_t pout = p0 + 16 * h + r;
+                if (nout < n && pout < p) y[pout * n + nout] = v;
+            }
+            __syncthreads();                           // slices free for the next step
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            cm += gx;
+        }
+    }
+}
+
+static bool use_stream(int64_t n, int64_t k, int64_t p) {
+    const int64_t ntn = (n + 31) / 32, ntp = (p + 31) / 32;
+    return k % 512 == 0 && k <= kStreamMaxK && ntn * ntp < (int64_t(1) << 31) &&
+           32 * ntp < (int64_t(1) << 31) && 32 * ntn < (int64_t(1) << 31);
+}
+
 size_t prefill_lds_bytes(int64_t k) {
+    if (k % 512 == 0 && k <= kStreamMaxK) return (size_t)kStreamLds;
     const size_t total_pad = ((size_t)64 * (size_t)(k / 32) + 255) & ~(size_t)255;
     return 4 * (size_t)kWaveSlice + (total_pad + 2) * 2;
 }
@@ -211,11 +423,18 @@ hipError_t prefill_prepare(const DeviceInfo& dev) {
 hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t p,
                           const int8_t* xq, const uint16_t* xd, float* y,
                           const DeviceInfo& dev, hipStream_t stream) {
-    (void)dev;
     const int nb = (int)(k / 32);
     const int64_t ntn = (n + 31) / 32, ntp = (p + 31) / 32;
-    const int64_t grid = 8 * ntp * ((ntn + 7) / 8);
     (void)hipGetLastError();
+    if (use_stream(n, k, p)) {
+        const int64_t per_xcd = ((ntn + 7) / 8) * ntp;          // most tiles of one XCD
+        int64_t gx = (int64_t)(dev.cu_count / 8 > 0 ? dev.cu_count / 8 : 1) * kStreamWgPerCu;
+        if (gx > per_xcd) gx = per_xcd;
+        prefill_stream_kernel<<<(unsigned)(8 * gx), 256, kStreamLds, stream>>>(
+            wq, wd, n, nb, p, xq, xd, y, (int)gx);
+        return hipGetLastError();
+    }
+    const int64_t grid = 8 * ntp * ((ntn + 7) / 8);
     const size_t lds = prefill_lds_bytes(k);
     prefill_kernel<<<(unsigned)grid, 256, lds, stream>>>(wq, wd, n, nb, p, xq, xd, y);
     return hipGetLastError();
