@@ -73,6 +73,20 @@ __device__ __forceinline__ int block_dot_i8(const uint32_t w[8], const uint32_t 
     return s;
 }
 
+// ---------------------------------------------------------------- buffer loads
+
+// raw buffer descriptor word 3 for gfx9-family targets: untyped 32-bit data
+constexpr int kRsrcWord3 = 0x00020000;
+// cache-policy bit of a buffer load: non-temporal (streamed once)
+constexpr int kLoadNT = 2;
+
+// Buffer descriptor over [base, base + bytes); offsets at or past `bytes` read
+// as zero without touching memory.  `bytes` must be below 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             bytes > 0 ? (int)bytes : 0, kRsrcWord3);
+}
+
 // ---------------------------------------------------------------- reductions
 
 template <int CTRL>

@@ -219,15 +219,6 @@ constexpr int kStreamSlice = 2 * 32 * kPitch + 64 * 16;   // operand rows + per-
 constexpr int kStreamLds = 4 * kStreamSlice;              // 40,960 B: three workgroups per CU
 constexpr int kStreamWgPerCu = 3;
 constexpr int64_t kStreamMaxK = int64_t(1) << 24;         // 32-bit buffer offsets
-// raw buffer descriptor word 3 for gfx9-family targets: untyped 32-bit data
-constexpr int kRsrcWord3 = 0x00020000;
-
-// Buffer descriptor over [base, base + bytes); offsets at or past `bytes` read
-// as zero without touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                             bytes > 0 ? (int)bytes : 0, kRsrcWord3);
-}
 
 // One four-block step of one wave: 16 bytes of each of 4 + 4 copied rows, and
 // the four binary16 scales of the lane's activation row and weight row.

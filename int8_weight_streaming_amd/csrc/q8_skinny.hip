@@ -268,15 +268,18 @@ static hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int 
                            const void* x, const uint16_t* xd, float* y,
                            const DeviceInfo& dev, hipStream_t stream) {
     (void)hipGetLastError();
-    // Configurations measured per Mimir shape (graph replay, batch 1 and 8):
-    //  * tall matrices (>= 32 rows per compute unit): 16-lane groups, 2 rows per
-    //    group, 6 chunks per lane per K tile (K = 1536 in one tile);
+    // Configurations measured per Mimir shape and batch (graph replay, weights
+    // rotated past the caches, batch 1, 2, 4 and 8):
+    //  * tall matrices: 16-lane groups, 2 rows per group, 6 chunks per lane per
+    //    K tile (K = 1536 in one tile) -- at batch 1-2 from 32 rows per compute
+    //    unit on, above batch 2 only from 128 (below that one workgroup per
+    //    compute unit leaves the per-lane arithmetic of 3-8 rows exposed);
     //  * shorter matrices need smaller row tiles to cover every compute unit:
     //    32-lane groups, one row each, K tile = 96 chunks (K = 1536 in one tile);
     //    for longer K, 32-lane groups with a 256-chunk tile at batch 1-2
     //    (activations in registers) and one wave per row above that.
     const int64_t tall_wgs = (n + 31) / 32;
-    if (tall_wgs >= (int64_t)dev.cu_count)
+    if (tall_wgs >= (int64_t)dev.cu_count * (M <= 2 ? 1 : 4))
         return launch_cfg<M, ACT, 16, 2, 6>(wq, wd, n, nb, x, xd, y, stream);
     if (nb <= 48) return launch_cfg<M, ACT, 32, 1, 3>(wq, wd, n, nb, x, xd, y, stream);
     if constexpr (M <= 2) {

@@ -211,6 +211,34 @@ def test_skinny_large_rows_ragged(m):
     assert_close(_run_skinny(wq, wd, x, xq, xd), oracle.q8q8(wq, wd, xq, xd), f"q8 large m={m}")
 
 
+@pytest.mark.parametrize("m", [3, 8])
+def test_skinny_very_tall_ragged(m):
+    """More than four 32-row tiles per compute unit (the tall layout at every
+    batch size), with a ragged last tile."""
+    n, k = 65536 + 37, 1536
+    log(f"skinny very tall ragged m={m}")
+    wq, wd, x = _w8a16_case(n, k, m, 4100 + m, mixed=True)
+    assert_close(_run_skinny(wq, wd, x), oracle.w8a16(wq, wd, x), f"bf16 very tall m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_skinny_subnormal_bf16_activations(m):
+    """bf16-subnormal activations (in contract: finite) times large weights, so
+    that every output lands in fp32's normal range: a flush of subnormal inputs
+    or products to zero anywhere on the path would show as a wrong result."""
+    n, k = 300, 1536
+    g = wl.rng(4200 + m)
+    w = (g.standard_normal((n, k)) * 1.0e4).astype(np.float32)
+    wq, wd = oracle.quantize_f32(w)
+    x = (g.integers(1, 128, size=(m, k)) | (g.integers(0, 2, size=(m, k)) << 15)).astype(np.uint16)
+    assert np.all(wl.bf16_bits_to_f32(x) != 0) and np.all(np.abs(wl.bf16_bits_to_f32(x)) < 2.0 ** -126)
+    y64 = oracle.w8a16(wq, wd, x)
+    assert np.all(np.abs(y64) < 1e-20) and np.linalg.norm(y64) > 0
+    assert_within_summation_bound(_run_skinny(wq, wd, x), wq, wd, x, f"subnormal x m={m}")
+    y = _run_skinny(wq, wd, x).astype(np.float64)
+    assert np.linalg.norm(y - y64) <= 1e-5 * np.linalg.norm(y64), f"subnormal x m={m}: rel-L2"
+
+
 def test_gemv_1536_config():
     cfg = wl.CONFIGS["gemv_1536x1536_b1"]
     w = wl.normal_weights(cfg["w_seed"], cfg["n"], cfg["k"])
