@@ -194,7 +194,7 @@ q8_status q8_gemm_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
         return Q8_ERR_ALIGN;
     const q8::DeviceInfo* dev = nullptr;
     Q8_TRY(device_for(stream, &dev));
-    if (q8::prefill_lds_bytes(k) > dev->max_lds) return Q8_ERR_SHAPE;
+    if (q8::prefill_lds_bytes(n, k, p, *dev) > dev->max_lds) return Q8_ERR_SHAPE;
     return finish(q8::launch_prefill(wq, wd, n, k, p, xq, xd, y, *dev, stream));
 }
 

@@ -25,9 +25,9 @@ hipError_t launch_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_
 hipError_t launch_block_dots(const int8_t* wq, int64_t n, int64_t k, int m, const int8_t* xq,
                              int32_t* isum, const DeviceInfo& dev, hipStream_t stream);
 
-// LDS the prefill kernel needs for a given K, and the one-time per-device setup
-// that lets it use up to dev.max_lds.
-size_t prefill_lds_bytes(int64_t k);
+// LDS the prefill kernel chosen for this shape needs, and the one-time
+// per-device setup that lets it use up to dev.max_lds.
+size_t prefill_lds_bytes(int64_t n, int64_t k, int64_t p, const DeviceInfo& dev);
 hipError_t prefill_prepare(const DeviceInfo& dev);
 
 hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t p,

@@ -43,6 +43,9 @@
 // one XCD (ids are dealt round-robin to the 8 XCDs) share its weight rows, so
 // its L2 fetches each weight tile from HBM once.
 //
+// prefill_tile64_kernel (K a multiple of 256, enough tiles: the large-P
+// kernel) computes a 64 x 64 tile per workgroup over all of K, below.
+//
 // prefill_kernel (any other K) computes one tile per workgroup, copies the
 // tile's scales to LDS once, and uses v_mfma_f32_32x32x2_f32 for the outer
 // product.
@@ -394,21 +397,232 @@ __global__ __launch_bounds__(256) void prefill_stream_kernel(const int8_t* __res
     }
 }
 
+// ------------------------------------------------------------------ 64 x 64 tiles
+
+// prefill_tile64_kernel<KS>: a workgroup computes a 64 x 64 output tile with
+// KS groups of four waves; each group takes a contiguous 1/KS of the K steps
+// and its four waves the 2 x 2 subtiles of 32 x 32, so every staged operand
+// row serves two waves.  With KS = 2 the groups' partial tiles are added in
+// LDS in a fixed order (group 0 + group 1) at the end; it is for shapes with
+// few tiles, where it halves each wave's chain of steps and puts twice as many
+// waves on every SIMD.  A step is four blocks (128 bytes of each of the 64 +
+// 64 rows plus their scales): each thread loads 4 x 16 bytes of rows t/8 and t/8 + 32 of
+// both operands (8 threads per 128-byte row segment) and wave 0 / 1 load the
+// 8 bytes of scales of one activation / weight row per lane, all through
+// buffer descriptors (rows past the matrix read as zero; a step past K has an
+// empty range).  Two steps are in flight in registers while a third is
+// multiplied from one of two LDS buffers; one barrier per step.
+constexpr int kT64Rows = 64;
+constexpr int kT64Buf = 2 * kT64Rows * kPitch + 2 * kT64Rows * 8;   // one LDS buffer: 19,456 B
+constexpr int kT64Lds = 2 * kT64Buf;               // per group of four waves
+
+struct T64Stage {
+    i32x4 a[2], b[2];
+    i32x2 s;
+};
+
+// Register use is held to four waves per SIMD (128 VGPRs): measured faster
+// than two or three waves with deeper per-wave overlap.
+template <int KS>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void prefill_tile64_kernel(const int8_t* __restrict__ wq,
+                           const uint16_t* __restrict__ wd,
+                           int64_t n, int nb, int64_t p,
+                           const int8_t* __restrict__ xq,
+                           const uint16_t* __restrict__ xd,
+                           float* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int ntn = (int)((n + 63) / 64), ntp = (int)((p + 63) / 64);
+    // id = xcd + 8 * (tp + ntp * c)  ->  weight tile tn = 8c + xcd, activation tile tp
+    const int id = blockIdx.x;
+    const int xcd = id & 7, rest = id >> 3;
+    const int tp = rest % ntp, tn = 8 * (rest / ntp) + xcd;
+    if (tn >= ntn) return;                             // whole padding workgroup leaves
+
+    const int lane = threadIdx.x & 63;
+    const int wg = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int grp = wg >> 2, wave = wg & 3;            // K group, wave inside the group
+    const int64_t p0 = (int64_t)tp * 64, n0 = (int64_t)tn * 64;
+    const int64_t k = (int64_t)nb * 32;
+    const int64_t pv = p - p0 < 64 ? p - p0 : 64, nv = n - n0 < 64 ? n - n0 : 64;
+    const int S = nb / (4 * KS);                       // steps of this group; even
+    const int step0 = grp * S;                         // its first step over all of K
+    unsigned char* const glds = lds + grp * kT64Lds;
+
+    // copy lanes: thread t of the group moves bytes 16*(t%8) of rows t/8 and t/8 + 32
+    const int tg = (int)(threadIdx.x & 255);
+    const int cr = tg >> 3, cb = (tg & 7) * 16;
+    const int voff0 = cr * (int)k + cb, voff1 = (cr + 32) * (int)k + cb;
+    // scale lanes: wave 0 the activation rows, wave 1 the weight rows
+    const int soff = lane * nb * 2;
+
+    auto issue = [&](int lstep, T64Stage& st) {
+        const bool live = lstep < S;
+        const int step = step0 + lstep;
+        const int64_t adv = (int64_t)step * 128;
+        const auto rA = range_rsrc(xq + (live ? p0 * k + adv : 0), live ? pv * k - adv : 0);
+        const auto rB = range_rsrc(wq + (live ? n0 * k + adv : 0), live ? nv * k - adv : 0);
+        const int64_t sblk = (int64_t)step * 4;
+        const uint16_t* sbase = wave == 0 ? xd + p0 * nb + sblk : wd + n0 * nb + sblk;
+        const int64_t sbytes = (!live || wave > 1) ? 0 : (wave == 0 ? pv * nb - sblk : nv * nb - sblk) * 2;
+        const auto rS = range_rsrc(sbytes > 0 ? sbase : xd, sbytes);
+        st.a[0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff0, 0, 0));
+        st.a[1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff1, 0, 0));
+        st.b[0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, voff0, 0, 0));
+        st.b[1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, voff1, 0, 0));
+        st.s = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rS, soff, 0, 0));
+    };
+    // LDS buffer: A rows [64][kPitch], B rows [64][kPitch], A scales [64][8 B], B scales [64][8 B]
+    auto put = [&](int buf, const T64Stage& st) {
+        unsigned char* base = glds + buf * kT64Buf;
+        *reinterpret_cast<i32x4*>(base + cr * kPitch + cb) = st.a[0];
+        *reinterpret_cast<i32x4*>(base + (cr + 32) * kPitch + cb) = st.a[1];
+        *reinterpret_cast<i32x4*>(base + (64 + cr) * kPitch + cb) = st.b[0];
+        *reinterpret_cast<i32x4*>(base + (96 + cr) * kPitch + cb) = st.b[1];
+        if (wave < 2)
+            *reinterpret_cast<i32x2*>(base + 128 * kPitch + (wave * 64 + lane) * 8) = st.s;
+    };
+
+    // MFMA lanes (same layout as the other kernels): lane (i, h) ends with the
+    // 16 consecutive tile rows 16h + r of column i of its wave's subtile.
+    const int i = lane & 31, h = lane >> 5;
+    const int pl = 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+    const int wp = wave & 1, wn = wave >> 1;
+    const int arow = 32 * wp + pl, brow = 64 + 32 * wn + i;
+    const int sa_off = 128 * kPitch + arow * 8, sb_off = 128 * kPitch + (64 + 32 * wn + i) * 8;
+
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    const i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const f32x16 zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int buf) {
+        const unsigned char* base = glds + buf * kT64Buf;
+        const i32x2 sa = *reinterpret_cast<const i32x2*>(base + sa_off);
+        const i32x2 sb = *reinterpret_cast<const i32x2*>(base + sb_off);
+        // scales of the four blocks; lanes 32..63 carry the zero k = 8 term
+        const unsigned sa0 = h ? 0u : (unsigned)sa[0], sa1 = h ? 0u : (unsigned)sa[1];
+        const unsigned sb0 = (unsigned)sb[0], sb1 = (unsigned)sb[1];
+        auto mm = [&](int u, i32x16& c, f32x16& t) {
+            const i32x4 av = *reinterpret_cast<const i32x4*>(base + arow * kPitch + u * 32 + 16 * h);
+            const i32x4 bv = *reinterpret_cast<const i32x4*>(base + brow * kPitch + u * 32 + 16 * h);
+            const unsigned wa = (u >> 1) ? sa1 : sa0, wb = (u >> 1) ? sb1 : sb0;
+            const i32x4 va = {(int)((u & 1) ? wa >> 16 : wa & 0xFFFFu), 0, 0, 0};
+            const i32x4 vb = {(int)((u & 1) ? wb >> 16 : wb & 0xFFFFu), 0, 0, 0};
+            c = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, zi, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va),
+                                                        __builtin_bit_cast(f16x8, vb), zf, 0, 0, 0);
+        };
+        auto fold = [&](const i32x16& c, const f32x16& t) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = fmaf((float)c[r], t[r], acc[r]);
+        };
+        // one block's products at a time: the other waves of the SIMD keep the
+        // matrix core and the vector ALUs busy meanwhile
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            i32x16 c;
+            f32x16 t;
+            mm(u, c, t);
+            fold(c, t);
+        }
+    };
+
+    // Steps 0 and 1 in flight; step 0 to buffer 0; then step s is multiplied
+    // from buffer s % 2 while step s + 1 is copied to the other buffer and
+    // steps s + 2, s + 3 are in flight.  Every load is unconditional (an empty
+    // range past K), so the compiler's counted waits stay exact.
+    // The folds of a step are finished before its barrier (an empty asm that
+    // takes the accumulators as operands), so the matrix products of different
+    // steps are never live together.
+    auto pin = [&]() {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(acc[r]));
+    };
+    T64Stage ra, rb;
+    issue(0, ra);
+    issue(1, rb);
+    put(0, ra);
+    issue(2, ra);
+    __syncthreads();
+    for (int s0 = 0; s0 < S; s0 += 2) {
+        put(1, rb);                                    // step s0 + 1 (S is even)
+        issue(s0 + 3, rb);
+        compute(0);                                    // step s0
+        pin();
+        __syncthreads();
+        if (s0 + 2 < S) put(0, ra);                    // step s0 + 2
+        issue(s0 + 4, ra);
+        compute(1);                                    // step s0 + 1
+        pin();
+        __syncthreads();
+    }
+
+    if (KS > 1) {
+        // groups 1.. leave their partial tiles in their own LDS (their operand
+        // buffers are consumed); group 0 adds them in group order and stores
+        if (grp > 0) {
+            float* part = reinterpret_cast<float*>(glds) + wave * 16 * 64;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) part[r * 64 + lane] = acc[r];
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll
+        for (int g = 1; g < KS; ++g) {
+            const float* part = reinterpret_cast<const float*>(lds + g * kT64Lds) + wave * 16 * 64;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] += part[r * 64 + lane];
+        }
+    }
+    // rows 16h + r of column i of subtile (wp, wn)
+    const int64_t nout = n0 + 32 * wn + i;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t pout = p0 + 32 * wp + 16 * h + r;
+        if (nout < n && pout < p) y[pout * n + nout] = acc[r];
+    }
+}
+
 static bool use_stream(int64_t n, int64_t k, int64_t p) {
     const int64_t ntn = (n + 31) / 32, ntp = (p + 31) / 32;
     return k % 512 == 0 && k <= kStreamMaxK && ntn * ntp < (int64_t(1) << 31) &&
            32 * ntp < (int64_t(1) << 31) && 32 * ntn < (int64_t(1) << 31);
 }
 
-size_t prefill_lds_bytes(int64_t k) {
+// Kernel choice, measured on the P = 256 .. 4096 Mimir products: the 64 x 64
+// kernel with one group of waves from four 64 x 64 tiles per compute unit on
+// (K a multiple of 256), with K split over two groups from 1.5 tiles per
+// compute unit on (K a multiple of 512); below that the streaming kernel
+// (K a multiple of 512) or the one-tile kernel.  Returns the number of groups,
+// or 0 for the other kernels.
+static int tile64_split(int64_t n, int64_t k, int64_t p, int cu_count) {
+    const int64_t ntn = (n + 63) / 64, ntp = (p + 63) / 64;
+    const int64_t grid = 8 * ntp * ((ntn + 7) / 8);
+    if (k % 256 != 0 || k > kStreamMaxK || grid >= (int64_t(1) << 31)) return 0;
+    const int64_t tiles = ntn * ntp;
+    if (tiles >= 4 * (int64_t)cu_count) return 1;
+    if (2 * tiles >= 3 * (int64_t)cu_count && k % 512 == 0) return 2;
+    if (tiles >= (int64_t)cu_count && k % 512 != 0) return 1;
+    return 0;
+}
+
+size_t prefill_lds_bytes(int64_t n, int64_t k, int64_t p, const DeviceInfo& dev) {
+    if (const int ks = tile64_split(n, k, p, dev.cu_count)) return (size_t)ks * kT64Lds;
     if (k % 512 == 0 && k <= kStreamMaxK) return (size_t)kStreamLds;
     const size_t total_pad = ((size_t)64 * (size_t)(k / 32) + 255) & ~(size_t)255;
     return 4 * (size_t)kWaveSlice + (total_pad + 2) * 2;
 }
 
 hipError_t prefill_prepare(const DeviceInfo& dev) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
+    const void* fns[2] = {reinterpret_cast<const void*>(&prefill_kernel),
+                          reinterpret_cast<const void*>(&prefill_tile64_kernel<2>)};
+    for (const void* f : fns) {
+        const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t p,
@@ -417,6 +631,15 @@ hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
     const int nb = (int)(k / 32);
     const int64_t ntn = (n + 31) / 32, ntp = (p + 31) / 32;
     (void)hipGetLastError();
+    if (const int ks = tile64_split(n, k, p, dev.cu_count)) {
+        const int64_t ntn64 = (n + 63) / 64, ntp64 = (p + 63) / 64;
+        const unsigned grid = (unsigned)(8 * ntp64 * ((ntn64 + 7) / 8));
+        if (ks == 1)
+            prefill_tile64_kernel<1><<<grid, 256, kT64Lds, stream>>>(wq, wd, n, nb, p, xq, xd, y);
+        else
+            prefill_tile64_kernel<2><<<grid, 512, 2 * kT64Lds, stream>>>(wq, wd, n, nb, p, xq, xd, y);
+        return hipGetLastError();
+    }
     if (use_stream(n, k, p)) {
         const int64_t per_xcd = ((ntn + 7) / 8) * ntp;          // most tiles of one XCD
         int64_t gx = (int64_t)(dev.cu_count / 8 > 0 ? dev.cu_count / 8 : 1) * kStreamWgPerCu;
@@ -426,7 +649,7 @@ hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
         return hipGetLastError();
     }
     const int64_t grid = 8 * ntp * ((ntn + 7) / 8);
-    const size_t lds = prefill_lds_bytes(k);
+    const size_t lds = prefill_lds_bytes(n, k, p, dev);
     prefill_kernel<<<(unsigned)grid, 256, lds, stream>>>(wq, wd, n, nb, p, xq, xd, y);
     return hipGetLastError();
 }

@@ -313,7 +313,13 @@ def _prefill_case(n, k, p, seed):
                                    (300, 4096, 256), (33, 1536, 257), (40, 7168, 37), (257, 160, 300),
                                    # K a multiple of 512: the persistent streaming kernel
                                    (1, 512, 1), (31, 1024, 33), (4097, 512, 3), (40, 16384, 40),
-                                   (777, 2048, 95)])
+                                   (777, 2048, 95),
+                                   # enough 64 x 64 tiles (MI355X: 256 compute units) for the
+                                   # 64 x 64 kernel, ragged in n and p: one group of waves
+                                   # (K % 512 != 0, or >= 4 tiles per compute unit) and K split
+                                   # over two groups (1.5 .. 4 tiles per compute unit)
+                                   (4100, 512, 300), (4097, 256, 257), (16383, 768, 70),
+                                   (16390, 512, 300), (8200, 1024, 200)])
 def test_prefill_small(n, k, p):
     log(f"prefill n={n} k={k} p={p}")
     wq, wd, xq, xd = _prefill_case(n, k, p, 6000 + n + k + p)
@@ -482,8 +488,14 @@ def test_outputs_leave_guard_bands_untouched():
     assert torch.all(wd_buf[n * k // 32:] == 0x1234)
     assert torch.all(y_buf[m * n:] == 7.0)
     assert torch.all(yp_buf[p * n:] == 7.0)
-    # the streaming prefill kernel (K a multiple of 512), ragged in n and p
-    n2, k2, p2 = 45, 512, 37
+    # the streaming prefill kernel (K a multiple of 512) and the 64 x 64 kernel
+    # (K a multiple of 256, enough tiles), ragged in n and p
+    for n2, k2, p2 in ((45, 512, 37), (8200, 256, 130), (6200, 512, 260)):
+        _guarded_prefill(n2, k2, p2, guard)
+
+
+def _guarded_prefill(n2, k2, p2, guard):
+    log(f"guarded prefill n={n2} k={k2} p={p2}")
     wq2, wd2 = q8.quantize_weights(to_dev(edge_weights(8403, n2, k2)))
     xq2, xd2 = q8.quantize_act(to_dev(wl.prefill_act_bf16(8404, p2, k2)))
     y2_buf = torch.full((p2 * n2 + guard,), 7.0, dtype=torch.float32, device=DEV)
@@ -491,7 +503,7 @@ def test_outputs_leave_guard_bands_untouched():
     torch.cuda.synchronize()
     assert torch.all(y2_buf[p2 * n2:] == 7.0)
     assert_close(to_host(y2_buf[: p2 * n2].view(p2, n2)),
-                 oracle.q8q8(to_host(wq2), to_host(wd2), to_host(xq2), to_host(xd2)), "stream guard")
+                 oracle.q8q8(to_host(wq2), to_host(wd2), to_host(xq2), to_host(xd2)), f"guarded prefill n={n2}")
 
 
 def test_empty_calls_are_noops():
