@@ -252,41 +252,108 @@ def bench_mimir(q8, wl, dev, weights, m: int, replays: int = 20) -> dict:
             "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": m * HBM_PEAK_GBPS * 1e9 / nbytes}
 
 
-def bench_prefill(q8, wl, dev, weights, reps: int = 50) -> dict:
-    """P = 256: qkv and gate_up on [256, 1536], down on [256, 4096] (block 0
-    weights); activations quantized by q8_quantize_act (timed separately)."""
+def time_graph(fn, per_graph: int, reps: int = 3, trials: int = 3) -> float:
+    """Mean ms per call of `fn` captured `per_graph` times into one HIP graph,
+    best of `trials` timed regions of `reps` replays (launch-independent)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    best = min(time_region(lambda i: g.replay(), reps)[0] for _ in range(trials))
+    return best / per_graph
+
+
+PREFILL_SWEEP = (16, 64, 256, 1024, 4096)
+
+
+def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP) -> dict:
+    """Q8 x Q8 prefill: qkv and gate_up on [P, 1536] activations, down on
+    [P, 4096] (block-0 weights), each product graph-replayed.  P = 256 is the
+    configured workload (activations with the seeded special rows); the sweep
+    over P also fits time = fixed + P * slope for the three products, the
+    pages' prefill measure."""
     import torch
     cfg = wl.CONFIGS["prefill_p256"]
-    xa = to_dev(wl.prefill_act_bf16(cfg["xa_seed"], 256, wl.HIDDEN), dev)
-    xb = to_dev(wl.prefill_act_bf16(cfg["xb_seed"], 256, wl.INTER), dev)
-    xaq, xad = q8.quantize_act(xa)
-    xbq, xbd = q8.quantize_act(xb)
     gemms = []
     for proj, (name, n, k) in enumerate(wl.BLOCK_SHAPES):
-        if name == "o":
+        if name != "o":
+            gemms.append((name, n, k, weights[(0, proj)]))
+    per_p = {}
+    for P in sweep:
+        if P == 256:
+            xa = wl.prefill_act_bf16(cfg["xa_seed"], P, wl.HIDDEN)
+            xb = wl.prefill_act_bf16(cfg["xb_seed"], P, wl.INTER)
+        else:
+            xa = wl.prefill_act_bf16(cfg["xa_seed"] + P, P, wl.HIDDEN)
+            xb = wl.prefill_act_bf16(cfg["xb_seed"] + P, P, wl.INTER)
+        xs = {}
+        for kk, xn in ((wl.HIDDEN, xa), (wl.INTER, xb)):
+            xd_ = to_dev(xn, dev)
+            q, d = q8.quantize_act(xd_)
+            xs[kk] = (xd_, q, d)
+        rows, tot_us, ops, nbytes = {}, 0.0, 0, 0
+        for name, n, k, (wq, wd) in gemms:
+            _, xq, xd = xs[k]
+            y = torch.empty((P, n), dtype=torch.float32, device=dev)
+            us = time_graph(lambda: q8.gemm_prefill(wq, wd, xq, xd, out=y), 10 if P >= 1024 else 20) * 1e3
+            o = 2 * P * n * k
+            rows[name] = {"us": us, "TOPS": o / us / 1e6}
+            tot_us += us
+            ops += o
+            nbytes += prefill_bytes(n, k, P)
+        qus = 0.0
+        for kk, (x_, q, d) in xs.items():
+            qus += time_graph(lambda: q8.quantize_act(x_, out=(q, d)), 20) * 1e3
+        tops = ops / tot_us / 1e6
+        per_p[P] = {"us_three_gemms": tot_us, "int_ops": ops, "TOPS": tops,
+                    "frac_int8_peak": tops / INT8_PEAK_TOPS, "bytes": nbytes,
+                    "us_per_token": tot_us / P, "per_gemm": rows, "quantize_act_us": qus}
+        log(f"prefill P={P}: {tot_us:.1f} us, {tops:.0f} TOPS ({100 * tops / INT8_PEAK_TOPS:.1f}% of int8 peak)")
+    ps = np.array(sorted(per_p), dtype=np.float64)
+    ts = np.array([per_p[int(P)]["us_three_gemms"] for P in ps])
+    big = ps >= 256
+    slope, fixed = np.polyfit(ps[big], ts[big], 1)
+    out = dict(per_p[256])
+    out["p_sweep"] = {str(P): v for P, v in per_p.items()}
+    out["fit_p_ge_256"] = {"fixed_us": float(fixed), "slope_us_per_token": float(slope),
+                           "slope_ms_per_token": float(slope) * 1e-3}
+    return out
+
+
+def bench_sync_probe(q8, dev) -> dict:
+    """What one dependency edge of a decode step costs on this GPU: the
+    per-launch cost of an empty kernel under graph replay, and one grid-wide
+    barrier over 64 / 128 / 256 single-wave workgroups (the synchronization a
+    single-launch step would need between two dependent products)."""
+    import torch
+    flags = q8.probe_barrier_flags(dev)
+    out = {"graph_node_us": time_graph(lambda: q8.probe_barrier(flags, 1, 0), 200) * 1e3}
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    bar = {}
+    for g in (64, 128, 256):
+        if g > cus:
             continue
-        gemms.append((name, n, k, weights[(0, proj)],
-                      (xbq, xbd) if k == wl.INTER else (xaq, xad),
-                      torch.empty((256, n), dtype=torch.float32, device=dev)))
-
-    def run(i):
-        for name, n, k, (wq, wd), (xq, xd), y in gemms:
-            q8.gemm_prefill(wq, wd, xq, xd, out=y)
-
-    run(0)
-    ms, _ = time_events(run, reps)
-    ops = sum(2 * 256 * n * k for _, n, k, *_ in gemms)
-    per = {}
-    for name, n, k, (wq, wd), (xq, xd), y in gemms:
-        gms, _ = time_events(lambda i: q8.gemm_prefill(wq, wd, xq, xd, out=y), reps)
-        per[name] = {"us": gms * 1e3, "TOPS": 2 * 256 * n * k / gms / 1e9}
-    qms, _ = time_events(lambda i: (q8.quantize_act(xa, out=(xaq, xad)),
-                                    q8.quantize_act(xb, out=(xbq, xbd))), reps)
-    nbytes = sum(prefill_bytes(n, k, 256) for _, n, k, *_ in gemms)
-    tops = ops / ms / 1e9
-    return {"ms_three_gemms": ms, "int_ops": ops, "TOPS": tops,
-            "frac_int8_peak": tops / INT8_PEAK_TOPS, "bytes": nbytes,
-            "per_gemm": per, "quantize_act_us": qms * 1e3}
+        flags.zero_()
+        q8.probe_barrier(flags, g, 10)
+        t = []
+        for rounds in (100, 1100):
+            ms, _ = time_region(lambda i: q8.probe_barrier(flags, g, rounds), 3)
+            t.append(ms)
+        torch.cuda.synchronize()
+        if int(flags[-1].item()) != 0:
+            bar[str(g)] = None
+            continue
+        bar[str(g)] = (t[1] - t[0]) * 1e3 / 1000
+    out["grid_barrier_us"] = bar
+    return out
 
 
 def cpu_baseline(oracle, wl, oq, od, x, seconds: float = 10.0) -> dict:
@@ -344,7 +411,7 @@ def main() -> int:
             if name != "o":
                 weights[(0, proj)] = quantize_on_device(
                     q8, wl.normal_weights(wl.mimir_weight_seed(0, proj), n_, k_), dev)
-        print(json.dumps({"prefill_p256": bench_prefill(q8, wl, dev, weights, reps=10)}), flush=True)
+        print(json.dumps({"prefill_p256": bench_prefill(q8, wl, dev, weights, sweep=(256,))}), flush=True)
         return 0
 
     # ---- headline: lm_head-shaped GEMV, batch 1
@@ -401,9 +468,11 @@ def main() -> int:
         for m in (1, 2, 4, 8):
             log(f"mimir step m={m}")
             extras[f"mimir_step_b{m}"] = bench_mimir(q8, wl, dev, weights, m)
-        log("prefill P=256")
+        log("prefill P sweep")
         extras["prefill_p256"] = bench_prefill(q8, wl, dev, weights)
         del weights
+        log("decode synchronization probe")
+        extras["sync_probe"] = bench_sync_probe(q8, dev)
 
     cpu = None
     if not args.metric_only and not args.no_cpu_baseline:

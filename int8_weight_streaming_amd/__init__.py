@@ -38,7 +38,8 @@ EXPORTED = (
     "q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
     "q8_gemm_prefill", "q8_block_dots",
 )
-PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words")
+PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words", "q8_probe_barrier",
+                  "q8_probe_barrier_words")
 
 
 class Q8Error(RuntimeError):
@@ -73,6 +74,9 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q8_probe_read.argtypes = [P, I64, P, P]
     L.q8_probe_read.restype = I
     L.q8_probe_sink_words.restype = I64
+    L.q8_probe_barrier.argtypes = [P, I, I, P]
+    L.q8_probe_barrier.restype = I
+    L.q8_probe_barrier_words.restype = I64
     for name in ("q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
                  "q8_gemm_prefill", "q8_block_dots"):
         getattr(L, name).restype = I
@@ -244,3 +248,17 @@ def probe_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Ten
     nbytes = buf.numel() * buf.element_size()
     _check("q8_probe_read", L.q8_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream()))
     return sink
+
+
+def probe_barrier_flags(device) -> torch.Tensor:
+    """A zero-filled flag buffer for probe_barrier."""
+    return torch.zeros((load_library().q8_probe_barrier_words(),), dtype=torch.int32, device=device)
+
+
+def probe_barrier(flags: torch.Tensor, workgroups: int, rounds: int) -> None:
+    """Enqueue `rounds` grid-wide barriers over `workgroups` single-wave
+    workgroups (rounds = 0: an empty kernel).  After synchronizing, a non-zero
+    last word of `flags` means a barrier timed out and the measurement is void."""
+    if flags.dtype != torch.int32 or not flags.is_cuda or flags.numel() < load_library().q8_probe_barrier_words():
+        raise ValueError("flags must come from probe_barrier_flags()")
+    _check("q8_probe_barrier", load_library().q8_probe_barrier(_ptr(flags), workgroups, rounds, _stream()))

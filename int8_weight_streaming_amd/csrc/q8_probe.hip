@@ -39,6 +39,43 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const q8::u32x4* __rest
         sink[blockIdx.x] = s;
     }
 }
+// ---- grid-barrier probe
+
+constexpr int kBarReplicas = 8;                // one flag array per XCD
+constexpr int kBarStride = 1024;               // words per replica (>= workgroups)
+constexpr unsigned kBarSpinLimit = 1u << 22;
+constexpr int kBarErr = kBarReplicas * kBarStride;   // index of the error word
+
+__device__ __forceinline__ unsigned coherent_load(const unsigned* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store(unsigned* p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One wave per workgroup.  Epochs continue from the value this workgroup's own
+// flag holds (every flag holds the same epoch between calls).
+__global__ __launch_bounds__(64) void probe_barrier_kernel(unsigned* __restrict__ flags, int rounds) {
+    const int g = blockIdx.x, lane = threadIdx.x, nwg = gridDim.x;
+    const unsigned* mine = flags + (g % kBarReplicas) * kBarStride;
+    unsigned epoch = coherent_load(flags + g);
+    for (int r = 0; r < rounds; ++r) {
+        ++epoch;
+        if (lane < kBarReplicas) coherent_store(flags + lane * kBarStride + g, epoch);
+        unsigned spins = 0;
+        bool done = false;
+        while (!done) {
+            bool all = true;
+            for (int i = lane; i < nwg; i += 64) all = all && (int)(coherent_load(mine + i) - epoch) >= 0;
+            done = __all(all);
+            if (!done && (coherent_load(flags + kBarErr) != 0u || ++spins > kBarSpinLimit)) {
+                if (lane == 0) coherent_store(flags + kBarErr, 1u);
+                return;                                 // every wave leaves
+            }
+        }
+    }
+}
+
 int cu_count_current() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -60,5 +97,18 @@ extern "C" q8_status q8_probe_read(const void* src, int64_t bytes, uint32_t* sin
     (void)hipGetLastError();
     probe_read_kernel<<<cus * kProbeBlocksPerCu, 256, 0, stream>>>(
         reinterpret_cast<const q8::u32x4*>(src), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ERR_HIP;
+}
+
+extern "C" int64_t q8_probe_barrier_words(void) { return (int64_t)kBarErr + 1; }
+
+extern "C" q8_status q8_probe_barrier(uint32_t* flags, int workgroups, int rounds, hipStream_t stream) {
+    if (!flags) return Q8_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(flags) & 3u) return Q8_ERR_ALIGN;
+    const int cus = cu_count_current();
+    if (cus <= 0) return Q8_ERR_DEVICE;
+    if (workgroups < 1 || workgroups > cus || workgroups > kBarStride || rounds < 0) return Q8_ERR_SHAPE;
+    (void)hipGetLastError();
+    probe_barrier_kernel<<<workgroups, 64, 0, stream>>>(flags, rounds);
     return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ERR_HIP;
 }

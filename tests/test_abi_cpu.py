@@ -125,3 +125,13 @@ def test_valid_arguments_without_gpu_report_device(lib):
         pytest.skip("a GPU is present")
     assert lib.q8_gemm_skinny(A, B, 8, 64, 1, 0, A, None, A, None) == DEVICE
     assert lib.q8_quantize_weights(A, 4, 64, A, B, None) == DEVICE
+
+
+def test_probe_validation(lib):
+    """The measurement probes check their arguments before any device call."""
+    assert lib.q8_probe_read(A, 0, A, None) == SHAPE
+    assert lib.q8_probe_read(A, 24, A, None) == SHAPE
+    assert lib.q8_probe_read(None, 64, A, None) == NULL
+    assert lib.q8_probe_barrier(None, 4, 1, None) == NULL
+    assert lib.q8_probe_barrier(0x300002, 4, 1, None) == ALIGN   # flags need 4-byte alignment
+    assert lib.q8_probe_barrier_words() > 8 * 1024
