@@ -58,6 +58,7 @@ def lib():
         L.oracle_w8a16.argtypes = [P, P, I64, I64, I64, P, P, I64, P]
         L.oracle_block_dots.argtypes = [P, I64, I64, P, I64, P]
         L.oracle_q8q8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, P]
+        L.oracle_attn_decode.argtypes = [P, P, P, P, P, I64, I64, I64, I64, C.c_double, P]
         _lib = L
     return _lib
 
@@ -174,3 +175,26 @@ def q8q8(wq, wd, xq, xd, rows=None) -> np.ndarray:
     lib().oracle_q8q8(_p(wq), _p(wd), n, k, m, _p(xq), _p(xd),
                       None if r is None else _p(r), nr, _p(y))
     return y
+
+
+def attn_decode(q, kq, kd, vq, vd, t: int, scale: float) -> np.ndarray:
+    """fp64 out [heads][d]: softmax(scale * q . K) . V over the first t cache rows.
+
+    q: bf16 bits [heads][d]; kq, vq: int8 codes [heads][t_cap][d]; kd, vd:
+    binary16 scale bits [heads][t_cap][d/32]."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    kq = np.ascontiguousarray(kq, dtype=np.int8)
+    vq = np.ascontiguousarray(vq, dtype=np.int8)
+    kd = np.ascontiguousarray(kd, dtype=np.uint16)
+    vd = np.ascontiguousarray(vd, dtype=np.uint16)
+    heads, t_cap, d = kq.shape
+    _check_k(d)
+    assert q.shape == (heads, d) and vq.shape == kq.shape
+    assert kd.shape == (heads, t_cap, d // 32) and vd.shape == kd.shape
+    if not 1 <= t <= t_cap:
+        raise ValueError("need 1 <= t <= t_cap")
+    out = np.empty((heads, d), dtype=np.float64)
+    lib().oracle_attn_decode(_p(q), _p(kq), _p(kd), _p(vq), _p(vd), heads, int(t), t_cap, d,
+                             float(scale), _p(out))
+    return out
+

@@ -31,6 +31,17 @@
  *    dot) and ACT 4, "How the GEMM was closed" (per-block int32 sum folded into
  *    a float accumulator with the block's scales)].
  *
+ *  - Decode attention over a Q8_0 key/value cache [Frigg README, "The model, as
+ *    verified": hidden 1536 = 12 heads x head_dim 128, multi-head attention
+ *    with 12 key/value heads; "Masks": decode passes no mask, one query
+ *    against the whole cache; "Cache": one static slab [heads][4096][128] per
+ *    virtual layer for K and for V; the bytes-per-token table counts an int8
+ *    KV read per token].  The pages name int8 KV without its block layout; it
+ *    is read here as the same Q8_0 format (blocks of 32 along head_dim, one
+ *    binary16 scale each).  For head h over the first t cache rows:
+ *    s[j] = scale * sum_d q[h][d] * K[h][j][d],  w = softmax(s),
+ *    out[h][d] = sum_j w[j] * V[h][j][d], in fp64 with K and V dequantized.
+ *
  * Threading: output rows are split over OpenMP threads; each output is computed
  * by one thread in a fixed order, so results do not depend on the thread count
  * [fak MODEL-BASELINE-RESULTS, ACT 1, "Parity lane": row-parallel matmul].
@@ -39,6 +50,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -215,5 +227,44 @@ void oracle_q8q8(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k,
             }
             y[mi * nrows + j] = acc;
         }
+    }
+}
+
+/* Decode attention, one bf16 query row per head against t rows of a Q8_0 key
+ * and value cache laid out [heads][t_cap][d] (codes) and [heads][t_cap][d/32]
+ * (binary16 scales).  Softmax with the maximum subtracted first (the value is
+ * that of the plain definition; the subtraction only keeps exp in range).
+ * out is fp64 [heads][d]. */
+void oracle_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd,
+                        const int8_t* vq, const uint16_t* vd, int64_t heads, int64_t t,
+                        int64_t t_cap, int64_t d, double scale, double* out) {
+    int64_t nb = d / 32;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (int64_t h = 0; h < heads; ++h) {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(t > 0 ? t : 1));
+        double smax = -INFINITY;
+        for (int64_t j = 0; j < t; ++j) {
+            const int64_t row = h * t_cap + j;
+            double acc = 0.0;
+            for (int64_t e = 0; e < d; ++e)
+                acc += (double)oracle_bf16_to_float(q[h * d + e]) *
+                       ((double)kq[row * d + e] * oracle_half_to_double(kd[row * nb + e / 32]));
+            s[j] = scale * acc;
+            if (s[j] > smax) smax = s[j];
+        }
+        double sum = 0.0;
+        for (int64_t j = 0; j < t; ++j) {
+            s[j] = exp(s[j] - smax);
+            sum += s[j];
+        }
+        for (int64_t e = 0; e < d; ++e) {
+            double o = 0.0;
+            for (int64_t j = 0; j < t; ++j) {
+                const int64_t row = h * t_cap + j;
+                o += s[j] * ((double)vq[row * d + e] * oracle_half_to_double(vd[row * nb + e / 32]));
+            }
+            out[h * d + e] = o / sum;
+        }
+        free(s);
     }
 }
