@@ -123,11 +123,14 @@ q8_status q8_gemm_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_
                          int64_t m, int act, const void* x, const uint16_t* xd,
                          float* y, hipStream_t stream);
 
-/* Q8 x Q8 prefill product for p activation rows (0 <= p <= 4,194,240).  A
- * workgroup keeps the binary16 scales of its rows for the whole of K in LDS:
- * 36 KiB + 128 bytes per 32-element block must fit the device's per-workgroup
- * LDS (K <= 7168 with 64 KiB, K <= 31744 with 160 KiB); a larger K returns
- * Q8_ERR_SHAPE, checked after the device check, with nothing enqueued.
+/* Q8 x Q8 prefill product for p activation rows (0 <= p <= 4,194,240).  For K
+ * a multiple of 512 (and K a multiple of 256 with at least as many 64 x 64
+ * output tiles as compute units) the kernels use a fixed 38-80 KiB of LDS per
+ * workgroup, for K up to 2^24.  For any other K a workgroup keeps the binary16
+ * scales of its rows for the whole of K in LDS: 36 KiB + 128 bytes per
+ * 32-element block must fit the device's per-workgroup LDS (K <= 7168 with 64
+ * KiB, K <= 31744 with 160 KiB); a larger K returns Q8_ERR_SHAPE, checked after
+ * the device check, with nothing enqueued.
  * y[t][j] = sum_b wd[j][b] * xd[t][b] * sum_{i<32} wq[j][32b+i] * xq[t][32b+i],
  * the int32 block sums taken on the int8 matrix cores, each block folded into an
  * fp32 accumulator with its two scales [fak MODEL-BASELINE-RESULTS, ACT 4,
@@ -144,6 +147,34 @@ q8_status q8_gemm_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
  * the Q8-activation decode products.  isum is int32 [m][n][k/32]. */
 q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m,
                         const int8_t* xq, int32_t* isum, hipStream_t stream);
+
+/* Decode attention over a Q8_0 key/value cache, one query row per head and no
+ * mask [Frigg README: "Masks" (decode passes no mask: one query against the
+ * whole cache), "Cache" (one static slab [heads][4096][128] per virtual layer
+ * for K and for V), "The model, as verified" (12 heads of head_dim 128,
+ * multi-head attention: one key/value head per query head)]:
+ *
+ *   s[j] = scale * sum_d q[h][d] * K[h][j][d]   for the cache rows j < t,
+ *   out[h][d] = sum_j softmax(s)[j] * V[h][j][d],
+ *
+ * with K and V dequantized (codes times their block's binary16 scale; the
+ * pages name an int8 cache without its layout, which is read as the same Q8_0
+ * format: blocks of 32 along head_dim, e.g. as written by q8_quantize_act).
+ * q: bf16 [heads][128]; kq, vq: int8 codes [heads][t_cap][128]; kd, vd:
+ * binary16 scales [heads][t_cap][4] (row h * t_cap + j of the slab); out: fp32
+ * [heads][128].  head_dim must be 128 (Q8_ERR_SHAPE otherwise); 1 <= t <= t_cap
+ * <= 2^24 - 128; heads <= 65536 (0 is a no-op); scale finite.
+ * `work`: caller-owned fp32 workspace of at least q8_attn_work_words(heads, t)
+ * words (0 when t <= 128, and then `work` may be NULL); its contents on entry
+ * do not matter and are overwritten.  Rows past t are never read.  fp32
+ * accumulation; results are bitwise reproducible for a given (heads, t). */
+q8_status q8_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd,
+                         const int8_t* vq, const uint16_t* vd, int64_t heads, int64_t t,
+                         int64_t t_cap, int64_t head_dim, float scale, float* out,
+                         float* work, int64_t work_words, hipStream_t stream);
+
+/* Workspace words q8_attn_decode needs for (heads, t); -1 when out of range. */
+int64_t q8_attn_work_words(int64_t heads, int64_t t);
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ MAX_BATCH = 8
 EXPORTED = (
     "q8_abi_version", "q8_status_str", "q8_last_hip_error",
     "q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
-    "q8_gemm_prefill", "q8_block_dots",
+    "q8_gemm_prefill", "q8_block_dots", "q8_attn_decode", "q8_attn_work_words",
 )
 PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words", "q8_probe_barrier",
                   "q8_probe_barrier_words")
@@ -71,6 +71,10 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q8_gemm_skinny.argtypes = [P, P, I64, I64, I64, I, P, P, P, P]
     L.q8_gemm_prefill.argtypes = [P, P, I64, I64, I64, P, P, P, P]
     L.q8_block_dots.argtypes = [P, I64, I64, I64, P, P, P]
+    L.q8_attn_decode.argtypes = [P, P, P, P, P, I64, I64, I64, I64, C.c_float, P, P, I64, P]
+    L.q8_attn_decode.restype = I
+    L.q8_attn_work_words.argtypes = [I64, I64]
+    L.q8_attn_work_words.restype = I64
     L.q8_probe_read.argtypes = [P, I64, P, P]
     L.q8_probe_read.restype = I
     L.q8_probe_sink_words.restype = I64
@@ -234,6 +238,39 @@ def block_dots(wq, xq, out=None):
     _check("q8_block_dots", load_library().q8_block_dots(
         _ptr(wq), n, k, m, _ptr(xq), _ptr(isum), _stream()))
     return isum
+
+
+def attn_work_words(heads: int, t: int) -> int:
+    """fp32 workspace words attn_decode needs for (heads, t)."""
+    return int(load_library().q8_attn_work_words(int(heads), int(t)))
+
+
+def attn_decode(q, kq, kd, vq, vd, t: int, scale: float, work=None, out=None):
+    """Decode attention over a Q8_0 cache: out fp32 [heads][128] from a bf16
+    query [heads][128] and the first t rows of kq, vq (int8 [heads][t_cap][128])
+    with their binary16 scales kd, vd ([heads][t_cap][4])."""
+    q = _as_bits16(q)
+    kd = _as_bits16(kd)
+    vd = _as_bits16(vd)
+    _need(q, "q", torch.uint16, 2)
+    _need(kq, "kq", torch.int8, 3)
+    _need(vq, "vq", torch.int8, 3)
+    _need(kd, "kd", torch.uint16, 3)
+    _need(vd, "vd", torch.uint16, 3)
+    heads, t_cap, d = kq.shape
+    if tuple(vq.shape) != (heads, t_cap, d) or tuple(q.shape) != (heads, d):
+        raise ValueError("q [heads][d], kq and vq [heads][t_cap][d] must agree")
+    if tuple(kd.shape) != (heads, t_cap, d // 32) or tuple(vd.shape) != tuple(kd.shape):
+        raise ValueError("kd and vd must be [heads][t_cap][d/32]")
+    need = attn_work_words(heads, t) if 1 <= t <= t_cap else 0
+    if work is None and need > 0:
+        work = torch.empty((need,), dtype=torch.float32, device=kq.device)
+    y = out if out is not None else torch.empty((heads, d), dtype=torch.float32, device=kq.device)
+    words = work.numel() if work is not None else 0
+    _check("q8_attn_decode", load_library().q8_attn_decode(
+        _ptr(q), _ptr(kq), _ptr(kd), _ptr(vq), _ptr(vd), heads, int(t), t_cap, d, float(scale),
+        _ptr(y), _ptr(work), words, _stream()))
+    return y
 
 
 # ------------------------------------------------------------------ measurement utility

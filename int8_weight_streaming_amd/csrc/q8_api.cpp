@@ -27,6 +27,8 @@ q8::DeviceInfo g_dev_info[kMaxDevices];
 constexpr int64_t kMaxExtent = (int64_t)1 << 31;   // per-dimension limit
 constexpr int64_t kMaxElems = (int64_t)1 << 46;    // n * k limit (64 TiB of codes)
 constexpr int64_t kMaxPrefillRows = (int64_t)65535 * 64;
+constexpr int64_t kMaxAttnHeads = (int64_t)1 << 16;
+constexpr int64_t kMaxAttnRows = ((int64_t)1 << 24) - 128;   // cache rows per head
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -209,6 +211,32 @@ q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m, const
     const q8::DeviceInfo* dev = nullptr;
     Q8_TRY(device_for(stream, &dev));
     return finish(q8::launch_block_dots(wq, n, k, (int)m, xq, isum, *dev, stream));
+}
+
+int64_t q8_attn_work_words(int64_t heads, int64_t t) {
+    if (heads < 0 || heads > kMaxAttnHeads || t < 1 || t > kMaxAttnRows) return -1;
+    return q8::attn_work_floats(heads, t);
+}
+
+q8_status q8_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd, const int8_t* vq,
+                         const uint16_t* vd, int64_t heads, int64_t t, int64_t t_cap,
+                         int64_t head_dim, float scale, float* out, float* work, int64_t work_words,
+                         hipStream_t stream) {
+    if (head_dim != 128) return Q8_ERR_SHAPE;
+    if (heads < 0 || heads > kMaxAttnHeads || t < 1 || t > t_cap || t_cap > kMaxAttnRows)
+        return Q8_ERR_SHAPE;
+    if (!(scale == scale) || scale - scale != 0.0f) return Q8_ERR_SHAPE;   // NaN or infinite
+    if (heads == 0) return Q8_OK;
+    const int64_t need = q8::attn_work_floats(heads, t);
+    if (work_words < need) return Q8_ERR_SHAPE;
+    if (!q || !kq || !kd || !vq || !vd || !out || (need > 0 && !work)) return Q8_ERR_NULL;
+    if (!aligned16(q) || !aligned16(kq) || !aligned16(kd) || !aligned16(vq) || !aligned16(vd) ||
+        !aligned16(out) || (need > 0 && !aligned16(work)))
+        return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_attn_decode(q, kq, kd, vq, vd, heads, t, t_cap, scale, out, work,
+                                         *dev, stream));
 }
 
 }  // extern "C"

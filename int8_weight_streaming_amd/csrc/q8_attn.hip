@@ -1,0 +1,196 @@
+// q8_attn.hip -- decode attention over a Q8_0 key/value cache.
+//
+//   s[j] = scale * sum_d q[h][d] * K[h][j][d],   w = softmax(s),
+//   out[h][d] = sum_j w[j] * V[h][j][d],   j < t,
+//
+// one bf16 query row per head against t rows of a static cache slab
+// [heads][t_cap][128] whose K and V are Q8_0 (int8 codes, one binary16 scale
+// per 32 consecutive elements of a row) [Frigg README: "Masks" (decode passes
+// no mask, one query against the whole cache), "Cache" (one static slab of
+// [heads][4096][128] per virtual layer for K and for V), "The model, as
+// verified" (12 heads of 128, multi-head attention), the bytes-per-token table
+// (an int8 KV read per decoded token)].
+//
+// The cache read is the cost (2 x 136 bytes per row and head), so the kernel
+// streams it once: a workgroup takes 128 rows of one head; each of its four
+// waves 32 rows, lane l the 16-byte segment l % 8 (dimensions 16 (l % 8) ..
+// + 15, inside one Q8 block) of rows 8j + l / 8, j < 4, for K and V alike, all
+// loads issued before the first use.  A score is the bf16 dot of the query
+// segment with the exactly converted codes, times the block scale, summed over
+// the row's eight lanes by a fixed DPP tree.  The workgroup subtracts its
+// maximum score, and writes (sum_j e^(s_j - m) V_j, m, sum_j e^(s_j - m)) to a
+// caller-provided workspace; a second kernel combines the chunks of a head in
+// chunk order (or the first kernel writes the result itself when one chunk
+// covers the context).  Every reduction has a fixed order: results are
+// bitwise reproducible.  Rows past t fall outside the buffer descriptors'
+// range, read as zero and get weight zero.
+#include "q8_device.hpp"
+#include "q8_internal.hpp"
+
+namespace q8 {
+
+constexpr int kAttnD = 128;                    // head dimension
+constexpr int kAttnChunk = 128;                // cache rows per workgroup
+constexpr int kAttnPart = kAttnD + 2;          // floats per (head, chunk): o[128], m, l
+
+int64_t attn_chunks(int64_t t) { return (t + kAttnChunk - 1) / kAttnChunk; }
+int64_t attn_work_floats(int64_t heads, int64_t t) {
+    const int64_t c = attn_chunks(t);
+    return c > 1 ? heads * c * kAttnPart : 0;
+}
+
+__global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restrict__ q,
+                                                         const int8_t* __restrict__ kq,
+                                                         const uint16_t* __restrict__ kd,
+                                                         const int8_t* __restrict__ vq,
+                                                         const uint16_t* __restrict__ vd,
+                                                         int64_t t, int64_t t_cap, float scale,
+                                                         int nchunks, float* __restrict__ work,
+                                                         float* __restrict__ out) {
+    __shared__ float red[4][kAttnD + 2];
+    const int h = (int)(blockIdx.x / (unsigned)nchunks), c = (int)(blockIdx.x % (unsigned)nchunks);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int seg = lane & 7, rsub = lane >> 3;
+
+    // descriptors over the first t rows of head h (codes 128 B, scales 8 B per row)
+    const int64_t hrow = (int64_t)h * t_cap;
+    const auto rK = range_rsrc(kq + hrow * kAttnD, t * kAttnD);
+    const auto rV = range_rsrc(vq + hrow * kAttnD, t * kAttnD);
+    const auto rKs = range_rsrc(kd + hrow * (kAttnD / 32), t * (kAttnD / 32) * 2);
+    const auto rVs = range_rsrc(vd + hrow * (kAttnD / 32), t * (kAttnD / 32) * 2);
+    const int row0 = c * kAttnChunk + wave * 32 + rsub;           // rows row0 + 8j
+
+    u32x4 kv[4], vv[4];
+    uint16_t ks[4], vs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = row0 + 8 * j;
+        kv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, row * kAttnD + 16 * seg, 0, kLoadNT));
+        vv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, row * kAttnD + 16 * seg, 0, kLoadNT));
+        ks[j] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rKs, row * 8 + 2 * (seg >> 1), 0, 0);
+        vs[j] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rVs, row * 8 + 2 * (seg >> 1), 0, 0);
+    }
+    // query segment: dimensions 16 seg .. 16 seg + 15 as eight bf16 pairs
+    const u32x4* qp = reinterpret_cast<const u32x4*>(q + (int64_t)h * kAttnD + 16 * seg);
+    const u32x4 qa = qp[0], qb = qp[1];
+    const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+
+    // ---- scores of the lane's four rows
+    float s[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t kb[8];
+        i8x4_to_bf16x4(kv[j].x, kb[0], kb[1]);
+        i8x4_to_bf16x4(kv[j].y, kb[2], kb[3]);
+        i8x4_to_bf16x4(kv[j].z, kb[4], kb[5]);
+        i8x4_to_bf16x4(kv[j].w, kb[6], kb[7]);
+        float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pa = dot2_bf16(kb[e], qw[e], pa);
+            pb = dot2_bf16(kb[4 + e], qw[4 + e], pb);
+        }
+        float v = (pa + pb) * half_bits_to_float(ks[j]);
+        // sum over the row's eight lanes (xor 1, xor 2, half-row mirror)
+        v += dpp_f<0xB1>(v);
+        v += dpp_f<0x4E>(v);
+        v += dpp_f<0x141>(v);
+        s[j] = row0 + 8 * j < t ? v * scale : -INFINITY;
+    }
+
+    // ---- workgroup maximum
+    float m = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    m = fmaxf(m, __shfl_xor(m, 8));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (lane == 0) red[wave][kAttnD] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0][kAttnD], red[1][kAttnD]), fmaxf(red[2][kAttnD], red[3][kAttnD]));
+
+    // ---- weights and the weighted value rows (lane: 16 dimensions)
+    float o[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = 0.0f;
+    float l = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float p = expf(s[j] - m);                 // rows past t: exp(-inf) = 0
+        l += p;
+        const float pv = p * half_bits_to_float(vs[j]);
+        const uint32_t w4[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o[4 * e + 0] = fmaf(pv, (float)(int)(int8_t)(w4[e]), o[4 * e + 0]);
+            o[4 * e + 1] = fmaf(pv, (float)(int)(int8_t)(w4[e] >> 8), o[4 * e + 1]);
+            o[4 * e + 2] = fmaf(pv, (float)(int)(int8_t)(w4[e] >> 16), o[4 * e + 2]);
+            o[4 * e + 3] = fmaf(pv, (float)((int)w4[e] >> 24), o[4 * e + 3]);
+        }
+    }
+    // the eight row groups of the wave (lanes with equal seg), fixed tree
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        o[e] += __shfl_xor(o[e], 8);
+        o[e] += __shfl_xor(o[e], 16);
+        o[e] += __shfl_xor(o[e], 32);
+    }
+    l += __shfl_xor(l, 8);
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (rsub == 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red[wave][16 * seg + e] = o[e];
+    }
+    if (lane == 0) red[wave][kAttnD + 1] = l;   // every lane of a row group holds the same l
+    __syncthreads();
+    if (threadIdx.x < kAttnD) {
+        const int d = threadIdx.x;
+        const float od = ((red[0][d] + red[1][d]) + red[2][d]) + red[3][d];
+        const float ls = ((red[0][kAttnD + 1] + red[1][kAttnD + 1]) + red[2][kAttnD + 1]) + red[3][kAttnD + 1];
+        if (nchunks == 1) {
+            out[(int64_t)h * kAttnD + d] = od / ls;
+        } else {
+            float* part = work + ((int64_t)h * nchunks + c) * kAttnPart;
+            part[d] = od;
+            if (d == 0) {
+                part[kAttnD] = m;
+                part[kAttnD + 1] = ls;
+            }
+        }
+    }
+}
+
+// One workgroup per head, thread d: combine the chunks in chunk order.
+__global__ __launch_bounds__(kAttnD) void attn_combine_kernel(const float* __restrict__ work,
+                                                              int nchunks, float* __restrict__ out) {
+    const int h = blockIdx.x, d = threadIdx.x;
+    const float* w = work + (int64_t)h * nchunks * kAttnPart;
+    float mx = -INFINITY;
+    for (int c = 0; c < nchunks; ++c) mx = fmaxf(mx, w[c * kAttnPart + kAttnD]);
+    float num = 0.0f, den = 0.0f;
+    for (int c = 0; c < nchunks; ++c) {
+        const float e = expf(w[c * kAttnPart + kAttnD] - mx);
+        num = fmaf(w[c * kAttnPart + d], e, num);
+        den = fmaf(w[c * kAttnPart + kAttnD + 1], e, den);
+    }
+    out[(int64_t)h * kAttnD + d] = num / den;
+}
+
+hipError_t launch_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd,
+                              const int8_t* vq, const uint16_t* vd, int64_t heads, int64_t t,
+                              int64_t t_cap, float scale, float* out, float* work,
+                              const DeviceInfo& dev, hipStream_t stream) {
+    (void)dev;
+    const int nchunks = (int)attn_chunks(t);
+    (void)hipGetLastError();
+    attn_split_kernel<<<(unsigned)(heads * nchunks), 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale,
+                                                                       nchunks, work, out);
+    if (nchunks > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        attn_combine_kernel<<<(unsigned)heads, kAttnD, 0, stream>>>(work, nchunks, out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace q8

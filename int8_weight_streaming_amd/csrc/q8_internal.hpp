@@ -34,4 +34,14 @@ hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
                           const int8_t* xq, const uint16_t* xd, float* y,
                           const DeviceInfo& dev, hipStream_t stream);
 
+// Decode attention over a Q8_0 key/value cache (head dimension 128): chunks of
+// cache rows per workgroup, and the workspace floats the chunk partials need
+// (0 when one chunk covers the context).
+int64_t attn_chunks(int64_t t);
+int64_t attn_work_floats(int64_t heads, int64_t t);
+hipError_t launch_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd,
+                              const int8_t* vq, const uint16_t* vd, int64_t heads, int64_t t,
+                              int64_t t_cap, float scale, float* out, float* work,
+                              const DeviceInfo& dev, hipStream_t stream);
+
 }  // namespace q8

@@ -135,3 +135,32 @@ def test_probe_validation(lib):
     assert lib.q8_probe_barrier(None, 4, 1, None) == NULL
     assert lib.q8_probe_barrier(0x300002, 4, 1, None) == ALIGN   # flags need 4-byte alignment
     assert lib.q8_probe_barrier_words() > 8 * 1024
+
+
+def test_attn_validation(lib):
+    f = lib.q8_attn_decode                                 # prototype set by load_library()
+    need = lib.q8_attn_work_words(2, 200)
+    assert need == 2 * 2 * 130
+    assert lib.q8_attn_work_words(12, 128) == 0
+    assert lib.q8_attn_work_words(12, 4096) == 12 * 32 * 130
+    assert lib.q8_attn_work_words(1, 0) == -1
+    args = lambda **kw: dict(dict(q=A, kq=B, kd=A, vq=B, vd=A, heads=2, t=200, t_cap=256, d=128,
+                                  scale=0.088, out=A, work=B, words=need), **kw)
+    call = lambda a: f(a["q"], a["kq"], a["kd"], a["vq"], a["vd"], a["heads"], a["t"], a["t_cap"],
+                       a["d"], a["scale"], a["out"], a["work"], a["words"], None)
+    assert call(args(d=64)) == SHAPE
+    assert call(args(t=0)) == SHAPE
+    assert call(args(t=300)) == SHAPE                      # t > t_cap
+    assert call(args(t_cap=1 << 24)) == SHAPE
+    assert call(args(scale=float("nan"))) == SHAPE
+    assert call(args(scale=float("inf"))) == SHAPE
+    assert call(args(words=need - 1)) == SHAPE
+    assert call(args(q=None)) == NULL
+    assert call(args(work=None)) == NULL
+    assert call(args(kd=MIS)) == ALIGN
+    assert call(args(heads=0, q=None, kq=None, kd=None, vq=None, vd=None, out=None, work=None)) == OK
+    # one chunk: no workspace needed
+    assert call(args(t=100, work=None, words=0)) in (DEVICE, OK)
+    import torch
+    if not torch.cuda.is_available():
+        assert call(args()) == DEVICE
