@@ -328,6 +328,85 @@ def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP) -> dict:
     return out
 
 
+ATTN_HEADS, ATTN_D, ATTN_CAP = 12, 128, 4096
+ATTN_SLABS = 40          # > 2 x the 256 MB Infinity Cache at full context
+
+
+def attn_bytes(t: int) -> int:
+    """Algorithmic bytes of one decode-attention call: K and V codes + scales of
+    t rows per head, the bf16 query and the fp32 output."""
+    return ATTN_HEADS * t * (ATTN_D + ATTN_D // 32 * 2) * 2 + ATTN_HEADS * ATTN_D * (2 + 4)
+
+
+def make_attn_slabs(q8, wl, dev, count: int = ATTN_SLABS):
+    """`count` Q8_0 K/V slabs [12][4096][128] (the pages' per-virtual-layer cache),
+    two distinct seeded ones quantized on the GPU from N(0,1) bf16 rows, the
+    rest copies at their own addresses."""
+    base = []
+    for i in range(2):
+        x = [to_dev(wl.normal_act_bf16(9500 + 2 * i + j, ATTN_HEADS * ATTN_CAP, ATTN_D), dev) for j in range(2)]
+        (kq, kd), (vq, vd) = (q8.quantize_act(a) for a in x)
+        shape, sshape = (ATTN_HEADS, ATTN_CAP, ATTN_D), (ATTN_HEADS, ATTN_CAP, ATTN_D // 32)
+        base.append((kq.view(shape), kd.view(sshape), vq.view(shape), vd.view(sshape)))
+    return [base[i % 2] if i < 2 else tuple(a.clone() for a in base[i % 2]) for i in range(count)]
+
+
+def bench_attn(q8, wl, dev, slabs) -> dict:
+    """Decode attention over the int8 cache: 12 heads x 128, graph-replayed,
+    rotating through the slabs; per call and per token (128 virtual layers)."""
+    import torch
+    q = to_dev(wl.normal_act_bf16(9600, ATTN_HEADS, ATTN_D), dev)
+    out = torch.empty((ATTN_HEADS, ATTN_D), dtype=torch.float32, device=dev)
+    work = torch.empty((q8.attn_work_words(ATTN_HEADS, ATTN_CAP),), dtype=torch.float32, device=dev)
+    scale = 1.0 / float(np.sqrt(ATTN_D))
+    res = {}
+    for t in (512, 2048, 4096):
+        cnt = [0]
+
+        def call():
+            kq, kd, vq, vd = slabs[cnt[0] % len(slabs)]
+            cnt[0] += 1
+            q8.attn_decode(q, kq, kd, vq, vd, t, scale, work=work, out=out)
+
+        us = time_graph(call, 2 * len(slabs)) * 1e3
+        nb = attn_bytes(t)
+        res[str(t)] = {"us_per_call": us, "GBps": nb / us / 1e3, "frac_hbm": nb / us / 1e3 / HBM_PEAK_GBPS,
+                       "bytes_per_call": nb, "ms_per_token_128_layers": 128 * us / 1e3}
+        log(f"attn t={t}: {us:.2f} us, {nb / us / 1e3:.0f} GB/s")
+    return res
+
+
+def bench_mimir_with_kv(q8, wl, dev, weights, slabs, t: int = 512, replays: int = 10) -> dict:
+    """One batch-1 decode token with the int8 KV read: the 513 products of the
+    Mimir step plus one decode-attention call after every qkv product (128
+    virtual layers, 12 heads x 128, context t), graph-replayed.  Bytes per token
+    = weights + KV, the pages' bytes-per-token model (Frigg, "The machine")."""
+    import torch
+    xs = {k: to_dev(wl.normal_act_bf16(9700 + k, 1, k), dev) for k in (wl.HIDDEN, wl.INTER)}
+    ys = {n: torch.empty((1, n), dtype=torch.float32, device=dev)
+          for n in {s_[1] for s_ in wl.BLOCK_SHAPES} | {wl.LM_HEAD_SHAPE[0]}}
+    q = to_dev(wl.normal_act_bf16(9601, ATTN_HEADS, ATTN_D), dev)
+    out = torch.empty((ATTN_HEADS, ATTN_D), dtype=torch.float32, device=dev)
+    work = torch.empty((max(1, q8.attn_work_words(ATTN_HEADS, t)),), dtype=torch.float32, device=dev)
+    order = wl.mimir_step_order()
+    scale = 1.0 / float(np.sqrt(ATTN_D))
+
+    def step():
+        layer = 0
+        for item in order:
+            wq, wd = weights["lm_head"] if item[0] == "lm_head" else weights[item]
+            q8.gemm_skinny(wq, wd, xs[wq.shape[1]], out=ys[wq.shape[0]])
+            if item[0] != "lm_head" and wl.BLOCK_SHAPES[item[1]][0] == "qkv":
+                kq, kd, vq, vd = slabs[layer % len(slabs)]
+                q8.attn_decode(q, kq, kd, vq, vd, t, scale, work=work, out=out)
+                layer += 1
+
+    ms = time_graph(step, 1, reps=replays)
+    nbytes = mimir_step_bytes(wl, 1) + 128 * attn_bytes(t)
+    return {"context": t, "ms_per_step": ms, "tok_per_s": 1e3 / ms, "bytes_per_step": nbytes,
+            "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": HBM_PEAK_GBPS * 1e9 / nbytes}
+
+
 def bench_sync_probe(q8, dev) -> dict:
     """What one dependency edge of a decode step costs on this GPU: the
     per-launch cost of an empty kernel under graph replay, and one grid-wide
@@ -468,6 +547,13 @@ def main() -> int:
         for m in (1, 2, 4, 8):
             log(f"mimir step m={m}")
             extras[f"mimir_step_b{m}"] = bench_mimir(q8, wl, dev, weights, m)
+        log("int8-KV decode attention")
+        slabs = make_attn_slabs(q8, wl, dev)
+        extras["attn_decode_int8kv"] = bench_attn(q8, wl, dev, slabs)
+        for t in (512, 4096):
+            log(f"mimir step with int8 KV at context {t}")
+            extras[f"mimir_step_b1_kv{t}"] = bench_mimir_with_kv(q8, wl, dev, weights, slabs, t)
+        del slabs
         log("prefill P sweep")
         extras["prefill_p256"] = bench_prefill(q8, wl, dev, weights)
         del weights

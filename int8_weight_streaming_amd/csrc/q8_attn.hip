@@ -160,18 +160,32 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
     }
 }
 
-// One workgroup per head, thread d: combine the chunks in chunk order.
+// One workgroup per head, thread d: combine the chunks.  The chunk maxima,
+// denominators and numerators are independent loads, issued eight chunks at a
+// time so their latencies overlap; every sum runs in chunk order.
 __global__ __launch_bounds__(kAttnD) void attn_combine_kernel(const float* __restrict__ work,
                                                               int nchunks, float* __restrict__ out) {
     const int h = blockIdx.x, d = threadIdx.x;
     const float* w = work + (int64_t)h * nchunks * kAttnPart;
     float mx = -INFINITY;
+#pragma unroll 8
     for (int c = 0; c < nchunks; ++c) mx = fmaxf(mx, w[c * kAttnPart + kAttnD]);
     float num = 0.0f, den = 0.0f;
-    for (int c = 0; c < nchunks; ++c) {
-        const float e = expf(w[c * kAttnPart + kAttnD] - mx);
-        num = fmaf(w[c * kAttnPart + d], e, num);
-        den = fmaf(w[c * kAttnPart + kAttnD + 1], e, den);
+    for (int c = 0; c < nchunks; c += 8) {
+        float m8[8], l8[8], o8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int cc = c + u < nchunks ? c + u : c;          // in bounds; weight 0 below
+            m8[u] = w[cc * kAttnPart + kAttnD];
+            l8[u] = w[cc * kAttnPart + kAttnD + 1];
+            o8[u] = w[cc * kAttnPart + d];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float e = c + u < nchunks ? expf(m8[u] - mx) : 0.0f;
+            num = fmaf(o8[u], e, num);
+            den = fmaf(l8[u], e, den);
+        }
     }
     out[(int64_t)h * kAttnD + d] = num / den;
 }
