@@ -87,6 +87,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, i
                                              bytes > 0 ? (int)bytes : 0, kRsrcWord3);
 }
 
+// The same with a 32-bit range (no 64-bit compare in the address arithmetic).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc32(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes > 0 ? bytes : 0,
+                                             kRsrcWord3);
+}
+
 // ---------------------------------------------------------------- reductions
 
 template <int CTRL>

@@ -37,7 +37,9 @@
 // per-step advance is scalar arithmetic, rows past the matrix fall outside the
 // descriptor's range and read as zero, and a step past the wave's last tile
 // has an empty range and touches no memory.  The scale outer product is a
-// v_mfma_f32_32x32x16_f16 on the raw binary16 scales, and the int8 product of
+// v_mfma_f32_32x32x16_f16 on the raw binary16 scales (one operand holds the
+// step's four activation scales in k = 0..3, the other one weight scale in
+// the block's k slot), and the int8 product of
 // the next block is issued before the fold of the current one, so the matrix
 // core and the vector ALUs overlap.  Tiles are dealt so that the workgroups of
 // one XCD (ids are dealt round-robin to the 8 XCDs) share its weight rows, so
@@ -275,14 +277,16 @@ __global__ __launch_bounds__(256) void prefill_stream_kernel(const int8_t* __res
         const bool live = ft < T;
         const int blk0 = wave * 4 * S + 4 * fs;
         const int64_t adv = (int64_t)blk0 * 32;
-        const int64_t pv = p - fp0 < 32 ? p - fp0 : 32;
-        const int64_t nv = n - fn0 < 32 ? n - fn0 : 32;
+        // ranges below 2^31 (rows <= 32, K <= 2^24): 32-bit range arithmetic
+        const int pv = (int)(p - fp0 < 32 ? p - fp0 : 32);
+        const int nv = (int)(n - fn0 < 32 ? n - fn0 : 32);
         const int64_t ra = live ? (int64_t)fp0 * k + adv : 0, rb = live ? (int64_t)fn0 * k + adv : 0;
         const int64_t rsa = live ? (int64_t)fp0 * nb + blk0 : 0, rsb = live ? (int64_t)fn0 * nb + blk0 : 0;
-        const auto rA = range_rsrc(xq + ra, live ? pv * k - adv : 0);
-        const auto rB = range_rsrc(wq + rb, live ? nv * k - adv : 0);
-        const auto rsA = range_rsrc(xd + rsa, live ? (pv * nb - blk0) * 2 : 0);
-        const auto rsB = range_rsrc(wd + rsb, live ? (nv * nb - blk0) * 2 : 0);
+        const int kk = (int)k, ad = (int)adv;
+        const auto rA = range_rsrc32(xq + ra, live ? pv * kk - ad : 0);
+        const auto rB = range_rsrc32(wq + rb, live ? nv * kk - ad : 0);
+        const auto rsA = range_rsrc32(xd + rsa, live ? (pv * nb - blk0) * 2 : 0);
+        const auto rsB = range_rsrc32(wd + rsb, live ? (nv * nb - blk0) * 2 : 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             st.a[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff[j], 0, 0));
@@ -305,6 +309,9 @@ __global__ __launch_bounds__(256) void prefill_stream_kernel(const int8_t* __res
     const i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     const f32x16 zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int cs = 0, cm = jw;                               // compute cursor
+    // scale operands: zero parts made opaque once, kept in registers
+    i32x4 sta = {0, 0, 0, 0}, stb[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    asm volatile("" : "+v"(sta), "+v"(stb[0]), "+v"(stb[1]));
 
     // Step q: copy the staged step into the LDS slice, refill the stage with
     // step q + 1 (scheduling barriers keep every load in issue order, so the
@@ -326,10 +333,14 @@ __global__ __launch_bounds__(256) void prefill_stream_kernel(const int8_t* __res
         issue(st);
         __builtin_amdgcn_sched_barrier(0);
 
-        // scales of the four blocks; lanes 32..63 carry the zero k = 8 term
+        // Scale outer product of block u: operand A holds the four blocks'
+        // activation scales in k = 0..3 (k = 4..15 zero), operand B the weight
+        // scale of block u in k = u only (zero on lanes 32..63, which carry
+        // k = 8..15), so the single product is xs_u * ws_u.
         const i32x4 sc = *reinterpret_cast<const i32x4*>(slS + lane * 16);
-        const unsigned sa0 = h ? 0u : (unsigned)sc[0], sa1 = h ? 0u : (unsigned)sc[1];
-        const unsigned sb0 = (unsigned)sc[2], sb1 = (unsigned)sc[3];
+        sta[0] = sc[0];
+        sta[1] = sc[1];
+        const int sb0 = h ? 0 : sc[2], sb1 = h ? 0 : sc[3];
         i32x4 av[4], bv[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -337,12 +348,13 @@ __global__ __launch_bounds__(256) void prefill_stream_kernel(const int8_t* __res
             bv[u] = *reinterpret_cast<const i32x4*>(slB + i * kPitch + u * 32 + 16 * h);
         }
         auto mm = [&](int u, i32x16& c, f32x16& t) {
-            const unsigned wa = (u >> 1) ? sa1 : sa0, wb = (u >> 1) ? sb1 : sb0;
-            const i32x4 va = {(int)((u & 1) ? wa >> 16 : wa & 0xFFFFu), 0, 0, 0};
-            const i32x4 vb = {(int)((u & 1) ? wb >> 16 : wb & 0xFFFFu), 0, 0, 0};
+            const int wb = (u >> 1) ? sb1 : sb0;
+            const int half = (u & 1) ? (wb & (int)0xFFFF0000u) : (wb & 0xFFFF);
+            stb[u & 1][0] = (u >> 1) ? 0 : half;
+            stb[u & 1][1] = (u >> 1) ? half : 0;
             c = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[u], bv[u], zi, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va),
-                                                        __builtin_bit_cast(f16x8, vb), zf, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, sta),
+                                                        __builtin_bit_cast(f16x8, stb[u & 1]), zf, 0, 0, 0);
         };
         auto fold = [&](const i32x16& c, const f32x16& t) {
 #pragma unroll
@@ -456,16 +468,20 @@ void prefill_tile64_kernel(const int8_t* __restrict__ wq,
     // scale lanes: wave 0 the activation rows, wave 1 the weight rows
     const int soff = lane * nb * 2;
 
+    // Descriptor state of step 0 of this group; a step advances every base by
+    // 128 code bytes (4 scales) and shrinks every range by as much.
+    const int8_t* const a0 = xq + p0 * k + (int64_t)step0 * 128;
+    const int8_t* const b0 = wq + n0 * k + (int64_t)step0 * 128;
+    // (ranges below 2^31: rows <= 64, K <= 2^24)
+    const int arec = (int)(pv * k - (int64_t)step0 * 128), brec = (int)(nv * k - (int64_t)step0 * 128);
+    const uint16_t* const s0 = (wave == 0 ? xd + p0 * nb : wd + n0 * nb) + (int64_t)step0 * 4;
+    const int srec = wave > 1 ? 0 : (int)(((wave == 0 ? pv : nv) * nb - (int64_t)step0 * 4) * 2);
     auto issue = [&](int lstep, T64Stage& st) {
         const bool live = lstep < S;
-        const int step = step0 + lstep;
-        const int64_t adv = (int64_t)step * 128;
-        const auto rA = range_rsrc(xq + (live ? p0 * k + adv : 0), live ? pv * k - adv : 0);
-        const auto rB = range_rsrc(wq + (live ? n0 * k + adv : 0), live ? nv * k - adv : 0);
-        const int64_t sblk = (int64_t)step * 4;
-        const uint16_t* sbase = wave == 0 ? xd + p0 * nb + sblk : wd + n0 * nb + sblk;
-        const int64_t sbytes = (!live || wave > 1) ? 0 : (wave == 0 ? pv * nb - sblk : nv * nb - sblk) * 2;
-        const auto rS = range_rsrc(sbytes > 0 ? sbase : xd, sbytes);
+        const int adv = lstep * 128;
+        const auto rA = range_rsrc32(a0 + adv, live ? arec - adv : 0);
+        const auto rB = range_rsrc32(b0 + adv, live ? brec - adv : 0);
+        const auto rS = range_rsrc32(s0 + lstep * 4, live ? srec - lstep * 8 : 0);
         st.a[0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff0, 0, 0));
         st.a[1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff1, 0, 0));
         st.b[0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, voff0, 0, 0));
@@ -497,22 +513,32 @@ void prefill_tile64_kernel(const int8_t* __restrict__ wq,
     const i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     const f32x16 zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
+    // Scale outer product of block u: operand A holds the four blocks'
+    // activation scales in k = 0..3 (the row's 8 raw bytes; k = 4..15 zero),
+    // operand B the weight scale of block u in k = u only (zero on lanes
+    // 32..63, which carry k = 8..15), so the single product is xs_u * ws_u.
+    // The zero parts of both operands are set once and never written again.
+    // (The zero halves are made opaque once, so the compiler keeps them in
+    // registers instead of writing zeros again for every block.)
+    i32x4 sta = {0, 0, 0, 0}, stb = {0, 0, 0, 0};
+    asm volatile("" : "+v"(sta), "+v"(stb));
     auto compute = [&](int buf) {
         const unsigned char* base = glds + buf * kT64Buf;
         const i32x2 sa = *reinterpret_cast<const i32x2*>(base + sa_off);
         const i32x2 sb = *reinterpret_cast<const i32x2*>(base + sb_off);
-        // scales of the four blocks; lanes 32..63 carry the zero k = 8 term
-        const unsigned sa0 = h ? 0u : (unsigned)sa[0], sa1 = h ? 0u : (unsigned)sa[1];
-        const unsigned sb0 = (unsigned)sb[0], sb1 = (unsigned)sb[1];
+        sta[0] = sa[0];
+        sta[1] = sa[1];
+        const int sb0 = h ? 0 : sb[0], sb1 = h ? 0 : sb[1];
         auto mm = [&](int u, i32x16& c, f32x16& t) {
             const i32x4 av = *reinterpret_cast<const i32x4*>(base + arow * kPitch + u * 32 + 16 * h);
             const i32x4 bv = *reinterpret_cast<const i32x4*>(base + brow * kPitch + u * 32 + 16 * h);
-            const unsigned wa = (u >> 1) ? sa1 : sa0, wb = (u >> 1) ? sb1 : sb0;
-            const i32x4 va = {(int)((u & 1) ? wa >> 16 : wa & 0xFFFFu), 0, 0, 0};
-            const i32x4 vb = {(int)((u & 1) ? wb >> 16 : wb & 0xFFFFu), 0, 0, 0};
+            const int wb = (u >> 1) ? sb1 : sb0;
+            const int half = (u & 1) ? (wb & (int)0xFFFF0000u) : (wb & 0xFFFF);
+            stb[0] = (u >> 1) ? 0 : half;
+            stb[1] = (u >> 1) ? half : 0;
             c = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, zi, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va),
-                                                        __builtin_bit_cast(f16x8, vb), zf, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, sta),
+                                                        __builtin_bit_cast(f16x8, stb), zf, 0, 0, 0);
         };
         auto fold = [&](const i32x16& c, const f32x16& t) {
 #pragma unroll
@@ -529,10 +555,6 @@ void prefill_tile64_kernel(const int8_t* __restrict__ wq,
         }
     };
 
-    // Steps 0 and 1 in flight; step 0 to buffer 0; then step s is multiplied
-    // from buffer s % 2 while step s + 1 is copied to the other buffer and
-    // steps s + 2, s + 3 are in flight.  Every load is unconditional (an empty
-    // range past K), so the compiler's counted waits stay exact.
     // The folds of a step are finished before its barrier (an empty asm that
     // takes the accumulators as operands), so the matrix products of different
     // steps are never live together.
