@@ -59,6 +59,10 @@ def lib():
         L.oracle_block_dots.argtypes = [P, I64, I64, P, I64, P]
         L.oracle_q8q8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, P]
         L.oracle_attn_decode.argtypes = [P, P, P, P, P, I64, I64, I64, I64, C.c_double, P]
+        L.oracle_q4_block_scale.argtypes = [C.c_float]
+        L.oracle_q4_block_scale.restype = C.c_uint16
+        L.oracle_q4_quantize_f32.argtypes = [P, I64, I64, P, P]
+        L.oracle_q4_unpack.argtypes = [P, I64, I64, P]
         _lib = L
     return _lib
 
@@ -175,6 +179,51 @@ def q8q8(wq, wd, xq, xd, rows=None) -> np.ndarray:
     lib().oracle_q8q8(_p(wq), _p(wd), n, k, m, _p(xq), _p(xd),
                       None if r is None else _p(r), nr, _p(y))
     return y
+
+
+def q4_block_scale(amax: float) -> int:
+    return lib().oracle_q4_block_scale(float(amax))
+
+
+def q4_quantize_f32(w: np.ndarray):
+    """fp32 [n][k] -> (packed int4 codes uint8 [n][k/2], binary16 scale bits [n][k/32])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    _check_k(k)
+    q = np.empty((n, k // 2), dtype=np.uint8)
+    d = np.empty((n, k // 32), dtype=np.uint16)
+    lib().oracle_q4_quantize_f32(_p(w), n, k, _p(q), _p(d))
+    return q, d
+
+
+def q4_unpack(q: np.ndarray) -> np.ndarray:
+    """Packed int4 codes uint8 [n][k/2] -> int8 codes [n][k] in [-8, 7]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    n, kh = q.shape
+    _check_k(2 * kh)
+    out = np.empty((n, 2 * kh), dtype=np.int8)
+    lib().oracle_q4_unpack(_p(q), n, 2 * kh, _p(out))
+    return out
+
+
+def w4a16(wq4, wd, x, rows=None) -> np.ndarray:
+    """fp64 y [m][len(rows) or n] over int4 weights: the W8A16 product of the
+    unpacked codes (only the selected rows are unpacked)."""
+    wq4 = np.ascontiguousarray(wq4, dtype=np.uint8)
+    if rows is not None:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        return w8a16(q4_unpack(wq4[r]), np.ascontiguousarray(wd)[r], x)
+    return w8a16(q4_unpack(wq4), wd, x)
+
+
+def q4q8(wq4, wd, xq, xd, rows=None) -> np.ndarray:
+    """fp64 y [m][len(rows) or n]: int4 weights times Q8 activations, the Q8 x Q8
+    product of the unpacked codes."""
+    wq4 = np.ascontiguousarray(wq4, dtype=np.uint8)
+    if rows is not None:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        return q8q8(q4_unpack(wq4[r]), np.ascontiguousarray(wd)[r], xq, xd)
+    return q8q8(q4_unpack(wq4), wd, xq, xd)
 
 
 def attn_decode(q, kq, kd, vq, vd, t: int, scale: float) -> np.ndarray:

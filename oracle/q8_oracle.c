@@ -31,6 +31,19 @@
  *    dot) and ACT 4, "How the GEMM was closed" (per-block int32 sum folded into
  *    a float accumulator with the block's scales)].
  *
+ *  - int4 weights [Frigg README, bytes-per-token table ("int4 core + int8
+ *    vocab") and benchmark matrix ("int4 W / int8 vocab"); "Known limits":
+ *    int4 is implemented there but slower and less accurate than int8].  The
+ *    pages give no int4 layout; it is read as the Q8_0 rule with the largest
+ *    4-bit magnitude in place of 127: blocks of 32 along the reduction axis,
+ *    d = maxabs / 7 (fp32 division, then binary16), codes
+ *    clamp(round_half_away(w / d), -7, 7) against the stored d, zero codes for
+ *    a zero scale.  Two codes share a byte as 4-bit two's complement: byte j of
+ *    a block holds element j in bits 0-3 and element j + 16 in bits 4-7, so a
+ *    block is 16 bytes of codes plus its 2-byte scale (0.5625 B/weight).  The
+ *    products over int4 weights are the W8A16 and Q8 x Q8 products above with
+ *    the unpacked codes (values in [-7, 7]) in place of the int8 codes.
+ *
  *  - Decode attention over a Q8_0 key/value cache [Frigg README, "The model, as
  *    verified": hidden 1536 = 12 heads x head_dim 128, multi-head attention
  *    with 12 key/value heads; "Masks": decode passes no mask, one query
@@ -165,6 +178,65 @@ void oracle_quantize_bf16(const uint16_t* x, int64_t m, int64_t k, int8_t* q, ui
             quantize_block(v, q + r * k + 32 * b, d + r * nb + b);
         }
     }
+}
+
+/* ---------- int4 weights ---------- */
+
+/* Scale of one int4 block: fp32 amax / 7, to binary16. */
+uint16_t oracle_q4_block_scale(float amax) {
+    float d = amax / 7.0f;                      /* fp32 division, correctly rounded */
+    return oracle_half_from_double((double)d);
+}
+
+/* Codes in [-7, 7] of one 32-element block of fp32 values, and its scale. */
+static void q4_codes_block(const float* v, int* c, uint16_t* d) {
+    float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    uint16_t s16 = oracle_q4_block_scale(amax);
+    *d = s16;
+    float s = (float)oracle_half_to_double(s16);
+    for (int i = 0; i < 32; ++i) {
+        if (s == 0.0f) { c[i] = 0; continue; }
+        float t = v[i] / s;                     /* fp32 division by the stored scale */
+        double r = oracle_rhaway(t);
+        if (r > 7.0) r = 7.0;
+        if (r < -7.0) r = -7.0;
+        c[i] = (int)r;
+    }
+}
+
+/* Low 4 bits of a code in two's complement (-7 -> 9, -1 -> 15, 3 -> 3). */
+static unsigned q4_nibble(int c) { return (unsigned)(c < 0 ? c + 16 : c); }
+
+/* fp32 W [n][k] -> packed codes [n][k/2], binary16 scales [n][k/32]; k % 32 == 0. */
+void oracle_q4_quantize_f32(const float* w, int64_t n, int64_t k, uint8_t* q, uint16_t* d) {
+    int64_t nb = k / 32;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            int c[32];
+            q4_codes_block(w + r * k + 32 * b, c, d + r * nb + b);
+            uint8_t* out = q + r * (k / 2) + 16 * b;
+            for (int j = 0; j < 16; ++j)
+                out[j] = (uint8_t)(q4_nibble(c[j]) | (q4_nibble(c[j + 16]) << 4));
+        }
+}
+
+/* Packed codes [n][k/2] -> one int8 per code [n][k]. */
+void oracle_q4_unpack(const uint8_t* q, int64_t n, int64_t k, int8_t* codes) {
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < k / 32; ++b) {
+            const uint8_t* in = q + r * (k / 2) + 16 * b;
+            int8_t* out = codes + r * k + 32 * b;
+            for (int j = 0; j < 16; ++j) {
+                int lo = in[j] & 15, hi = in[j] >> 4;
+                out[j] = (int8_t)(lo >= 8 ? lo - 16 : lo);
+                out[j + 16] = (int8_t)(hi >= 8 ? hi - 16 : hi);
+            }
+        }
 }
 
 /* ---------- products ---------- */
