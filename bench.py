@@ -189,32 +189,83 @@ def bench_gemv_1536(q8, wl, dev, copies: int = 256, iters: int = 2000) -> dict:
     return out
 
 
-def load_mimir(q8, wl, dev) -> dict:
-    weights = {}
+def bench_q4_lm_head(q8, wl, dev, w, m_list=(1, 2, 4, 8), per_graph: int = 20, reps: int = 10) -> dict:
+    """The lm_head shape in int4 (262144 x 1536, 226 MB per copy), two copies
+    alternated so no call finds its weights in cache; graph-replayed, HIP events
+    on the launch stream."""
+    import torch
+    cfg = wl.CONFIGS["lm_head_gemv_262144x1536_b1"]
+    n, k = w.shape
+    copies = [q8.q4_quantize_weights(w)]
+    copies.append((copies[0][0].clone(), copies[0][1].clone()))
+    out = {}
+    for act in ("bf16", "q8"):
+        for m in m_list:
+            xb = wl.rms_unit_act_bf16(cfg["x_seed"], k) if m == 1 else wl.normal_act_bf16(9800 + m, m, k)
+            x = to_dev(xb, dev)
+            xa = (x,) if act == "bf16" else q8.quantize_act(x)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for i in range(4):
+                    q8.q4_gemm_skinny(*copies[i & 1], *xa, out=y)
+            torch.cuda.current_stream().wait_stream(s)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(per_graph):
+                    q8.q4_gemm_skinny(*copies[i & 1], *xa, out=y)
+            g.replay()
+            torch.cuda.synchronize()
+            ms, _ = time_events(lambda i: g.replay(), reps)
+            us = ms * 1e3 / per_graph
+            nbytes = q4_gemv_bytes(n, k, m) - (m * k if act == "q8" else 0) + (m * k // 16 if act == "q8" else 0)
+            out[f"{act}_b{m}"] = {"us_per_call": us, "bytes_per_call": nbytes, "GBps": nbytes / us / 1e3,
+                                  "weights_per_s": n * k / us * 1e6}
+            log(f"int4 lm_head {act} m={m}: {us:.2f} us, {nbytes / us / 1e3:.0f} GB/s")
+    return out
+
+
+def load_mimir(q8, wl, dev) -> tuple[dict, dict]:
+    """The 128 block matrices and the lm_head in Q8_0, and the block matrices
+    also in int4 (the "int4 core + int8 vocab" build), from one draw each."""
+    import torch
+    weights, core_q4 = {}, {}
     for blk in range(wl.N_BLOCKS):
         for proj, (_, n, k) in enumerate(wl.BLOCK_SHAPES):
-            weights[(blk, proj)] = quantize_on_device(
-                q8, wl.normal_weights(wl.mimir_weight_seed(blk, proj), n, k), dev)
+            w = to_dev(wl.normal_weights(wl.mimir_weight_seed(blk, proj), n, k), dev)
+            weights[(blk, proj)] = q8.quantize_weights(w)
+            core_q4[(blk, proj)] = q8.q4_quantize_weights(w)
+            torch.cuda.synchronize()
+            del w
     n, k = wl.LM_HEAD_SHAPE
     weights["lm_head"] = quantize_on_device(q8, wl.normal_weights(wl.LM_HEAD_SEED, n, k), dev)
-    return weights
+    return weights, core_q4
 
 
-def mimir_step_bytes(wl, m: int) -> int:
+def q4_gemv_bytes(n: int, k: int, m: int = 1) -> int:
+    """Algorithmic bytes of one int4 product: 4-bit codes + binary16 scales,
+    m bf16 activation rows, m fp32 output rows."""
+    return n * k // 2 + n * (k // 32) * 2 + m * k * 2 + m * n * 4
+
+
+def mimir_step_bytes(wl, m: int, int4_core: bool = False) -> int:
     total = 0
     for item in wl.mimir_step_order():
         if item[0] == "lm_head":
             n, k = wl.LM_HEAD_SHAPE
+            total += gemv_bytes(n, k, m)
         else:
             _, n, k = wl.BLOCK_SHAPES[item[1]]
-        total += gemv_bytes(n, k, m)
+            total += q4_gemv_bytes(n, k, m) if int4_core else gemv_bytes(n, k, m)
     return total
 
 
-def bench_mimir(q8, wl, dev, weights, m: int, replays: int = 20) -> dict:
+def bench_mimir(q8, wl, dev, weights, m: int, replays: int = 20, core_q4=None) -> dict:
     """One decode token (m streams): 513 skinny products in recurrence order,
     captured once into a graph and replayed; eager replay of the same launches
-    is timed too."""
+    is timed too.  With `core_q4` the 512 block products use int4 weights and
+    the lm_head stays Q8_0."""
     import torch
     xs = {k: [to_dev(wl.normal_act_bf16(9000 + 16 * m + 2 * i + (k == wl.INTER), m, k), dev)
               for i in range(8)] for k in (wl.HIDDEN, wl.INTER)}
@@ -227,6 +278,10 @@ def bench_mimir(q8, wl, dev, weights, m: int, replays: int = 20) -> dict:
             if item[0] == "lm_head":
                 wq, wd = weights["lm_head"]
                 x = xs[wl.HIDDEN][0]
+            elif core_q4 is not None:
+                wq, wd = core_q4[item]
+                q8.q4_gemm_skinny(wq, wd, xs[2 * wq.shape[1]][i % 8], out=ys[wq.shape[0]])
+                continue
             else:
                 wq, wd = weights[item]
                 x = xs[wq.shape[1]][i % 8]
@@ -246,7 +301,7 @@ def bench_mimir(q8, wl, dev, weights, m: int, replays: int = 20) -> dict:
     g.replay()
     torch.cuda.synchronize()
     ms, _ = time_events(lambda i: g.replay(), replays)
-    nbytes = mimir_step_bytes(wl, m)
+    nbytes = mimir_step_bytes(wl, m, int4_core=core_q4 is not None)
     return {"m": m, "ms_per_step": ms, "tok_per_s": m * 1e3 / ms, "eager_ms_per_step": eager_ms,
             "eager_tok_per_s": m * 1e3 / eager_ms, "bytes_per_step": nbytes,
             "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": m * HBM_PEAK_GBPS * 1e9 / nbytes}
@@ -522,6 +577,13 @@ def main() -> int:
     import oracle
     oracle.set_threads(max(1, min(16, len(os.sched_getaffinity(0)))))
     oq, od = oracle.quantize_f32(w_np)
+    q4_lm = None
+    if not args.metric_only:
+        log("int4 lm_head products")
+        w_dev = to_dev(w_np, dev)
+        q4_lm = bench_q4_lm_head(q8, wl, dev, w_dev)
+        del w_dev
+        torch.cuda.empty_cache()
     del w_np
     rows = np.random.Generator(np.random.PCG64(77)).choice(n, size=4096, replace=False)
     y_host = y.cpu().numpy()[rows].astype(np.float64)
@@ -539,14 +601,20 @@ def main() -> int:
     extras["copy_probe"] = bench_copy_probe(dev)
     log(f"copy probe: {extras['copy_probe']['GBps_read_plus_write']:.1f} GB/s (read + write)")
 
+    if q4_lm is not None:
+        extras["q4_lm_head"] = q4_lm
     if not args.metric_only:
         log("gemv 1536x1536")
         extras["gemv_1536x1536_b1"] = bench_gemv_1536(q8, wl, dev)
-        log("loading Mimir weight set (32 blocks + lm_head)")
-        weights = load_mimir(q8, wl, dev)
+        log("loading Mimir weight set (32 blocks in Q8_0 and int4, lm_head in Q8_0)")
+        weights, core_q4 = load_mimir(q8, wl, dev)
         for m in (1, 2, 4, 8):
             log(f"mimir step m={m}")
             extras[f"mimir_step_b{m}"] = bench_mimir(q8, wl, dev, weights, m)
+        for m in (1, 2, 4, 8):
+            log(f"mimir step, int4 core + int8 vocab, m={m}")
+            extras[f"mimir_step_int4core_b{m}"] = bench_mimir(q8, wl, dev, weights, m, core_q4=core_q4)
+        del core_q4
         log("int8-KV decode attention")
         slabs = make_attn_slabs(q8, wl, dev)
         extras["attn_decode_int8kv"] = bench_attn(q8, wl, dev, slabs)

@@ -176,6 +176,39 @@ q8_status q8_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd
 /* Workspace words q8_attn_decode needs for (heads, t); -1 when out of range. */
 int64_t q8_attn_work_words(int64_t heads, int64_t t);
 
+/* ---- int4 weights ----------------------------------------------------------
+ *
+ * The pages price and measure an "int4 core + int8 vocab" build (Frigg README:
+ * bytes-per-token table, benchmark matrix row "int4 W / int8 vocab"; "Known
+ * limits" reports int4 as slower and less accurate than int8 there) but give no
+ * int4 layout.  It is read as the Q8_0 rule above with 7 in place of 127:
+ * blocks of 32 along K, one binary16 scale d = maxabs / 7 (fp32 quotient
+ * rounded to binary16, nearest-even), codes clamp(round_half_away(w / d), -7, 7)
+ * against the stored d, all-zero codes for a zero scale.  Codes are packed two
+ * per byte as 4-bit two's complement: byte j of a block's 16 bytes holds element
+ * j in bits 0-3 and element j + 16 in bits 4-7.
+ *   int4 codes [rows][K/2] bytes (row pitch K/2), scales [rows][K/32] binary16;
+ *   18 bytes per 32 weights (0.5625 B/weight).
+ * Conventions (pointers, alignment, ownership, asynchrony, errors, empty calls,
+ * determinism) are those of the Q8_0 calls. */
+
+/* Quantize fp32 weights W [n][k] into packed int4 codes wq [n][k/2] and
+ * binary16 scales wd [n][k/32] with the rule above.  Offline work. */
+q8_status q4_quantize_weights(const float* w, int64_t n, int64_t k,
+                              uint8_t* wq, uint16_t* wd, hipStream_t stream);
+
+/* Batch 0..8 product over int4 weights, reading every weight byte once for all
+ * m rows [Frigg README, Finding 8; "The machine": at batch 1 the time is weight
+ * bytes / bandwidth]:
+ *   y[t][j] = sum_b wd[j][b] * sum_{i<32} c[j][32b+i] * x[t][32b+i],
+ * c the unpacked codes.  act Q8_ACT_BF16: x is bf16 [m][k], xd NULL, fp32
+ * accumulation.  act Q8_ACT_Q8: x is int8 codes [m][k] with binary16 xd
+ * [m][k/32]; each block contributes wd * xd * (exact int32 sum of code
+ * products).  y is fp32 [m][n]. */
+q8_status q4_gemm_skinny(const uint8_t* wq, const uint16_t* wd, int64_t n, int64_t k,
+                         int64_t m, int act, const void* x, const uint16_t* xd,
+                         float* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,9 @@ Names mirror the C entry points:
     gemm_skinny(wq, wd, x, xd=None) x [m][k], m <= 8      -> y fp32 [m][n]
     gemm_prefill(wq, wd, xq, xd)   xq int8 [p][k]         -> y fp32 [p][n]
     block_dots(wq, xq)             xq int8 [m][k]         -> isum int32 [m][n][k/32]
+    attn_decode(q, kq, kd, vq, vd, t, scale)              -> out fp32 [heads][128]
+    q4_quantize_weights(w)         fp32 [n][k]            -> (wq uint8 [n][k/2], wd uint16 [n][k/32])
+    q4_gemm_skinny(wq, wd, x, xd=None) int4 weights, m <= 8 -> y fp32 [m][n]
 
 Binary16 scales travel as torch.uint16 tensors holding the bit patterns
 (``wd.view(torch.float16)`` gives the values).
@@ -37,6 +40,7 @@ EXPORTED = (
     "q8_abi_version", "q8_status_str", "q8_last_hip_error",
     "q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
     "q8_gemm_prefill", "q8_block_dots", "q8_attn_decode", "q8_attn_work_words",
+    "q4_quantize_weights", "q4_gemm_skinny",
 )
 PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words", "q8_probe_barrier",
                   "q8_probe_barrier_words")
@@ -81,8 +85,10 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q8_probe_barrier.argtypes = [P, I, I, P]
     L.q8_probe_barrier.restype = I
     L.q8_probe_barrier_words.restype = I64
+    L.q4_quantize_weights.argtypes = [P, I64, I64, P, P, P]
+    L.q4_gemm_skinny.argtypes = [P, P, I64, I64, I64, I, P, P, P, P]
     for name in ("q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
-                 "q8_gemm_prefill", "q8_block_dots"):
+                 "q8_gemm_prefill", "q8_block_dots", "q4_quantize_weights", "q4_gemm_skinny"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -238,6 +244,51 @@ def block_dots(wq, xq, out=None):
     _check("q8_block_dots", load_library().q8_block_dots(
         _ptr(wq), n, k, m, _ptr(xq), _ptr(isum), _stream()))
     return isum
+
+
+# ------------------------------------------------------------------ int4 weights
+
+def q4_quantize_weights(w: torch.Tensor, out=None):
+    """fp32 [n][k] -> (packed int4 codes uint8 [n][k/2], binary16 scale bits uint16 [n][k/32])."""
+    _need(w, "w", torch.float32, 2)
+    n, k = w.shape
+    if out is None:
+        wq = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+        wd = torch.empty((n, k // 32), dtype=torch.uint16, device=w.device)
+    else:
+        wq, wd = out
+    _check("q4_quantize_weights", load_library().q4_quantize_weights(
+        _ptr(w), n, k, _ptr(wq), _ptr(wd), _stream()))
+    return wq, wd
+
+
+def q4_gemm_skinny(wq, wd, x, xd=None, out=None):
+    """y fp32 [m][n] over int4 weights (wq uint8 [n][k/2], wd [n][k/32]) for
+    m = x.shape[0] <= 8; x bf16 [m][k] or int8 codes with xd [m][k/32]."""
+    _need(wq, "wq", torch.uint8, 2)
+    wd = _as_bits16(wd)
+    _need(wd, "wd", torch.uint16, 2)
+    n, k = wq.shape[0], 2 * wq.shape[1]
+    if tuple(wd.shape) != (n, k // 32):
+        raise ValueError(f"wd must be [{n}][{k // 32}], got {tuple(wd.shape)}")
+    if xd is None:
+        x = _as_bits16(x)
+        _need(x, "x", torch.uint16, 2)
+        act = Q8_ACT_BF16
+    else:
+        _need(x, "x", torch.int8, 2)
+        xd = _as_bits16(xd)
+        _need(xd, "xd", torch.uint16, 2)
+        if tuple(xd.shape) != (x.shape[0], k // 32):
+            raise ValueError("xd must be [m][k/32]")
+        act = Q8_ACT_Q8
+    m = x.shape[0]
+    if x.shape[1] != k:
+        raise ValueError(f"x must have {k} columns, got {x.shape[1]}")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=wq.device)
+    _check("q4_gemm_skinny", load_library().q4_gemm_skinny(
+        _ptr(wq), _ptr(wd), n, k, m, act, _ptr(x), _ptr(xd), _ptr(y), _stream()))
+    return y
 
 
 def attn_work_words(heads: int, t: int) -> int:

@@ -213,6 +213,35 @@ q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m, const
     return finish(q8::launch_block_dots(wq, n, k, (int)m, xq, isum, *dev, stream));
 }
 
+q8_status q4_quantize_weights(const float* w, int64_t n, int64_t k, uint8_t* wq, uint16_t* wd,
+                              hipStream_t stream) {
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(n, k));
+    if (n == 0) return Q8_OK;
+    if (!w || !wq || !wd) return Q8_ERR_NULL;
+    if (!aligned16(w) || !aligned16(wq) || !aligned16(wd)) return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_q4_quantize(w, n * (k / 32), wq, wd, *dev, stream));
+}
+
+q8_status q4_gemm_skinny(const uint8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t m,
+                         int act, const void* x, const uint16_t* xd, float* y,
+                         hipStream_t stream) {
+    Q8_TRY(check_act(act, xd));
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(n, k));
+    if (m < 0 || m > Q8_MAX_BATCH) return Q8_ERR_BATCH;
+    if (n == 0 || m == 0) return Q8_OK;
+    if (!wq || !wd || !x || !y) return Q8_ERR_NULL;
+    if (!aligned16(wq) || !aligned16(wd) || !aligned16(x) || !aligned16(y) ||
+        (xd && !aligned16(xd)))
+        return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_q4_skinny(wq, wd, n, k, (int)m, act, x, xd, y, *dev, stream));
+}
+
 int64_t q8_attn_work_words(int64_t heads, int64_t t) {
     if (heads < 0 || heads > kMaxAttnHeads || t < 1 || t > kMaxAttnRows) return -1;
     return q8::attn_work_floats(heads, t);

@@ -25,6 +25,13 @@ hipError_t launch_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_
 hipError_t launch_block_dots(const int8_t* wq, int64_t n, int64_t k, int m, const int8_t* xq,
                              int32_t* isum, const DeviceInfo& dev, hipStream_t stream);
 
+// int4 weights (two codes per byte, binary16 scale per 32-element block).
+hipError_t launch_q4_quantize(const float* w, int64_t nblocks, uint8_t* q, uint16_t* d,
+                              const DeviceInfo& dev, hipStream_t stream);
+hipError_t launch_q4_skinny(const uint8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int m,
+                            int act, const void* x, const uint16_t* xd, float* y,
+                            const DeviceInfo& dev, hipStream_t stream);
+
 // LDS the prefill kernel chosen for this shape needs, and the one-time
 // per-device setup that lets it use up to dev.max_lds.
 size_t prefill_lds_bytes(int64_t n, int64_t k, int64_t p, const DeviceInfo& dev);

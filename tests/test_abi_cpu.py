@@ -22,7 +22,7 @@ MIS = 0x300004        # misaligned
 def declared_functions(header=HEADER):
     text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q8_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q[48]_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -117,6 +117,28 @@ def test_prefill_and_block_dots_validation(lib):
     assert g(None, 0, 64, 1, None, None, None) == OK
 
 
+def test_q4_validation(lib):
+    f = lib.q4_quantize_weights
+    assert f(A, 4, 48, A, B, None) == SHAPE
+    assert f(A, -1, 64, A, B, None) == SHAPE
+    assert f(None, 4, 64, A, B, None) == NULL
+    assert f(A, 4, 64, None, B, None) == NULL
+    assert f(A, 4, 64, A, MIS, None) == ALIGN
+    assert f(None, 0, 64, None, None, None) == OK
+    g = lib.q4_gemm_skinny
+    assert g(A, B, 8, 64, 1, 2, A, None, A, None) == ENUM
+    assert g(A, B, 8, 64, 1, 0, A, B, A, None) == ENUM
+    assert g(A, B, 8, 64, 1, 1, A, None, A, None) == ENUM
+    assert g(A, B, 8, 40, 1, 0, A, None, A, None) == SHAPE
+    assert g(A, B, 8, 64, 9, 0, A, None, A, None) == BATCH
+    assert g(None, B, 8, 64, 1, 0, A, None, A, None) == NULL
+    assert g(A, B, 8, 64, 1, 0, A, None, None, None) == NULL
+    assert g(MIS, B, 8, 64, 1, 0, A, None, A, None) == ALIGN
+    assert g(A, B, 8, 64, 1, 1, A, MIS, A, None) == ALIGN
+    assert g(None, None, 0, 64, 3, 0, None, None, None, None) == OK
+    assert g(None, None, 5, 64, 0, 1, None, B, None, None) == OK
+
+
 def test_valid_arguments_without_gpu_report_device(lib):
     """With valid arguments the call reaches the device check; with no usable
     gfx950 it refuses with Q8_ERR_DEVICE instead of launching anything."""
@@ -125,6 +147,7 @@ def test_valid_arguments_without_gpu_report_device(lib):
         pytest.skip("a GPU is present")
     assert lib.q8_gemm_skinny(A, B, 8, 64, 1, 0, A, None, A, None) == DEVICE
     assert lib.q8_quantize_weights(A, 4, 64, A, B, None) == DEVICE
+    assert lib.q4_gemm_skinny(A, B, 8, 64, 2, 0, A, None, A, None) == DEVICE
 
 
 def test_probe_validation(lib):
