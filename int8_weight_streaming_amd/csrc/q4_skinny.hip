@@ -88,7 +88,9 @@ hipError_t launch_q4_quantize(const float* w, int64_t nblocks, uint8_t* q, uint1
 __device__ __forceinline__ uint32_t q4_low16(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t q4_high16(uint32_t w) { return w & 0xF0F0F0F0u; }
 
-template <int M, int ACT, int G, int R, int CPL>
+// XL = 1 stages each K tile's activations in LDS (shared by the workgroup's
+// rows); XL = 0 keeps them in the registers of the lanes that use them.
+template <int M, int ACT, int G, int R, int CPL, int XL>
 __global__ __launch_bounds__(256) void q4_skinny_kernel(const uint8_t* __restrict__ wq,
                                                         const uint16_t* __restrict__ wd, int64_t n,
                                                         int nb, const void* __restrict__ xv,
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256) void q4_skinny_kernel(const uint8_t* __restric
     constexpr int GPW = 64 / G;                  // lane groups per wave
     constexpr int RPW = 4 * GPW * R;             // rows per workgroup
     constexpr int TCH = G * CPL;                 // blocks per K tile
-    constexpr bool XREG = M <= 2;                // activations of a tile in registers
+    constexpr bool XREG = XL == 0;
     constexpr int XW = ACT == 0 ? 16 : 8;        // activation words per block and row
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int gl = lane & (G - 1), grp = lane / G;
@@ -296,15 +298,15 @@ __global__ __launch_bounds__(256) void q4_skinny_kernel(const uint8_t* __restric
     }
 }
 
-template <int M, int ACT, int G, int R, int CPL>
+template <int M, int ACT, int G, int R, int CPL, int XL>
 static hipError_t q4_launch_cfg(const uint8_t* wq, const uint16_t* wd, int64_t n, int nb,
                                 const void* x, const uint16_t* xd, float* y, hipStream_t stream) {
     constexpr int RPW = 4 * (64 / G) * R;
     constexpr int TCH = G * CPL;
     size_t lds = 0;
-    if (M > 2) lds = ACT == 0 ? (size_t)M * TCH * 64 : (size_t)M * TCH * 32 + (size_t)M * TCH * 4;
+    if (XL) lds = ACT == 0 ? (size_t)M * TCH * 64 : (size_t)M * TCH * 32 + (size_t)M * TCH * 4;
     const int64_t grid = (n + RPW - 1) / RPW;
-    q4_skinny_kernel<M, ACT, G, R, CPL><<<(unsigned)grid, 256, lds, stream>>>(wq, wd, n, nb, x, xd, y);
+    q4_skinny_kernel<M, ACT, G, R, CPL, XL><<<(unsigned)grid, 256, lds, stream>>>(wq, wd, n, nb, x, xd, y);
     return hipGetLastError();
 }
 
@@ -313,18 +315,33 @@ static hipError_t q4_launch_m(const uint8_t* wq, const uint16_t* wd, int64_t n, 
                               const void* x, const uint16_t* xd, float* y,
                               const DeviceInfo& dev, hipStream_t stream) {
     (void)hipGetLastError();
-    // Tall matrices: 16-lane groups, 2 rows each, 3 blocks per lane per K tile
-    // (K = 1536 in one tile).  Shorter ones: 32-lane groups of one row, so that
-    // the grid still covers every compute unit.  Above batch 2 the staged tile
-    // is at most 64 blocks (32 KiB of bf16 activations at batch 8).
-    const int64_t tall_wgs = (n + 31) / 32;
-    if (tall_wgs >= (int64_t)dev.cu_count * (M <= 2 ? 1 : 4))
-        return q4_launch_cfg<M, ACT, 16, 2, 3>(wq, wd, n, nb, x, xd, y, stream);
-    if (nb <= 64) return q4_launch_cfg<M, ACT, 32, 1, 2>(wq, wd, n, nb, x, xd, y, stream);
+    // Configurations measured on the Mimir shapes and the 262144 x 1536 lm_head
+    // (graph replay, weights rotated past the caches, batch 1, 2, 4 and 8).  The
+    // bf16 form is bound by its arithmetic (unpack, convert, dot), so lane
+    // occupancy decides more than for the Q8_0 products:
+    //  * at least 4 workgroups of 64 rows per compute unit: 16-lane groups; at
+    //    batch 1 two rows each and 16-block K tiles (bf16) or 48-block tiles
+    //    (Q8); above that four rows each with the activation tile in LDS;
+    //  * from half a workgroup of 32 rows per compute unit: 16-lane groups of
+    //    two rows, 48-block tiles (K = 1536 in one tile);
+    //  * shorter matrices: one row per 32-lane group, 64-block tiles; for K
+    //    above 2048 at batch 1-2 a 128-block tile, above that one wave per row
+    //    with 128-block tiles staged in LDS.
+    if ((n + 63) / 64 >= 4 * (int64_t)dev.cu_count) {
+        if constexpr (M == 1) {
+            if constexpr (ACT == 0) return q4_launch_cfg<M, ACT, 16, 2, 1, 0>(wq, wd, n, nb, x, xd, y, stream);
+            else return q4_launch_cfg<M, ACT, 16, 2, 3, 0>(wq, wd, n, nb, x, xd, y, stream);
+        } else {
+            return q4_launch_cfg<M, ACT, 16, 4, 3, 1>(wq, wd, n, nb, x, xd, y, stream);
+        }
+    }
+    if (2 * ((n + 31) / 32) >= (int64_t)dev.cu_count)
+        return q4_launch_cfg<M, ACT, 16, 2, 3, (M > 2)>(wq, wd, n, nb, x, xd, y, stream);
+    if (nb <= 64) return q4_launch_cfg<M, ACT, 32, 1, 2, (M > 2)>(wq, wd, n, nb, x, xd, y, stream);
     if constexpr (M <= 2) {
-        return q4_launch_cfg<M, ACT, 32, 1, 4>(wq, wd, n, nb, x, xd, y, stream);
+        return q4_launch_cfg<M, ACT, 32, 1, 4, 0>(wq, wd, n, nb, x, xd, y, stream);
     } else {
-        return q4_launch_cfg<M, ACT, 64, 1, 1>(wq, wd, n, nb, x, xd, y, stream);
+        return q4_launch_cfg<M, ACT, 64, 1, 2, 1>(wq, wd, n, nb, x, xd, y, stream);
     }
 }
 
