@@ -128,6 +128,23 @@ def test_attn_repeat_graph_replay_and_guard_band():
     assert_close(to_host(ref), oracle.attn_decode(q, kq, kd, vq, vd, t, SCALE), "attn replay")
 
 
+def test_attn_one_workspace_across_context_lengths():
+    """One workspace serves back-to-back calls on one stream with different t
+    (different chunk counts, so the partials land at different places), in any
+    order, with no synchronization between them."""
+    heads, t_cap = 12, 4096
+    q, kq, kd, vq, vd = cache(9350, heads, t_cap, t_cap)
+    dq, dkq, dkd, dvq, dvd = (to_dev(a) for a in (q, kq, kd, vq, vd))
+    work = torch.full((q8.attn_work_words(heads, t_cap),), float("nan"), dtype=torch.float32, device=DEV)
+    ts = [4096, 129, 1000, 4000, 256, 257, 3001, 128, 2048]
+    outs = [q8.attn_decode(dq, dkq, dkd, dvq, dvd, t, SCALE, work=work) for t in ts]   # no syncs between
+    torch.cuda.synchronize()
+    for t, y in zip(ts, outs):
+        log(f"attn shared workspace t={t}")
+        assert_close(to_host(y), oracle.attn_decode(q, kq, kd, vq, vd, t, SCALE), f"shared workspace t={t}")
+        assert torch.equal(y, q8.attn_decode(dq, dkq, dkd, dvq, dvd, t, SCALE))
+
+
 def test_attn_rejects_bad_arguments():
     q, kq, kd, vq, vd = cache(9400, 2, 10, 16)
     dq, dkq, dkd, dvq, dvd = (to_dev(a) for a in (q, kq, kd, vq, vd))
