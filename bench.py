@@ -184,8 +184,9 @@ def bench_gemv_1536(q8, wl, dev, copies: int = 256, iters: int = 2000) -> dict:
         reps = max(1, iters // per_graph)
         ms, _ = time_events(lambda i: g.replay(), reps)
         per_call_us = ms * 1e3 / per_graph
+        gbps = gemv_bytes(n, k) / per_call_us / 1e3
         out[label] = {"us_per_gemv": per_call_us, "gemv_per_s": 1e6 / per_call_us,
-                      "GBps": gemv_bytes(n, k) / per_call_us / 1e3}
+                      "GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
     return out
 
 
@@ -221,6 +222,7 @@ def bench_q4_lm_head(q8, wl, dev, w, m_list=(1, 2, 4, 8), per_graph: int = 20, r
             us = ms * 1e3 / per_graph
             nbytes = q4_gemv_bytes(n, k, m) - (m * k if act == "q8" else 0) + (m * k // 16 if act == "q8" else 0)
             out[f"{act}_b{m}"] = {"us_per_call": us, "bytes_per_call": nbytes, "GBps": nbytes / us / 1e3,
+                                  "frac_hbm_peak": nbytes / us / 1e3 / HBM_PEAK_GBPS,
                                   "weights_per_s": n * k / us * 1e6}
             log(f"int4 lm_head {act} m={m}: {us:.2f} us, {nbytes / us / 1e3:.0f} GB/s")
     return out
@@ -304,7 +306,8 @@ def bench_mimir(q8, wl, dev, weights, m: int, replays: int = 20, core_q4=None) -
     nbytes = mimir_step_bytes(wl, m, int4_core=core_q4 is not None)
     return {"m": m, "ms_per_step": ms, "tok_per_s": m * 1e3 / ms, "eager_ms_per_step": eager_ms,
             "eager_tok_per_s": m * 1e3 / eager_ms, "bytes_per_step": nbytes,
-            "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": m * HBM_PEAK_GBPS * 1e9 / nbytes}
+            "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": m * HBM_PEAK_GBPS * 1e9 / nbytes,
+            "frac_hbm_roofline": (m * 1e3 / ms) / (m * HBM_PEAK_GBPS * 1e9 / nbytes)}
 
 
 def time_graph(fn, per_graph: int, reps: int = 3, trials: int = 3) -> float:
@@ -459,7 +462,8 @@ def bench_mimir_with_kv(q8, wl, dev, weights, slabs, t: int = 512, replays: int 
     ms = time_graph(step, 1, reps=replays)
     nbytes = mimir_step_bytes(wl, 1) + 128 * attn_bytes(t)
     return {"context": t, "ms_per_step": ms, "tok_per_s": 1e3 / ms, "bytes_per_step": nbytes,
-            "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": HBM_PEAK_GBPS * 1e9 / nbytes}
+            "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": HBM_PEAK_GBPS * 1e9 / nbytes,
+            "frac_hbm_roofline": (1e3 / ms) / (HBM_PEAK_GBPS * 1e9 / nbytes)}
 
 
 def bench_sync_probe(q8, dev) -> dict:
