@@ -63,6 +63,9 @@ def lib():
         L.oracle_q4_block_scale.restype = C.c_uint16
         L.oracle_q4_quantize_f32.argtypes = [P, I64, I64, P, P]
         L.oracle_q4_unpack.argtypes = [P, I64, I64, P]
+        L.oracle_rmsnorm.argtypes = [P, I64, I64, C.c_double, P]
+        L.oracle_rope.argtypes = [P, I64, I64, I64, C.c_double]
+        L.oracle_swiglu.argtypes = [P, P, I64, P]
         _lib = L
     return _lib
 
@@ -224,6 +227,40 @@ def q4q8(wq4, wd, xq, xd, rows=None) -> np.ndarray:
         r = np.ascontiguousarray(rows, dtype=np.int64)
         return q8q8(q4_unpack(wq4[r]), np.ascontiguousarray(wd)[r], xq, xd)
     return q8q8(q4_unpack(wq4), wd, xq, xd)
+
+
+# ---------------------------------------------------------------- decode-step glue
+
+RMS_EPS = 1e-6
+ROPE_THETA = 10000.0
+
+
+def rmsnorm(x, eps: float = RMS_EPS) -> np.ndarray:
+    """fp64 [m][k]: weightless RMSNorm of the fp32 rows of x."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    m, k = x.shape
+    y = np.empty((m, k), dtype=np.float64)
+    lib().oracle_rmsnorm(_p(x), m, k, float(eps), _p(y))
+    return y
+
+
+def rope(v, heads: int, d: int, pos: int, theta: float = ROPE_THETA) -> np.ndarray:
+    """fp64 copy of v (heads x d values, natural dimension order) turned by the
+    default rotary embedding at position pos."""
+    out = np.ascontiguousarray(v, dtype=np.float64).copy()
+    assert out.size == heads * d and d % 2 == 0
+    lib().oracle_rope(_p(out), heads, d, int(pos), float(theta))
+    return out
+
+
+def swiglu(g, u) -> np.ndarray:
+    """fp64 g / (1 + e^-g) * u, elementwise."""
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    assert g.shape == u.shape
+    s = np.empty(g.shape, dtype=np.float64)
+    lib().oracle_swiglu(_p(g), _p(u), g.size, _p(s))
+    return s
 
 
 def attn_decode(q, kq, kd, vq, vd, t: int, scale: float) -> np.ndarray:

@@ -31,6 +31,14 @@
  *    dot) and ACT 4, "How the GEMM was closed" (per-block int32 sum folded into
  *    a float accumulator with the block's scales)].
  *
+ *  - The glue of a decode step [Frigg README, "The model, as verified": RMSNorm
+ *    with no learnable weight, eps 1e-6, pre-norm and a final norm per module;
+ *    RoPE with theta 10,000 and the default rotation; SwiGLU MLP; residual
+ *    stream]: rmsnorm(x)_i = x_i / sqrt(mean_j x_j^2 + 1e-6); the default
+ *    rotation pairs dimension i with i + 64 of a 128-wide head and turns the
+ *    pair by pos * 10000^(-i/64); swiglu(g, u) = g / (1 + e^-g) * u.  All in
+ *    fp64 from fp32 inputs.
+ *
  *  - int4 weights [Frigg README, bytes-per-token table ("int4 core + int8
  *    vocab") and benchmark matrix ("int4 W / int8 vocab"); "Known limits":
  *    int4 is implemented there but slower and less accurate than int8].  The
@@ -178,6 +186,40 @@ void oracle_quantize_bf16(const uint16_t* x, int64_t m, int64_t k, int8_t* q, ui
             quantize_block(v, q + r * k + 32 * b, d + r * nb + b);
         }
     }
+}
+
+/* ---------- decode-step glue ---------- */
+
+/* Weightless RMSNorm of each of m rows of length k: y = x / sqrt(mean(x^2) + eps). */
+void oracle_rmsnorm(const float* x, int64_t m, int64_t k, double eps, double* y) {
+    for (int64_t r = 0; r < m; ++r) {
+        double ss = 0.0;
+        for (int64_t i = 0; i < k; ++i) ss += (double)x[r * k + i] * (double)x[r * k + i];
+        const double inv = 1.0 / sqrt(ss / (double)k + eps);
+        for (int64_t i = 0; i < k; ++i) y[r * k + i] = (double)x[r * k + i] * inv;
+    }
+}
+
+/* Rotary embedding of `heads` heads of width d (even) at position pos, in place
+ * on fp64 values: dimension i < d/2 pairs with i + d/2 and the pair turns by
+ * pos * theta^(-2i/d). */
+void oracle_rope(double* v, int64_t heads, int64_t d, int64_t pos, double theta) {
+    const int64_t half = d / 2;
+    for (int64_t h = 0; h < heads; ++h)
+        for (int64_t i = 0; i < half; ++i) {
+            const double ang = (double)pos * pow(theta, -2.0 * (double)i / (double)d);
+            const double c = cos(ang), sn = sin(ang);
+            double* a = v + h * d + i;
+            double* b = v + h * d + i + half;
+            const double x0 = *a, x1 = *b;
+            *a = x0 * c - x1 * sn;
+            *b = x1 * c + x0 * sn;
+        }
+}
+
+/* SwiGLU: s_j = g_j / (1 + exp(-g_j)) * u_j, n values. */
+void oracle_swiglu(const double* g, const double* u, int64_t n, double* s) {
+    for (int64_t j = 0; j < n; ++j) s[j] = g[j] / (1.0 + exp(-g[j])) * u[j];
 }
 
 /* ---------- int4 weights ---------- */
