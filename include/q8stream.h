@@ -177,6 +177,52 @@ q8_status q8_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd
 /* Workspace words q8_attn_decode needs for (heads, t); -1 when out of range. */
 int64_t q8_attn_work_words(int64_t heads, int64_t t);
 
+/* ---- decode-step glue fused into the W8A16 products ---------------------------
+ *
+ * A decode block [Frigg README, "The model, as verified": pre-norm blocks,
+ * RMSNorm without a learnable weight (eps 1e-6) and a final norm per module run;
+ * rotary embedding with theta 10,000, default rotation; SwiGLU MLP; 12 heads of
+ * 128] needs glue between its products.  q8_gemm_fused runs a W8A16 product
+ * (Q8_0 weights, fp32 accumulation, m = 0..8 rows) with one prologue on its
+ * activations and one epilogue on its outputs, so a block is its four product
+ * launches plus attention.
+ *
+ * Prologues (x, row-major [m][k]):
+ *   Q8_PRO_BF16     x is bf16, used as is.
+ *   Q8_PRO_F32      x is fp32, rounded to bf16 (nearest, ties to even).
+ *   Q8_PRO_RMSNORM  x is fp32; each row is scaled by 1 / sqrt(mean(x^2) + 1e-6)
+ *                   (fp32 arithmetic, the reduction of q8_rmsnorm) and rounded
+ *                   to bf16.
+ * Epilogues (y[t][j] = the product, fp32):
+ *   Q8_EPI_F32      out fp32 [m][n] = y.
+ *   Q8_EPI_ADD      out fp32 [m][n] += y (the residual stream; read and written).
+ *   Q8_EPI_SWIGLU   n even; rows 2j and 2j + 1 are gate_j and up_j; out bf16
+ *                   [m][n/2]: out[t][j] = bf16(g / (1 + exp(-g)) * u).
+ *   Q8_EPI_ROPE     n even; rows [0, rope_rows) (rope_rows a multiple of 128)
+ *                   hold heads of 128 in pair order: row 2(64h + i) is dimension
+ *                   i of head h and the next row dimension i + 64; each pair
+ *                   (a, b) turns by the angle pos * 10000^(-i/64) (computed in
+ *                   fp64): out[t][128h + i] = bf16(a cos - b sin),
+ *                   out[t][128h + i + 64] = bf16(b cos + a sin).  Rows from
+ *                   rope_rows on are copied: out[t][j] = bf16(y[t][j]).  out bf16
+ *                   [m][n] in natural dimension order.
+ * Supported pairs (others return Q8_ERR_ENUM): RMSNORM+ROPE (qkv), F32+ADD (o),
+ * RMSNORM+SWIGLU (gate/up), BF16+ADD (down), F32+F32 and RMSNORM+F32 (lm_head).
+ * `out` must not overlap x, wq or wd.  rope_rows and pos are read only by the
+ * ROPE epilogue (0 <= rope_rows <= n, 0 <= pos < 2^31).  Other conventions are
+ * those of the Q8_0 products. */
+typedef enum { Q8_PRO_BF16 = 0, Q8_PRO_F32 = 1, Q8_PRO_RMSNORM = 2 } q8_prologue;
+typedef enum { Q8_EPI_F32 = 0, Q8_EPI_ADD = 1, Q8_EPI_SWIGLU = 2, Q8_EPI_ROPE = 3 } q8_epilogue;
+
+q8_status q8_gemm_fused(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t m,
+                        int prologue, const void* x, int epilogue, void* out,
+                        int64_t rope_rows, int64_t pos, hipStream_t stream);
+
+/* Weightless RMSNorm of m fp32 rows of length k (the final norm of a module
+ * run): y = x / sqrt(mean(x^2) + 1e-6), fp32, with the same reduction as the
+ * RMSNORM prologue.  y may be x (in place).  1 <= k < 2^31, 0 <= m < 2^31. */
+q8_status q8_rmsnorm(const float* x, int64_t m, int64_t k, float* y, hipStream_t stream);
+
 /* ---- int4 weights ----------------------------------------------------------
  *
  * The pages price and measure an "int4 core + int8 vocab" build (Frigg README:

@@ -17,6 +17,9 @@ Names mirror the C entry points:
     attn_decode(q, kq, kd, vq, vd, t, scale)              -> out fp32 [heads][128]
     q4_quantize_weights(w)         fp32 [n][k]            -> (wq uint8 [n][k/2], wd uint16 [n][k/32])
     q4_gemm_skinny(wq, wd, x, xd=None) int4 weights, m <= 8 -> y fp32 [m][n]
+    gemm_fused(wq, wd, x, prologue, epilogue, out=None, rope_rows=0, pos=0)
+                                   W8A16 product with decode-step glue (see q8stream.h)
+    rmsnorm(x, out=None)           fp32 [m][k] -> weightless RMSNorm, fp32
 
 Binary16 scales travel as torch.uint16 tensors holding the bit patterns
 (``wd.view(torch.float16)`` gives the values).
@@ -34,13 +37,15 @@ LIB_PATH = os.path.join(_HERE, "libq8stream.so")
 Q8_OK = 0
 Q8_ACT_BF16 = 0
 Q8_ACT_Q8 = 1
+PRO_BF16, PRO_F32, PRO_RMSNORM = 0, 1, 2
+EPI_F32, EPI_ADD, EPI_SWIGLU, EPI_ROPE = 0, 1, 2, 3
 MAX_BATCH = 8
 
 EXPORTED = (
     "q8_abi_version", "q8_status_str", "q8_last_hip_error",
     "q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
     "q8_gemm_prefill", "q8_block_dots", "q8_attn_decode", "q8_attn_work_words",
-    "q4_quantize_weights", "q4_gemm_skinny",
+    "q4_quantize_weights", "q4_gemm_skinny", "q8_gemm_fused", "q8_rmsnorm",
 )
 PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words", "q8_probe_barrier",
                   "q8_probe_barrier_words")
@@ -87,8 +92,11 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q8_probe_barrier_words.restype = I64
     L.q4_quantize_weights.argtypes = [P, I64, I64, P, P, P]
     L.q4_gemm_skinny.argtypes = [P, P, I64, I64, I64, I, P, P, P, P]
+    L.q8_gemm_fused.argtypes = [P, P, I64, I64, I64, I, P, I, P, I64, I64, P]
+    L.q8_rmsnorm.argtypes = [P, I64, I64, P, P]
     for name in ("q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
-                 "q8_gemm_prefill", "q8_block_dots", "q4_quantize_weights", "q4_gemm_skinny"):
+                 "q8_gemm_prefill", "q8_block_dots", "q4_quantize_weights", "q4_gemm_skinny",
+                 "q8_gemm_fused", "q8_rmsnorm"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -244,6 +252,48 @@ def block_dots(wq, xq, out=None):
     _check("q8_block_dots", load_library().q8_block_dots(
         _ptr(wq), n, k, m, _ptr(xq), _ptr(isum), _stream()))
     return isum
+
+
+# ------------------------------------------------------------------ decode-step glue
+
+def gemm_fused(wq, wd, x, prologue: int, epilogue: int, out=None, rope_rows: int = 0, pos: int = 0):
+    """W8A16 product (m = x.shape[0] <= 8) with a fused prologue and epilogue.
+
+    prologue PRO_BF16: x bf16 [m][k]; PRO_F32 / PRO_RMSNORM: x fp32 [m][k].
+    epilogue EPI_F32: returns fp32 [m][n]; EPI_ADD: `out` (fp32 [m][n], required)
+    += the product; EPI_SWIGLU: bf16 [m][n/2]; EPI_ROPE: bf16 [m][n] (rows below
+    rope_rows rotated at position pos).  Row orders as in include/q8stream.h."""
+    wd, n, k = _weights(wq, wd)
+    if prologue == PRO_BF16:
+        x = _as_bits16(x)
+        _need(x, "x", torch.uint16, 2)
+    else:
+        _need(x, "x", torch.float32, 2)
+    m = x.shape[0]
+    if x.shape[1] != k:
+        raise ValueError(f"x must have {k} columns, got {x.shape[1]}")
+    if out is None:
+        if epilogue == EPI_ADD:
+            raise ValueError("EPI_ADD needs the residual buffer as `out`")
+        if epilogue == EPI_F32:
+            out = torch.empty((m, n), dtype=torch.float32, device=wq.device)
+        elif epilogue == EPI_SWIGLU:
+            out = torch.empty((m, n // 2), dtype=torch.uint16, device=wq.device)
+        else:
+            out = torch.empty((m, n), dtype=torch.uint16, device=wq.device)
+    _check("q8_gemm_fused", load_library().q8_gemm_fused(
+        _ptr(wq), _ptr(wd), n, k, m, int(prologue), _ptr(x), int(epilogue), _ptr(out),
+        int(rope_rows), int(pos), _stream()))
+    return out
+
+
+def rmsnorm(x, out=None):
+    """Weightless RMSNorm (eps 1e-6) of the fp32 rows of x; `out` may be x."""
+    _need(x, "x", torch.float32, 2)
+    m, k = x.shape
+    y = out if out is not None else torch.empty_like(x)
+    _check("q8_rmsnorm", load_library().q8_rmsnorm(_ptr(x), m, k, _ptr(y), _stream()))
+    return y
 
 
 # ------------------------------------------------------------------ int4 weights

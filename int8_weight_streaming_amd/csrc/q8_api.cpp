@@ -213,6 +213,39 @@ q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m, const
     return finish(q8::launch_block_dots(wq, n, k, (int)m, xq, isum, *dev, stream));
 }
 
+q8_status q8_gemm_fused(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int64_t m,
+                        int prologue, const void* x, int epilogue, void* out, int64_t rope_rows,
+                        int64_t pos, hipStream_t stream) {
+    if (prologue < Q8_PRO_BF16 || prologue > Q8_PRO_RMSNORM || epilogue < Q8_EPI_F32 ||
+        epilogue > Q8_EPI_ROPE || !q8::fused_combo_supported(prologue, epilogue))
+        return Q8_ERR_ENUM;
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(n, k));
+    if (m < 0 || m > Q8_MAX_BATCH) return Q8_ERR_BATCH;
+    if ((epilogue == Q8_EPI_SWIGLU || epilogue == Q8_EPI_ROPE) && n % 2 != 0) return Q8_ERR_SHAPE;
+    if (epilogue == Q8_EPI_ROPE &&
+        (rope_rows < 0 || rope_rows > n || rope_rows % 128 != 0 || pos < 0 || pos >= kMaxExtent))
+        return Q8_ERR_SHAPE;
+    if (n == 0 || m == 0) return Q8_OK;
+    if (!wq || !wd || !x || !out) return Q8_ERR_NULL;
+    if (!aligned16(wq) || !aligned16(wd) || !aligned16(x) || !aligned16(out)) return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_fused(wq, wd, n, k, (int)m, prologue, x, epilogue, out, rope_rows, pos, *dev,
+                                   stream));
+}
+
+q8_status q8_rmsnorm(const float* x, int64_t m, int64_t k, float* y, hipStream_t stream) {
+    if (k < 1 || k >= kMaxExtent || m < 0 || m >= kMaxExtent) return Q8_ERR_SHAPE;
+    if (m > 0 && m > kMaxElems / k) return Q8_ERR_SHAPE;
+    if (m == 0) return Q8_OK;
+    if (!x || !y) return Q8_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y)) return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_rmsnorm(x, m, k, y, stream));
+}
+
 q8_status q4_quantize_weights(const float* w, int64_t n, int64_t k, uint8_t* wq, uint16_t* wd,
                               hipStream_t stream) {
     Q8_TRY(check_k(k));

@@ -25,6 +25,14 @@ hipError_t launch_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_
 hipError_t launch_block_dots(const int8_t* wq, int64_t n, int64_t k, int m, const int8_t* xq,
                              int32_t* isum, const DeviceInfo& dev, hipStream_t stream);
 
+// W8A16 products with a fused prologue / epilogue (codes of q8_prologue and
+// q8_epilogue), and the standalone weightless RMSNorm.
+bool fused_combo_supported(int pro, int epi);
+hipError_t launch_fused(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int m, int pro,
+                        const void* x, int epi, void* out, int64_t rope_rows, int64_t pos,
+                        const DeviceInfo& dev, hipStream_t stream);
+hipError_t launch_rmsnorm(const float* x, int64_t m, int64_t k, float* y, hipStream_t stream);
+
 // int4 weights (two codes per byte, binary16 scale per 32-element block).
 hipError_t launch_q4_quantize(const float* w, int64_t nblocks, uint8_t* q, uint16_t* d,
                               const DeviceInfo& dev, hipStream_t stream);

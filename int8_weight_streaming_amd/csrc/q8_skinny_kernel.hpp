@@ -1,0 +1,381 @@
+// q8_skinny_kernel.hpp -- the batch 1..8 decode product kernel over Q8_0
+// weights, shared by the plain products (q8_skinny.hip) and the fused decode-step
+// products (q8_fused.hip).  The work layout is described in q8_skinny.hip.
+#pragma once
+
+#include "q8_device.hpp"
+#include "q8_internal.hpp"
+
+namespace q8 {
+
+// Fused prologues and epilogues: the glue of a decode step around the W8A16
+// products [Frigg README, "The model, as verified": RMSNorm without a learnable
+// weight (eps 1e-6) before every product that reads the residual stream, the
+// default rotary embedding (theta 10,000) on the query and key rows, SwiGLU
+// between the gate/up and down products, residual adds after the output and
+// down products].
+enum { kProBf16 = 0, kProF32 = 1, kProNorm = 2 };
+enum { kEpiF32 = 0, kEpiAdd = 1, kEpiSwiglu = 2, kEpiRope = 3 };
+constexpr float kRmsEps = 1e-6f;
+constexpr double kRopeTheta = 10000.0;
+constexpr int kRopeHead = 128;                 // head width of the rotated rows
+
+struct FuseArgs {
+    int64_t rope_rows;                         // rows [0, rope_rows) hold rotated heads
+    int64_t pos;                               // position of the token
+};
+
+__device__ __forceinline__ uint16_t to_bf16(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return (uint32_t)to_bf16(a) | ((uint32_t)to_bf16(b) << 16);
+}
+
+// Eight consecutive fp32 activations times `mul`, rounded to bf16 (nearest,
+// ties to even), as four packed pairs.
+__device__ __forceinline__ uint4 load_x8_f32(const float* p, float mul) {
+    const float4 f0 = reinterpret_cast<const float4*>(p)[0], f1 = reinterpret_cast<const float4*>(p)[1];
+    return make_uint4(pack_bf16(f0.x * mul, f0.y * mul), pack_bf16(f0.z * mul, f0.w * mul),
+                      pack_bf16(f1.x * mul, f1.y * mul), pack_bf16(f1.z * mul, f1.w * mul));
+}
+
+// Sixteen activations of one chunk as eight bf16 pairs: read as bf16, or
+// converted from fp32 (scaled by `mul`).
+template <int PRO>
+__device__ __forceinline__ void load_x16(const void* xv, int64_t off, float mul, uint32_t out[8]) {
+    uint4 a, b;
+    if constexpr (PRO == kProBf16) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + off);
+        a = p[0];
+        b = p[1];
+    } else {
+        const float* p = static_cast<const float*>(xv) + off;
+        a = load_x8_f32(p, mul);
+        b = load_x8_f32(p + 8, mul);
+    }
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+// Inverse RMS of each of the M fp32 rows of x [M][k]: 1 / sqrt(mean(x^2) + eps).
+// Every workgroup computes it for itself (a few KiB from L2) in a fixed order:
+// thread t sums elements t, t + 256, ... in order, a fixed DPP tree sums each
+// wave, and the four waves are added 0 + 1 + 2 + 3.  Must be reached by every
+// thread of the 256-thread workgroup.
+template <int M>
+__device__ __forceinline__ void row_inv_rms(const float* x, int64_t k, float inv[M]) {
+    __shared__ float red[4][M];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float ss[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) ss[m] = 0.0f;
+    for (int64_t i = threadIdx.x; i < k; i += 256)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float v = x[(int64_t)m * k + i];
+            ss[m] = fmaf(v, v, ss[m]);
+        }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        ss[m] = group_sum<64>(ss[m]);
+        if (lane == 0) red[wave][m] = ss[m];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float t = ((red[0][m] + red[1][m]) + red[2][m]) + red[3][m];
+        inv[m] = 1.0f / sqrtf(t / (float)k + kRmsEps);
+    }
+    __syncthreads();                           // red is free again
+}
+
+// Epilogue of one pair of rows (2p, 2p + 1) = (a, b) for activation row m.
+//  SwiGLU: the pair is (gate_j, up_j); out bf16 [m][n/2] gets silu(a) * b.
+//  RoPE:   rows below rope_rows hold heads of 128 in pair order (stored row
+//          2(64h + i) is dimension i of head h, the next one dimension i + 64);
+//          the pair turns by pos * theta^(-i/64) (angle and its sine and cosine
+//          in fp64) and lands at dimensions i and i + 64; rows at or above
+//          rope_rows are copied in place.  out bf16 [m][n].
+template <int EPI>
+__device__ __forceinline__ void paired_epilogue(float a, float b, int64_t row, int m, int64_t n,
+                                                const FuseArgs& fa, uint16_t* out) {
+    const int64_t p = row >> 1;
+    if constexpr (EPI == kEpiSwiglu) {
+        out[(int64_t)m * (n >> 1) + p] = to_bf16(a / (1.0f + expf(-a)) * b);
+    } else {
+        if (row < fa.rope_rows) {
+            const int64_t h = p / (kRopeHead / 2);
+            const int i = (int)(p % (kRopeHead / 2));
+            const double ang = (double)fa.pos * pow(kRopeTheta, -(double)i / (double)(kRopeHead / 2));
+            double sd, cd;
+            sincos(ang, &sd, &cd);
+            const float c = (float)cd, s = (float)sd;
+            uint16_t* o = out + (int64_t)m * n + h * kRopeHead + i;
+            o[0] = to_bf16(a * c - b * s);
+            o[kRopeHead / 2] = to_bf16(b * c + a * s);
+        } else {
+            out[(int64_t)m * n + row] = to_bf16(a);
+            out[(int64_t)m * n + row + 1] = to_bf16(b);
+        }
+    }
+}
+
+// Activations of one K tile: registers or LDS.
+template <int M, int ACT, int CPL>
+struct XRegs {
+    // bf16: 8 dwords per chunk; Q8: 4 dwords of codes per chunk + block scale.
+    uint32_t v[M][CPL][ACT == 0 ? 8 : 4];
+    float s[M][CPL];
+};
+
+// Activations in registers at batch 1-2 (bf16 or Q8 input); fp32 input
+// (fused prologues) holds twice the bytes per chunk, so above batch 1 it is
+// converted into LDS instead.
+template <int M, int ACT, int PRO = 0>
+constexpr bool x_in_registers() { return M <= 2 && (PRO == 0 || M == 1); }
+
+template <int M, int ACT, int G, int R, int CPL, int PRO = kProBf16, int EPI = kEpiF32>
+__global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ wq,
+                                                     const uint16_t* __restrict__ wd, int64_t n,
+                                                     int nb, const void* __restrict__ xv,
+                                                     const uint16_t* __restrict__ xdp,
+                                                     void* __restrict__ yv, FuseArgs fa) {
+    static_assert(PRO == kProBf16 || ACT == 0, "fp32 prologues take bf16-product weights");
+    static_assert(EPI < kEpiSwiglu || R == 2 || (R == 1 && G == 32),
+                  "paired epilogues need both rows of a pair in one wave");
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    constexpr int GPW = 64 / G;                  // lane groups per wave
+    constexpr int RPW = 4 * GPW * R;             // rows per workgroup
+    constexpr int TCH = G * CPL;                 // chunks per K tile
+    constexpr bool XREG = x_in_registers<M, ACT, PRO>();
+    constexpr int XCH_BYTES = ACT == 0 ? 32 : 16;   // activation bytes per chunk and row
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gl = lane & (G - 1), grp = lane / G;
+    const int nch = nb * 2;
+    const int64_t k = (int64_t)nb * 32;
+    const int64_t rbase = (int64_t)blockIdx.x * RPW + (int64_t)(wave * GPW + grp) * R;
+    float* y = static_cast<float*>(yv);
+
+    // Prologue: per activation row the factor its fp32 values are scaled by
+    // before rounding to bf16 (the inverse RMS for the norm prologue, else 1).
+    float xmul[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) xmul[m] = 1.0f;
+    if constexpr (PRO == kProNorm) row_inv_rms<M>(static_cast<const float*>(xv), k, xmul);
+
+    const int8_t* wrow[R];
+    const uint16_t* srow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = rbase + r < n ? rbase + r : n - 1;   // clamp: loads stay in bounds
+        wrow[r] = wq + row * k;
+        srow[r] = wd + row * nb;
+    }
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+    for (int c0 = 0; c0 < nch; c0 += TCH) {
+        // ---- activations held in registers: fetched first (small, cache
+        // resident), so their latency hides under the weight stream
+        XRegs<M, ACT, CPL> xr;
+        if (XREG) {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = c0 + gl + G * j;
+                const int cc = c < nch ? c : 0;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    if (ACT == 0) {
+                        load_x16<PRO>(xv, m * k + (int64_t)cc * 16, xmul[m], xr.v[m][j]);
+                    } else {
+                        const uint4 a = *reinterpret_cast<const uint4*>(
+                            static_cast<const int8_t*>(xv) + m * k + (int64_t)cc * 16);
+                        xr.v[m][j][0] = a.x; xr.v[m][j][1] = a.y; xr.v[m][j][2] = a.z; xr.v[m][j][3] = a.w;
+                        xr.s[m][j] = half_bits_to_float(xdp[(int64_t)m * nb + (cc >> 1)]);
+                    }
+                }
+            }
+        }
+        // ---- weights and their block scales (raw binary16, converted at use)
+        u32x4 w[CPL][R];
+        uint16_t sb[CPL][R];
+        bool okj[CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = c0 + gl + G * j;
+            okj[j] = c < nch;
+            const int cc = okj[j] ? c : 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                w[j][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + (int64_t)cc * 16));
+                sb[j][r] = srow[r][cc >> 1];
+            }
+        }
+        if (!XREG) {
+            // stage the tile in LDS while the weight loads are in flight:
+            // [m][chunk] with XCH_BYTES per chunk, then the Q8 scales
+            const int tch = nch - c0 < TCH ? nch - c0 : TCH;
+            __syncthreads();
+            const int pieces = M * tch * (XCH_BYTES / 16);
+            for (int i = threadIdx.x; i < pieces; i += 256) {
+                const int q = ACT == 0 ? (i & 1) : 0;
+                const int rest = ACT == 0 ? (i >> 1) : i;
+                const int ch = rest % tch, m = rest / tch;
+                uint4 piece;
+                if constexpr (PRO == kProBf16) {
+                    const unsigned char* src = static_cast<const unsigned char*>(xv) +
+                        ((int64_t)m * k + (int64_t)(c0 + ch) * 16) * (ACT == 0 ? 2 : 1) + q * 16;
+                    piece = *reinterpret_cast<const uint4*>(src);
+                } else {
+                    float mul = 1.0f;
+#pragma unroll
+                    for (int mm = 0; mm < M; ++mm) mul = mm == m ? xmul[mm] : mul;
+                    piece = load_x8_f32(static_cast<const float*>(xv) + (int64_t)m * k + (int64_t)(c0 + ch) * 16 + q * 8, mul);
+                }
+                *reinterpret_cast<uint4*>(lds + (m * TCH + ch) * XCH_BYTES + q * 16) = piece;
+            }
+            if (ACT == 1) {
+                float* sc = reinterpret_cast<float*>(lds + M * TCH * XCH_BYTES);
+                for (int i = threadIdx.x; i < M * (tch >> 1); i += 256) {
+                    const int bl = i % (tch >> 1), m = i / (tch >> 1);
+                    sc[m * (TCH / 2) + bl] = half_bits_to_float(xdp[(int64_t)m * nb + (c0 >> 1) + bl]);
+                }
+            }
+            __syncthreads();
+        }
+        // keep every load of the tile ahead of the arithmetic
+        __builtin_amdgcn_sched_barrier(0);
+        float ws[CPL][R];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int r = 0; r < R; ++r) ws[j][r] = okj[j] ? half_bits_to_float(sb[j][r]) : 0.0f;
+
+        // ---- compute
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int cl = gl + G * j;                    // chunk index inside the tile
+            const int clc = c0 + cl < nch ? cl : 0;       // LDS slot that exists
+            if (ACT == 0) {
+                uint32_t wbf[R][8];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    i8x4_to_bf16x4(w[j][r].x, wbf[r][0], wbf[r][1]);
+                    i8x4_to_bf16x4(w[j][r].y, wbf[r][2], wbf[r][3]);
+                    i8x4_to_bf16x4(w[j][r].z, wbf[r][4], wbf[r][5]);
+                    i8x4_to_bf16x4(w[j][r].w, wbf[r][6], wbf[r][7]);
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    uint32_t xc[8];
+                    if (XREG) {
+#pragma unroll
+                        for (int d = 0; d < 8; ++d) xc[d] = xr.v[m][j][d];
+                    } else {
+                        const uint4* xp = reinterpret_cast<const uint4*>(lds + (m * TCH + clc) * 32);
+                        const uint4 a = xp[0], b = xp[1];
+                        xc[0] = a.x; xc[1] = a.y; xc[2] = a.z; xc[3] = a.w;
+                        xc[4] = b.x; xc[5] = b.y; xc[6] = b.z; xc[7] = b.w;
+                    }
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            pa = dot2_bf16(wbf[r][d], xc[d], pa);
+                            pb = dot2_bf16(wbf[r][4 + d], xc[4 + d], pb);
+                        }
+                        acc[r][m] = fmaf(pa + pb, ws[j][r], acc[r][m]);
+                    }
+                }
+            } else {
+                const bool even = (gl & 1) == 0;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    uint32_t xc[4];
+                    float xs;
+                    if (XREG) {
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) xc[d] = xr.v[m][j][d];
+                        xs = xr.s[m][j];
+                    } else {
+                        const uint4 a = *reinterpret_cast<const uint4*>(lds + (m * TCH + clc) * 16);
+                        xc[0] = a.x; xc[1] = a.y; xc[2] = a.z; xc[3] = a.w;
+                        xs = reinterpret_cast<const float*>(lds + M * TCH * 16)[m * (TCH / 2) + (clc >> 1)];
+                    }
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        int s = 0;
+                        s = __builtin_amdgcn_sdot4((int)w[j][r].x, (int)xc[0], s, false);
+                        s = __builtin_amdgcn_sdot4((int)w[j][r].y, (int)xc[1], s, false);
+                        s = __builtin_amdgcn_sdot4((int)w[j][r].z, (int)xc[2], s, false);
+                        s = __builtin_amdgcn_sdot4((int)w[j][r].w, (int)xc[3], s, false);
+                        // exact int32 block sum: add the neighbouring lane's half
+                        s += __builtin_amdgcn_update_dpp(0, s, 0xB1, 0xF, 0xF, true);
+                        const float t = even ? ws[j][r] * xs : 0.0f;
+                        acc[r][m] = fmaf((float)s, t, acc[r][m]);
+                    }
+                }
+            }
+        }
+    }
+
+    // Combine the G partial sums of every (row, m); all lanes of the group end
+    // with the same value.
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = group_sum<G>(acc[r][m]);
+
+    if constexpr (EPI == kEpiF32 || EPI == kEpiAdd) {
+        // Lane g of the group stores value g (then g + G, ...): rows of one m
+        // land on consecutive lanes.
+        constexpr int NV = R * M;
+#pragma unroll
+        for (int base = 0; base < NV; base += G) {
+            const int idx = base + gl;
+            float out = 0.0f;
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (idx == m * R + r) out = acc[r][m];
+            if (idx < NV) {
+                const int m = idx / R, r = idx % R;
+                const int64_t row = rbase + r;
+                if (row < n) {
+                    if constexpr (EPI == kEpiAdd) y[(int64_t)m * n + row] += out;
+                    else y[(int64_t)m * n + row] = out;
+                }
+            }
+        }
+    } else {
+        // Paired rows (2p, 2p + 1): both values of every m, on every lane of the
+        // group that holds the even row; its lane m stores activation row m.
+        float pa[M], pb[M];
+        bool lead = true;
+        if constexpr (R == 2) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) { pa[m] = acc[0][m]; pb[m] = acc[1][m]; }
+        } else {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float other = __shfl_xor(acc[0][m], 32);
+                pa[m] = grp == 0 ? acc[0][m] : other;
+                pb[m] = grp == 0 ? other : acc[0][m];
+            }
+            lead = grp == 0;
+        }
+        if (lead && gl < M && rbase < n) {
+            float a = 0.0f, b = 0.0f;
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                if (m == gl) { a = pa[m]; b = pb[m]; }
+            paired_epilogue<EPI>(a, b, rbase, gl, n, fa, static_cast<uint16_t*>(yv));
+        }
+    }
+}
+
+}  // namespace q8

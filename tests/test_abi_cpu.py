@@ -139,6 +139,32 @@ def test_q4_validation(lib):
     assert g(None, None, 5, 64, 0, 1, None, B, None, None) == OK
 
 
+def test_fused_validation(lib):
+    f = lib.q8_gemm_fused
+    # (prologue, epilogue) pairs outside the supported set
+    assert f(A, B, 8, 64, 1, 0, A, 0, A, 0, 0, None) == ENUM      # BF16 + F32: the plain product
+    assert f(A, B, 8, 64, 1, 1, A, 3, A, 0, 0, None) == ENUM
+    assert f(A, B, 8, 64, 1, 3, A, 0, A, 0, 0, None) == ENUM
+    assert f(A, B, 8, 64, 1, 2, A, 4, A, 0, 0, None) == ENUM
+    assert f(A, B, 8, 40, 1, 2, A, 3, A, 0, 0, None) == SHAPE
+    assert f(A, B, 8, 64, 9, 2, A, 3, A, 0, 0, None) == BATCH
+    assert f(A, B, 7, 64, 1, 2, A, 2, A, 0, 0, None) == SHAPE     # odd n, paired epilogue
+    assert f(A, B, 256, 64, 1, 2, A, 3, A, 64, 0, None) == SHAPE  # rope_rows not a multiple of 128
+    assert f(A, B, 256, 64, 1, 2, A, 3, A, 384, 0, None) == SHAPE # rope_rows > n
+    assert f(A, B, 256, 64, 1, 2, A, 3, A, 128, -1, None) == SHAPE
+    assert f(A, B, 7, 64, 1, 1, A, 1, A, 0, 0, None) != SHAPE     # odd n is fine unpaired
+    assert f(None, B, 8, 64, 1, 2, A, 3, A, 0, 0, None) == NULL
+    assert f(A, B, 8, 64, 1, 2, A, 3, None, 0, 0, None) == NULL
+    assert f(A, B, 8, 64, 1, 2, MIS, 3, A, 0, 0, None) == ALIGN
+    assert f(None, None, 0, 64, 1, 2, None, 3, None, 0, 0, None) == OK
+    g = lib.q8_rmsnorm
+    assert g(A, 2, 0, B, None) == SHAPE
+    assert g(A, -1, 8, B, None) == SHAPE
+    assert g(None, 2, 8, B, None) == NULL
+    assert g(A, 2, 8, MIS, None) == ALIGN
+    assert g(None, 0, 8, None, None) == OK
+
+
 def test_valid_arguments_without_gpu_report_device(lib):
     """With valid arguments the call reaches the device check; with no usable
     gfx950 it refuses with Q8_ERR_DEVICE instead of launching anything."""

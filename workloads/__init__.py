@@ -142,6 +142,32 @@ def mimir_step_order():
     return seq
 
 
+# Row orders of the fused decode-step products (layout only: which stored row
+# holds which natural row; the weights themselves are not changed).
+
+def rope_pair_rows(rope_rows: int, n: int) -> np.ndarray:
+    """Stored row s -> natural row, for a matrix whose first rope_rows rows are
+    heads of 128 stored in pair order (dimension i of a head, then i + 64) and
+    whose remaining rows keep their order."""
+    assert rope_rows % 128 == 0 and rope_rows <= n
+    perm = np.arange(n, dtype=np.int64)
+    for h in range(rope_rows // 128):
+        for i in range(64):
+            perm[128 * h + 2 * i] = 128 * h + i
+            perm[128 * h + 2 * i + 1] = 128 * h + i + 64
+    return perm
+
+
+def swiglu_pair_rows(n: int) -> np.ndarray:
+    """Stored row s -> natural row, for a [gate; up] matrix of n rows stored
+    interleaved (gate j, up j)."""
+    assert n % 2 == 0
+    perm = np.empty(n, dtype=np.int64)
+    perm[0::2] = np.arange(n // 2)
+    perm[1::2] = np.arange(n // 2) + n // 2
+    return perm
+
+
 # The five workloads, by what they are.
 CONFIGS = {
     "gemv_1536x1536_b1": dict(n=1536, k=1536, m=1, w_seed=101, x_seed=102),
