@@ -177,6 +177,19 @@ q8_status q8_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd
 /* Workspace words q8_attn_decode needs for (heads, t); -1 when out of range. */
 int64_t q8_attn_work_words(int64_t heads, int64_t t);
 
+/* Decode attention that first appends the token's own key and value: knew and
+ * vnew are bf16 [heads][128] (the key already rotated); each 32-wide block is
+ * quantized with the q8_quantize_act rule and written into row t - 1 of the
+ * caches (kq, vq codes; kd, vd scales), then the attention of q8_attn_decode
+ * runs over rows [0, t) with those rows.  The launch that computes it writes
+ * row t - 1 and reads nothing else it writes.  Same arguments, workspace and
+ * errors as q8_attn_decode otherwise; knew and vnew must be non-NULL and
+ * 16-byte aligned (Q8_ERR_NULL / Q8_ERR_ALIGN). */
+q8_status q8_attn_decode_append(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_t* vq, uint16_t* vd,
+                                int64_t heads, int64_t t, int64_t t_cap, int64_t head_dim, float scale,
+                                const uint16_t* knew, const uint16_t* vnew, float* out, float* work,
+                                int64_t work_words, hipStream_t stream);
+
 /* ---- decode-step glue fused into the W8A16 products ---------------------------
  *
  * A decode block [Frigg README, "The model, as verified": pre-norm blocks,

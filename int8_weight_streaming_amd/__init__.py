@@ -45,7 +45,7 @@ EXPORTED = (
     "q8_abi_version", "q8_status_str", "q8_last_hip_error",
     "q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
     "q8_gemm_prefill", "q8_block_dots", "q8_attn_decode", "q8_attn_work_words",
-    "q4_quantize_weights", "q4_gemm_skinny", "q8_gemm_fused", "q8_rmsnorm",
+    "q4_quantize_weights", "q4_gemm_skinny", "q8_gemm_fused", "q8_rmsnorm", "q8_attn_decode_append",
 )
 PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words", "q8_probe_barrier",
                   "q8_probe_barrier_words")
@@ -94,6 +94,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q4_gemm_skinny.argtypes = [P, P, I64, I64, I64, I, P, P, P, P]
     L.q8_gemm_fused.argtypes = [P, P, I64, I64, I64, I, P, I, P, I64, I64, P]
     L.q8_rmsnorm.argtypes = [P, I64, I64, P, P]
+    L.q8_attn_decode_append.argtypes = [P, P, P, P, P, I64, I64, I64, I64, C.c_float, P, P, P, P, I64, P]
+    L.q8_attn_decode_append.restype = I
     for name in ("q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
                  "q8_gemm_prefill", "q8_block_dots", "q4_quantize_weights", "q4_gemm_skinny",
                  "q8_gemm_fused", "q8_rmsnorm"):
@@ -371,6 +373,34 @@ def attn_decode(q, kq, kd, vq, vd, t: int, scale: float, work=None, out=None):
     _check("q8_attn_decode", load_library().q8_attn_decode(
         _ptr(q), _ptr(kq), _ptr(kd), _ptr(vq), _ptr(vd), heads, int(t), t_cap, d, float(scale),
         _ptr(y), _ptr(work), words, _stream()))
+    return y
+
+
+def attn_decode_append(q, kq, kd, vq, vd, t: int, scale: float, knew, vnew, work=None, out=None):
+    """attn_decode after writing the Q8_0 quantization of the bf16 rows knew,
+    vnew ([heads][128]) into cache row t - 1."""
+    q, kd, vd, knew, vnew = (_as_bits16(a) for a in (q, kd, vd, knew, vnew))
+    _need(q, "q", torch.uint16, 2)
+    _need(knew, "knew", torch.uint16, 2)
+    _need(vnew, "vnew", torch.uint16, 2)
+    _need(kq, "kq", torch.int8, 3)
+    _need(vq, "vq", torch.int8, 3)
+    _need(kd, "kd", torch.uint16, 3)
+    _need(vd, "vd", torch.uint16, 3)
+    heads, t_cap, d = kq.shape
+    if tuple(q.shape) != (heads, d) or tuple(knew.shape) != (heads, d) or tuple(vnew.shape) != (heads, d):
+        raise ValueError("q, knew and vnew must be [heads][d]")
+    if tuple(vq.shape) != (heads, t_cap, d) or tuple(kd.shape) != (heads, t_cap, d // 32) or \
+            tuple(vd.shape) != tuple(kd.shape):
+        raise ValueError("cache shapes disagree")
+    need = attn_work_words(heads, t) if 1 <= t <= t_cap else 0
+    if work is None and need > 0:
+        work = torch.empty((need,), dtype=torch.float32, device=kq.device)
+    y = out if out is not None else torch.empty((heads, d), dtype=torch.float32, device=kq.device)
+    words = work.numel() if work is not None else 0
+    _check("q8_attn_decode_append", load_library().q8_attn_decode_append(
+        _ptr(q), _ptr(kq), _ptr(kd), _ptr(vq), _ptr(vd), heads, int(t), t_cap, d, float(scale),
+        _ptr(knew), _ptr(vnew), _ptr(y), _ptr(work), words, _stream()))
     return y
 
 

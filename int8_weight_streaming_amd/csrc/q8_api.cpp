@@ -297,7 +297,30 @@ q8_status q8_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd
         return Q8_ERR_ALIGN;
     const q8::DeviceInfo* dev = nullptr;
     Q8_TRY(device_for(stream, &dev));
-    return finish(q8::launch_attn_decode(q, kq, kd, vq, vd, heads, t, t_cap, scale, out, work,
+    // the cache is only read on this path (knew == NULL)
+    return finish(q8::launch_attn_decode(q, const_cast<int8_t*>(kq), const_cast<uint16_t*>(kd),
+                                         const_cast<int8_t*>(vq), const_cast<uint16_t*>(vd), heads, t,
+                                         t_cap, scale, out, work, nullptr, nullptr, *dev, stream));
+}
+
+q8_status q8_attn_decode_append(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_t* vq, uint16_t* vd,
+                                int64_t heads, int64_t t, int64_t t_cap, int64_t head_dim, float scale,
+                                const uint16_t* knew, const uint16_t* vnew, float* out, float* work,
+                                int64_t work_words, hipStream_t stream) {
+    if (head_dim != 128) return Q8_ERR_SHAPE;
+    if (heads < 0 || heads > kMaxAttnHeads || t < 1 || t > t_cap || t_cap > kMaxAttnRows)
+        return Q8_ERR_SHAPE;
+    if (!(scale == scale) || scale - scale != 0.0f) return Q8_ERR_SHAPE;
+    if (heads == 0) return Q8_OK;
+    const int64_t need = q8::attn_work_floats(heads, t);
+    if (work_words < need) return Q8_ERR_SHAPE;
+    if (!q || !kq || !kd || !vq || !vd || !knew || !vnew || !out || (need > 0 && !work)) return Q8_ERR_NULL;
+    if (!aligned16(q) || !aligned16(kq) || !aligned16(kd) || !aligned16(vq) || !aligned16(vd) ||
+        !aligned16(knew) || !aligned16(vnew) || !aligned16(out) || (need > 0 && !aligned16(work)))
+        return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_attn_decode(q, kq, kd, vq, vd, heads, t, t_cap, scale, out, work, knew, vnew,
                                          *dev, stream));
 }
 

@@ -39,14 +39,44 @@ int64_t attn_work_floats(int64_t heads, int64_t t) {
     return c > 1 ? heads * c * kAttnPart : 0;
 }
 
+// One 16-dimension segment of a new bf16 key or value row as Q8_0 codes: the
+// lane's 16 values and its neighbour's (the other half of the 32-wide block)
+// give the block maximum; scale and codes follow the activation quantizer's
+// rule.  Every lane of the wave must call it (it shuffles).
+__device__ __forceinline__ void quantize_segment(const uint16_t* src, u32x4& codes, uint16_t& sbits) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(src), b = *reinterpret_cast<const u32x4*>(src + 8);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        v[2 * e] = bf16_lo(w[e]);
+        v[2 * e + 1] = bf16_hi(w[e]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    sbits = block_scale_bits(amax);
+    const float s = half_bits_to_float(sbits);
+    uint32_t c[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        c[d] = ((uint32_t)block_code(v[4 * d], s) & 0xFFu) | (((uint32_t)block_code(v[4 * d + 1], s) & 0xFFu) << 8) |
+               (((uint32_t)block_code(v[4 * d + 2], s) & 0xFFu) << 16) |
+               ((uint32_t)block_code(v[4 * d + 3], s) << 24);
+    codes = u32x4{c[0], c[1], c[2], c[3]};
+}
+
 __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restrict__ q,
-                                                         const int8_t* __restrict__ kq,
-                                                         const uint16_t* __restrict__ kd,
-                                                         const int8_t* __restrict__ vq,
-                                                         const uint16_t* __restrict__ vd,
+                                                         int8_t* __restrict__ kq,
+                                                         uint16_t* __restrict__ kd,
+                                                         int8_t* __restrict__ vq,
+                                                         uint16_t* __restrict__ vd,
                                                          int64_t t, int64_t t_cap, float scale,
                                                          int nchunks, float* __restrict__ work,
-                                                         float* __restrict__ out) {
+                                                         float* __restrict__ out,
+                                                         const uint16_t* __restrict__ knew,
+                                                         const uint16_t* __restrict__ vnew) {
     __shared__ float red[4][kAttnD + 2];
     const int h = (int)(blockIdx.x / (unsigned)nchunks), c = (int)(blockIdx.x % (unsigned)nchunks);
     const int lane = threadIdx.x & 63;
@@ -71,6 +101,37 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
         ks[j] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rKs, row * 8 + 2 * (seg >> 1), 0, 0);
         vs[j] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rVs, row * 8 + 2 * (seg >> 1), 0, 0);
     }
+    // A new row t - 1 (knew / vnew given): the wave that covers it quantizes the
+    // bf16 key and value rows, writes them into the cache and uses them in
+    // place of what the cache held there.
+    if (knew != nullptr) {
+        const int rnew = (int)t - 1;
+        if (c == nchunks - 1 && wave == ((rnew & (kAttnChunk - 1)) >> 5)) {
+            u32x4 kc, vc;
+            uint16_t ksb, vsb;
+            quantize_segment(knew + (int64_t)h * kAttnD + 16 * seg, kc, ksb);
+            quantize_segment(vnew + (int64_t)h * kAttnD + 16 * seg, vc, vsb);
+            if (rsub == (rnew & 7)) {
+                const int jn = (rnew & 31) >> 3;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j == jn) {
+                        kv[j] = kc;
+                        vv[j] = vc;
+                        ks[j] = ksb;
+                        vs[j] = vsb;
+                    }
+                const int64_t crow = hrow + rnew;
+                *reinterpret_cast<u32x4*>(kq + crow * kAttnD + 16 * seg) = kc;
+                *reinterpret_cast<u32x4*>(vq + crow * kAttnD + 16 * seg) = vc;
+                if ((seg & 1) == 0) {
+                    kd[crow * (kAttnD / 32) + (seg >> 1)] = ksb;
+                    vd[crow * (kAttnD / 32) + (seg >> 1)] = vsb;
+                }
+            }
+        }
+    }
+
     // query segment: dimensions 16 seg .. 16 seg + 15 as eight bf16 pairs
     const u32x4* qp = reinterpret_cast<const u32x4*>(q + (int64_t)h * kAttnD + 16 * seg);
     const u32x4 qa = qp[0], qb = qp[1];
@@ -190,15 +251,15 @@ __global__ __launch_bounds__(kAttnD) void attn_combine_kernel(const float* __res
     out[(int64_t)h * kAttnD + d] = num / den;
 }
 
-hipError_t launch_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd,
-                              const int8_t* vq, const uint16_t* vd, int64_t heads, int64_t t,
-                              int64_t t_cap, float scale, float* out, float* work,
+hipError_t launch_attn_decode(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_t* vq, uint16_t* vd,
+                              int64_t heads, int64_t t, int64_t t_cap, float scale, float* out,
+                              float* work, const uint16_t* knew, const uint16_t* vnew,
                               const DeviceInfo& dev, hipStream_t stream) {
     (void)dev;
     const int nchunks = (int)attn_chunks(t);
     (void)hipGetLastError();
     attn_split_kernel<<<(unsigned)(heads * nchunks), 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale,
-                                                                       nchunks, work, out);
+                                                                       nchunks, work, out, knew, vnew);
     if (nchunks > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -54,9 +54,11 @@ hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
 // (0 when one chunk covers the context).
 int64_t attn_chunks(int64_t t);
 int64_t attn_work_floats(int64_t heads, int64_t t);
-hipError_t launch_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd,
-                              const int8_t* vq, const uint16_t* vd, int64_t heads, int64_t t,
-                              int64_t t_cap, float scale, float* out, float* work,
+// With knew / vnew (bf16 [heads][128]) the key and value rows t - 1 are first
+// quantized into the cache; NULL leaves the cache untouched.
+hipError_t launch_attn_decode(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_t* vq, uint16_t* vd,
+                              int64_t heads, int64_t t, int64_t t_cap, float scale, float* out,
+                              float* work, const uint16_t* knew, const uint16_t* vnew,
                               const DeviceInfo& dev, hipStream_t stream);
 
 }  // namespace q8

@@ -165,6 +165,26 @@ def test_fused_validation(lib):
     assert g(None, 0, 8, None, None) == OK
 
 
+def test_attn_append_validation(lib):
+    f = lib.q8_attn_decode_append
+    need = lib.q8_attn_work_words(2, 200)
+    base = [A, B, A, B, A, 2, 200, 256, 128, 0.088, A, B, A, B, need, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a8=64) == SHAPE                        # head_dim
+    assert call(a6=300) == SHAPE                       # t > t_cap
+    assert call(a6=0) == SHAPE
+    assert call(a10=None) == NULL                      # knew
+    assert call(a11=None) == NULL                      # vnew
+    assert call(a11=MIS) == ALIGN
+    assert call(a14=need - 1) == SHAPE
+    assert call(a5=0) == OK
+
+
 def test_valid_arguments_without_gpu_report_device(lib):
     """With valid arguments the call reaches the device check; with no usable
     gfx950 it refuses with Q8_ERR_DEVICE instead of launching anything."""

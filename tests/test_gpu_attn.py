@@ -145,6 +145,30 @@ def test_attn_one_workspace_across_context_lengths():
         assert torch.equal(y, q8.attn_decode(dq, dkq, dkd, dvq, dvd, t, SCALE))
 
 
+@pytest.mark.parametrize("t,t_cap", [(1, 16), (128, 256), (129, 256), (200, 200), (4096, 4096), (1500, 2048)])
+def test_attn_append_writes_row_and_attends(t, t_cap):
+    """The new key/value rows land in cache row t - 1 exactly as the activation
+    quantizer writes them, nothing else in the cache changes, and the output is
+    the attention over the updated cache."""
+    heads = 12
+    log(f"attn append t={t} t_cap={t_cap}")
+    q, kq, kd, vq, vd = cache(9700 + t, heads, t_cap, t_cap)
+    g = wl.rng(9701 + t)
+    knew = wl.f32_to_bf16_bits(g.standard_normal((heads, D)).astype(np.float32) * 2)
+    vnew = wl.f32_to_bf16_bits(g.standard_normal((heads, D)).astype(np.float32))
+    knew[0, :32] = 0                                   # a zero block
+    dq, dkq, dkd, dvq, dvd = (to_dev(a) for a in (q, kq, kd, vq, vd))
+    y = q8.attn_decode_append(dq, dkq, dkd, dvq, dvd, t, SCALE, to_dev(knew), to_dev(vnew))
+    torch.cuda.synchronize()
+    ck, cks = oracle.quantize_bf16(knew)
+    cv, cvs = oracle.quantize_bf16(vnew)
+    kq2, kd2, vq2, vd2 = kq.copy(), kd.copy(), vq.copy(), vd.copy()
+    kq2[:, t - 1], kd2[:, t - 1], vq2[:, t - 1], vd2[:, t - 1] = ck, cks, cv, cvs
+    assert np.array_equal(to_host(dkq), kq2) and np.array_equal(to_host(dkd), kd2)
+    assert np.array_equal(to_host(dvq), vq2) and np.array_equal(to_host(dvd), vd2)
+    assert_close(to_host(y), oracle.attn_decode(q, kq2, kd2, vq2, vd2, t, SCALE), f"append t={t}")
+
+
 def test_attn_rejects_bad_arguments():
     q, kq, kd, vq, vd = cache(9400, 2, 10, 16)
     dq, dkq, dkd, dvq, dvd = (to_dev(a) for a in (q, kq, kd, vq, vd))
