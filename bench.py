@@ -466,6 +466,31 @@ def bench_mimir_with_kv(q8, wl, dev, weights, slabs, t: int = 512, replays: int 
             "frac_hbm_roofline": (1e3 / ms) / (HBM_PEAK_GBPS * 1e9 / nbytes)}
 
 
+def bench_fused_step(q8, wl, dev, weights, t: int, replays: int = 10) -> dict:
+    """One batch-1 decode token of the whole block -- the glue fused into the
+    products (RMSNorm, RoPE, SwiGLU, residual adds), attention that appends the
+    token's key and value to its int8 cache, a final norm per module run, the
+    lm_head -- captured once into a graph and replayed (context t, one cache of
+    t rows per virtual layer).  Bytes per token = weights + KV read."""
+    import torch
+    from int8_weight_streaming_amd.decode_step import DecodeStep
+    order = [blk for blk, _ in wl.mimir_step_order()[:-1:4]]
+    module_ends = [v for v in range(len(order)) if v % 16 == 15]
+    core = {key: val for key, val in weights.items() if key != "lm_head"}
+    st = DecodeStep(core, weights["lm_head"], order, module_ends, t,
+                    wl.rope_pair_rows(2 * wl.HIDDEN, 3 * wl.HIDDEN), wl.swiglu_pair_rows(2 * wl.INTER))
+    st.h.copy_(to_dev(wl.bf16_bits_to_f32(wl.normal_act_bf16(9901, 1, wl.HIDDEN)), dev))
+    ms = time_graph(lambda: st.run(t), 1, reps=replays)
+    launches = len(order) * (5 + (1 if t > 128 else 0)) + len(module_ends) + 1
+    nbytes = mimir_step_bytes(wl, 1) + 128 * attn_bytes(t)
+    del st
+    torch.cuda.empty_cache()
+    return {"context": t, "ms_per_step": ms, "tok_per_s": 1e3 / ms, "launches_per_token": launches,
+            "bytes_per_step": nbytes, "GBps": nbytes / ms / 1e6,
+            "hbm_roofline_tok_per_s": HBM_PEAK_GBPS * 1e9 / nbytes,
+            "frac_hbm_roofline": (1e3 / ms) / (HBM_PEAK_GBPS * 1e9 / nbytes)}
+
+
 def bench_sync_probe(q8, dev) -> dict:
     """What one dependency edge of a decode step costs on this GPU: the
     per-launch cost of an empty kernel under graph replay, and one grid-wide
@@ -626,6 +651,9 @@ def main() -> int:
             log(f"mimir step with int8 KV at context {t}")
             extras[f"mimir_step_b1_kv{t}"] = bench_mimir_with_kv(q8, wl, dev, weights, slabs, t)
         del slabs
+        for t in (512, 4096):
+            log(f"fused decode step (glue in the products, KV append) at context {t}")
+            extras[f"fused_step_b1_ctx{t}"] = bench_fused_step(q8, wl, dev, weights, t)
         log("prefill P sweep")
         extras["prefill_p256"] = bench_prefill(q8, wl, dev, weights)
         del weights

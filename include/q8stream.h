@@ -233,7 +233,8 @@ q8_status q8_gemm_fused(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t
 
 /* Weightless RMSNorm of m fp32 rows of length k (the final norm of a module
  * run): y = x / sqrt(mean(x^2) + 1e-6), fp32, with the same reduction as the
- * RMSNORM prologue.  y may be x (in place).  1 <= k < 2^31, 0 <= m < 2^31. */
+ * RMSNORM prologue.  y may be x (in place).  k a multiple of 32 (the K of the
+ * products it feeds), 32 <= k < 2^31; 0 <= m < 2^31, m * k <= 2^46. */
 q8_status q8_rmsnorm(const float* x, int64_t m, int64_t k, float* y, hipStream_t stream);
 
 /* ---- int4 weights ----------------------------------------------------------

@@ -236,8 +236,8 @@ q8_status q8_gemm_fused(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t
 }
 
 q8_status q8_rmsnorm(const float* x, int64_t m, int64_t k, float* y, hipStream_t stream) {
-    if (k < 1 || k >= kMaxExtent || m < 0 || m >= kMaxExtent) return Q8_ERR_SHAPE;
-    if (m > 0 && m > kMaxElems / k) return Q8_ERR_SHAPE;
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(m, k));
     if (m == 0) return Q8_OK;
     if (!x || !y) return Q8_ERR_NULL;
     if (!aligned16(x) || !aligned16(y)) return Q8_ERR_ALIGN;

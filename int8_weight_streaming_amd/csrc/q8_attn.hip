@@ -39,32 +39,13 @@ int64_t attn_work_floats(int64_t heads, int64_t t) {
     return c > 1 ? heads * c * kAttnPart : 0;
 }
 
-// One 16-dimension segment of a new bf16 key or value row as Q8_0 codes: the
-// lane's 16 values and its neighbour's (the other half of the 32-wide block)
-// give the block maximum; scale and codes follow the activation quantizer's
-// rule.  Every lane of the wave must call it (it shuffles).
-__device__ __forceinline__ void quantize_segment(const uint16_t* src, u32x4& codes, uint16_t& sbits) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(src), b = *reinterpret_cast<const u32x4*>(src + 8);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    float v[16];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        v[2 * e] = bf16_lo(w[e]);
-        v[2 * e + 1] = bf16_hi(w[e]);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    sbits = block_scale_bits(amax);
-    const float s = half_bits_to_float(sbits);
-    uint32_t c[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-        c[d] = ((uint32_t)block_code(v[4 * d], s) & 0xFFu) | (((uint32_t)block_code(v[4 * d + 1], s) & 0xFFu) << 8) |
-               (((uint32_t)block_code(v[4 * d + 2], s) & 0xFFu) << 16) |
-               ((uint32_t)block_code(v[4 * d + 3], s) << 24);
-    codes = u32x4{c[0], c[1], c[2], c[3]};
+// Maximum over each group of 32 lanes (exact in any order).
+__device__ __forceinline__ float max32(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    return fmaxf(v, __shfl_xor(v, 16));
 }
 
 __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restrict__ q,
@@ -91,50 +72,67 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
     const auto rVs = range_rsrc(vd + hrow * (kAttnD / 32), t * (kAttnD / 32) * 2);
     const int row0 = c * kAttnChunk + wave * 32 + rsub;           // rows row0 + 8j
 
+    // query segment: dimensions 16 seg .. 16 seg + 15 as eight bf16 pairs
+    // (fetched first: small and cache resident)
+    const u32x4* qp = reinterpret_cast<const u32x4*>(q + (int64_t)h * kAttnD + 16 * seg);
+    const u32x4 qa = qp[0], qb = qp[1];
+
+    // A new row t - 1 (knew / vnew given) is appended by the workgroup of the
+    // last chunk: thread i quantizes value i of [key row | value row] of head h
+    // (its 32-value block is reduced over the 32 lanes that hold it; the
+    // activation quantizer's rule), the codes meet in LDS, and the lanes of the
+    // wave that covers row t - 1 write them into the cache and use them in place
+    // of what the cache held there.  The bf16 value is fetched before the cache.
+    const int rnew = (int)t - 1;
+    const bool append = knew != nullptr && c == nchunks - 1;          // whole workgroup
+    uint32_t nbits = 0;
+    if (append) {
+        const int i = threadIdx.x;
+        nbits = (i < kAttnD ? knew : vnew)[(int64_t)h * kAttnD + (i & (kAttnD - 1))];
+    }
+
     u32x4 kv[4], vv[4];
-    uint16_t ks[4], vs[4];
+    uint32_t ks[4], vs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int row = row0 + 8 * j;
         kv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, row * kAttnD + 16 * seg, 0, kLoadNT));
         vv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, row * kAttnD + 16 * seg, 0, kLoadNT));
-        ks[j] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rKs, row * 8 + 2 * (seg >> 1), 0, 0);
-        vs[j] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rVs, row * 8 + 2 * (seg >> 1), 0, 0);
+        ks[j] = __builtin_amdgcn_raw_buffer_load_b16(rKs, row * 8 + 2 * (seg >> 1), 0, 0);
+        vs[j] = __builtin_amdgcn_raw_buffer_load_b16(rVs, row * 8 + 2 * (seg >> 1), 0, 0);
     }
-    // A new row t - 1 (knew / vnew given): the wave that covers it quantizes the
-    // bf16 key and value rows, writes them into the cache and uses them in
-    // place of what the cache held there.
-    if (knew != nullptr) {
-        const int rnew = (int)t - 1;
-        if (c == nchunks - 1 && wave == ((rnew & (kAttnChunk - 1)) >> 5)) {
-            u32x4 kc, vc;
-            uint16_t ksb, vsb;
-            quantize_segment(knew + (int64_t)h * kAttnD + 16 * seg, kc, ksb);
-            quantize_segment(vnew + (int64_t)h * kAttnD + 16 * seg, vc, vsb);
-            if (rsub == (rnew & 7)) {
-                const int jn = (rnew & 31) >> 3;
+    if (append) {
+        __shared__ __attribute__((aligned(16))) int8_t ncode[2 * kAttnD];
+        __shared__ uint16_t nscale[2 * kAttnD / 32];
+        pin(nbits);
+        const float v = __uint_as_float(nbits << 16);
+        const uint16_t sb = block_scale_bits(max32(fabsf(v)));
+        ncode[threadIdx.x] = (int8_t)block_code(v, half_bits_to_float(sb));
+        if ((threadIdx.x & 31) == 0) nscale[threadIdx.x >> 5] = sb;
+        __syncthreads();
+        if (wave == ((rnew & (kAttnChunk - 1)) >> 5) && rsub == (rnew & 7)) {
+            const u32x4 kc = *reinterpret_cast<const u32x4*>(ncode + 16 * seg);
+            const u32x4 vc = *reinterpret_cast<const u32x4*>(ncode + kAttnD + 16 * seg);
+            const uint16_t ksb = nscale[seg >> 1], vsb = nscale[kAttnD / 32 + (seg >> 1)];
+            const int jn = (rnew & 31) >> 3;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (j == jn) {
-                        kv[j] = kc;
-                        vv[j] = vc;
-                        ks[j] = ksb;
-                        vs[j] = vsb;
-                    }
-                const int64_t crow = hrow + rnew;
-                *reinterpret_cast<u32x4*>(kq + crow * kAttnD + 16 * seg) = kc;
-                *reinterpret_cast<u32x4*>(vq + crow * kAttnD + 16 * seg) = vc;
-                if ((seg & 1) == 0) {
-                    kd[crow * (kAttnD / 32) + (seg >> 1)] = ksb;
-                    vd[crow * (kAttnD / 32) + (seg >> 1)] = vsb;
+            for (int j = 0; j < 4; ++j)
+                if (j == jn) {
+                    kv[j] = kc;
+                    vv[j] = vc;
+                    ks[j] = ksb;
+                    vs[j] = vsb;
                 }
+            const int64_t crow = hrow + rnew;
+            *reinterpret_cast<u32x4*>(kq + crow * kAttnD + 16 * seg) = kc;
+            *reinterpret_cast<u32x4*>(vq + crow * kAttnD + 16 * seg) = vc;
+            if ((seg & 1) == 0) {
+                kd[crow * (kAttnD / 32) + (seg >> 1)] = ksb;
+                vd[crow * (kAttnD / 32) + (seg >> 1)] = vsb;
             }
         }
     }
 
-    // query segment: dimensions 16 seg .. 16 seg + 15 as eight bf16 pairs
-    const u32x4* qp = reinterpret_cast<const u32x4*>(q + (int64_t)h * kAttnD + 16 * seg);
-    const u32x4 qa = qp[0], qb = qp[1];
     const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
 
     // ---- scores of the lane's four rows
@@ -152,7 +150,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
             pa = dot2_bf16(kb[e], qw[e], pa);
             pb = dot2_bf16(kb[4 + e], qw[4 + e], pb);
         }
-        float v = (pa + pb) * half_bits_to_float(ks[j]);
+        float v = (pa + pb) * half_bits_to_float((uint16_t)ks[j]);
         // sum over the row's eight lanes (xor 1, xor 2, half-row mirror)
         v += dpp_f<0xB1>(v);
         v += dpp_f<0x4E>(v);
@@ -178,7 +176,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
     for (int j = 0; j < 4; ++j) {
         const float p = expf(s[j] - m);                 // rows past t: exp(-inf) = 0
         l += p;
-        const float pv = p * half_bits_to_float(vs[j]);
+        const float pv = p * half_bits_to_float((uint16_t)vs[j]);
         const uint32_t w4[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

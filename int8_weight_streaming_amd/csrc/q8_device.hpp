@@ -37,10 +37,9 @@ __device__ __forceinline__ uint16_t block_scale_bits(float amax) {
 // [fak MODEL-BASELINE-RESULTS, ACT 4, "Correctness": math.Round semantics,
 // never add-0.5-and-truncate].  roundf() is half-away-from-zero.
 __device__ __forceinline__ int block_code(float v, float s) {
-    if (s == 0.0f) return 0;
-    float r = roundf(v / s);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
+    // branch-free: a zero scale's quotient (inf / NaN) is discarded by the select
+    const float r = fminf(fmaxf(roundf(v / s), -127.0f), 127.0f);
+    return s == 0.0f ? 0 : (int)r;
 }
 
 // ---------------------------------------------------------------- conversions
@@ -92,6 +91,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc32(const void* base,
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes > 0 ? bytes : 0,
                                              kRsrcWord3);
 }
+
+// Ties a value to this point of the program: nothing computed from it is moved
+// above, so a value fetched early stays in flight until here (work on it would
+// otherwise be hoisted next to its load, which then waits at once).
+template <typename T>
+__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
 
 // ---------------------------------------------------------------- reductions
 

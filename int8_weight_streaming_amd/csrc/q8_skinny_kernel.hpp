@@ -56,24 +56,17 @@ __device__ __forceinline__ void load_x16(const void* xv, int64_t off, float mul,
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
-// Inverse RMS of each of the M fp32 rows of x [M][k]: 1 / sqrt(mean(x^2) + eps).
-// Every workgroup computes it for itself (a few KiB from L2) in a fixed order:
-// thread t sums elements t, t + 256, ... in order, a fixed DPP tree sums each
-// wave, and the four waves are added 0 + 1 + 2 + 3.  Must be reached by every
-// thread of the 256-thread workgroup.
+// Inverse RMS of each of the M fp32 rows of x [M][k]: 1 / sqrt(mean(x^2) + eps),
+// summed in one fixed order: thread t of the 256 takes the eight-value groups
+// t, t + 256, ... of the row (values 8g .. 8g + 7) and sums their squares in
+// order (fmaf), a fixed DPP tree sums each wave, and the four waves are added
+// 0 + 1 + 2 + 3.  Every workgroup computes it for itself (a few KiB from L2).
+// rms_finish is the part after the per-thread sums; it must be reached by every
+// thread of the 256-thread workgroup, at most once per kernel.
 template <int M>
-__device__ __forceinline__ void row_inv_rms(const float* x, int64_t k, float inv[M]) {
+__device__ __forceinline__ void rms_finish(float ss[M], int64_t k, float inv[M]) {
     __shared__ float red[4][M];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float ss[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) ss[m] = 0.0f;
-    for (int64_t i = threadIdx.x; i < k; i += 256)
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float v = x[(int64_t)m * k + i];
-            ss[m] = fmaf(v, v, ss[m]);
-        }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         ss[m] = group_sum<64>(ss[m]);
@@ -85,19 +78,86 @@ __device__ __forceinline__ void row_inv_rms(const float* x, int64_t k, float inv
         const float t = ((red[0][m] + red[1][m]) + red[2][m]) + red[3][m];
         inv[m] = 1.0f / sqrtf(t / (float)k + kRmsEps);
     }
-    __syncthreads();                           // red is free again
 }
 
-// Epilogue of one pair of rows (2p, 2p + 1) = (a, b) for activation row m.
-//  SwiGLU: the pair is (gate_j, up_j); out bf16 [m][n/2] gets silu(a) * b.
-//  RoPE:   rows below rope_rows hold heads of 128 in pair order (stored row
-//          2(64h + i) is dimension i of head h, the next one dimension i + 64);
-//          the pair turns by pos * theta^(-i/64) (angle and its sine and cosine
-//          in fp64) and lands at dimensions i and i + 64; rows at or above
-//          rope_rows are copied in place.  out bf16 [m][n].
+__device__ __forceinline__ float sumsq8(const float4& a, const float4& b, float s) {
+    s = fmaf(a.x, a.x, s); s = fmaf(a.y, a.y, s); s = fmaf(a.z, a.z, s); s = fmaf(a.w, a.w, s);
+    s = fmaf(b.x, b.x, s); s = fmaf(b.y, b.y, s); s = fmaf(b.z, b.z, s); s = fmaf(b.w, b.w, s);
+    return s;
+}
+
+template <int M>
+__device__ __forceinline__ void row_inv_rms(const float* x, int64_t k, float inv[M]) {
+    float ss[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) ss[m] = 0.0f;
+    for (int64_t g = threadIdx.x; 8 * g < k; g += 256)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float4* p = reinterpret_cast<const float4*>(x + (int64_t)m * k + 8 * g);
+            ss[m] = sumsq8(p[0], p[1], ss[m]);
+        }
+    rms_finish<M>(ss, k, inv);
+}
+
+// Row staging of fp32 activations, rows of k <= kStageK: thread t holds values
+// 8t .. 8t + 7 of every row -- its one group of the norm's order above -- so
+// the same registers give the inverse RMS and, scaled and rounded to bf16, the
+// staged tile.  The loads are unconditional (clamped to the row).
+constexpr int kStageK = 256 * 8;
+template <int M>
+__device__ __forceinline__ void stage_load(const float* x, int64_t k, float4 v[M][2]) {
+    const int64_t g = 8 * (int64_t)threadIdx.x < k ? threadIdx.x : 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float4* p = reinterpret_cast<const float4*>(x + (int64_t)m * k + 8 * g);
+        v[m][0] = p[0];
+        v[m][1] = p[1];
+    }
+}
+
+// theta^(-i/64) = 10000^(-i/64), i = 0..63: the rotary frequencies of a
+// 128-wide head, to double precision.
+static __constant__ double kRopeInvFreq[kRopeHead / 2] = {
+    1.0, 0.8659643233600653, 0.7498942093324559, 0.6493816315762113,
+    0.5623413251903491, 0.4869675251658631, 0.4216965034285822, 0.3651741272548377,
+    0.31622776601683794, 0.27384196342643613, 0.23713737056616552, 0.2053525026457146,
+    0.1778279410038923, 0.1539926526059492, 0.1333521432163324, 0.11547819846894582,
+    0.1, 0.08659643233600653, 0.07498942093324558, 0.06493816315762113,
+    0.05623413251903491, 0.04869675251658631, 0.042169650342858224, 0.03651741272548377,
+    0.03162277660168379, 0.027384196342643614, 0.023713737056616554, 0.02053525026457146,
+    0.01778279410038923, 0.01539926526059492, 0.01333521432163324, 0.011547819846894581,
+    0.01, 0.008659643233600654, 0.007498942093324558, 0.006493816315762113,
+    0.005623413251903491, 0.004869675251658631, 0.004216965034285823, 0.003651741272548377,
+    0.0031622776601683794, 0.0027384196342643613, 0.0023713737056616554, 0.002053525026457146,
+    0.0017782794100389228, 0.001539926526059492, 0.001333521432163324, 0.0011547819846894581,
+    0.001, 0.0008659643233600654, 0.0007498942093324559, 0.0006493816315762113,
+    0.0005623413251903491, 0.0004869675251658631, 0.00042169650342858224, 0.0003651741272548377,
+    0.00031622776601683794, 0.0002738419634264361, 0.00023713737056616554, 0.0002053525026457146,
+    0.00017782794100389227, 0.0001539926526059492, 0.0001333521432163324, 0.00011547819846894582,
+};
+
+// Rotation of the pair that starts at stored row `row` (rows below rope_rows):
+// pair p = row / 2 is dimension i = p % 64 of its head, turned by
+// pos * theta^(-i/64).  rope_freq reads the frequency (issued first, so its
+// latency hides under the weight loads); rope_turn forms the angle and reduces
+// it modulo 2 pi in fp64 (|angle| < 2^31 rad keeps the reduced angle accurate
+// to ~1e-9 rad; the quotient estimate only has to be within one of the
+// nearest integer) and takes its sine and cosine in fp32.
+__device__ __forceinline__ double rope_freq(int64_t row, const FuseArgs& fa) {
+    return row < fa.rope_rows ? kRopeInvFreq[(row >> 1) % (kRopeHead / 2)] : 0.0;
+}
+__device__ __forceinline__ void rope_turn(double freq, const FuseArgs& fa, float& c, float& s) {
+    const double ang = (double)fa.pos * freq;
+    const double twopi_hi = 6.283185307179586, twopi_lo = 2.4492935982947064e-16;
+    const double kq = rint(ang * 0.15915494309189535);
+    const double red = fma(-kq, twopi_lo, fma(-kq, twopi_hi, ang));
+    sincosf((float)red, &s, &c);
+}
+
 template <int EPI>
 __device__ __forceinline__ void paired_epilogue(float a, float b, int64_t row, int m, int64_t n,
-                                                const FuseArgs& fa, uint16_t* out) {
+                                                const FuseArgs& fa, float c, float s, uint16_t* out) {
     const int64_t p = row >> 1;
     if constexpr (EPI == kEpiSwiglu) {
         out[(int64_t)m * (n >> 1) + p] = to_bf16(a / (1.0f + expf(-a)) * b);
@@ -105,10 +165,6 @@ __device__ __forceinline__ void paired_epilogue(float a, float b, int64_t row, i
         if (row < fa.rope_rows) {
             const int64_t h = p / (kRopeHead / 2);
             const int i = (int)(p % (kRopeHead / 2));
-            const double ang = (double)fa.pos * pow(kRopeTheta, -(double)i / (double)(kRopeHead / 2));
-            double sd, cd;
-            sincos(ang, &sd, &cd);
-            const float c = (float)cd, s = (float)sd;
             uint16_t* o = out + (int64_t)m * n + h * kRopeHead + i;
             o[0] = to_bf16(a * c - b * s);
             o[kRopeHead / 2] = to_bf16(b * c + a * s);
@@ -128,10 +184,9 @@ struct XRegs {
 };
 
 // Activations in registers at batch 1-2 (bf16 or Q8 input); fp32 input
-// (fused prologues) holds twice the bytes per chunk, so above batch 1 it is
-// converted into LDS instead.
+// (fused prologues) is converted once per workgroup into LDS instead.
 template <int M, int ACT, int PRO = 0>
-constexpr bool x_in_registers() { return M <= 2 && (PRO == 0 || M == 1); }
+constexpr bool x_in_registers() { return M <= 2 && PRO == 0; }
 
 template <int M, int ACT, int G, int R, int CPL, int PRO = kProBf16, int EPI = kEpiF32>
 __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ wq,
@@ -156,11 +211,32 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
     float* y = static_cast<float*>(yv);
 
     // Prologue: per activation row the factor its fp32 values are scaled by
-    // before rounding to bf16 (the inverse RMS for the norm prologue, else 1).
+    // before rounding to bf16 (the inverse RMS for the norm prologue, else 1);
+    // computed once the first tile's weight loads are in flight.
     float xmul[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) xmul[m] = 1.0f;
-    if constexpr (PRO == kProNorm) row_inv_rms<M>(static_cast<const float*>(xv), k, xmul);
+    // Residual-add epilogue: lane g of a group adds into output value g (see
+    // the store below); its old value is fetched now, under the weight stream.
+    float hres = 0.0f;
+    if constexpr (EPI == kEpiAdd) {
+        static_assert(R * M <= G, "one store per lane");
+        if (gl < R * M) {
+            const int64_t row = rbase + gl % R;
+            if (row < n) hres = y[(int64_t)(gl / R) * n + row];
+        }
+    }
+    // RoPE epilogue: the pair's rotation, computed under the first tile's loads.
+    float rc = 1.0f, rs = 0.0f;
+    double rfreq = 0.0;
+    if constexpr (EPI == kEpiRope) rfreq = rope_freq(rbase, fa);
+    // fp32 activations at batch 1-2 with the whole row in one tile: staged
+    // from registers fetched before anything else (rows read once per
+    // workgroup); otherwise per tile from memory, below.
+    constexpr bool RS = PRO != kProBf16 && M <= 2;
+    const bool rstage = RS && k <= kStageK && k <= (int64_t)TCH * 16;
+    float4 sv[RS ? M : 1][2];
+    if constexpr (RS) stage_load<M>(static_cast<const float*>(xv), k, sv);
 
     const int8_t* wrow[R];
     const uint16_t* srow[R];
@@ -213,7 +289,51 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
                 sb[j][r] = srow[r][cc >> 1];
             }
         }
-        if (!XREG) {
+        if constexpr (RS) {
+            // staged rows: wanted only now, after the weight loads are issued
+            if (rstage) {
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        pin(sv[m][h].x); pin(sv[m][h].y); pin(sv[m][h].z); pin(sv[m][h].w);
+                    }
+            }
+        }
+        if (c0 == 0) {
+            if constexpr (PRO == kProNorm) {
+                if (RS && rstage) {
+                    float ss[M];
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        ss[m] = 8 * (int64_t)threadIdx.x < k ? sumsq8(sv[m][0], sv[m][1], 0.0f) : 0.0f;
+                    rms_finish<M>(ss, k, xmul);
+                } else {
+                    row_inv_rms<M>(static_cast<const float*>(xv), k, xmul);
+                }
+            }
+            if constexpr (EPI == kEpiRope) {
+                if (rbase < fa.rope_rows) {
+                    pin(rfreq);
+                    rope_turn(rfreq, fa, rc, rs);
+                }
+            }
+        }
+        if (RS && rstage) {
+            // the one tile, from the staged rows: values 8t .. 8t + 7 of row m
+            // go to bytes 16t .. 16t + 15 of the row's slot
+            if (8 * (int64_t)threadIdx.x < k) {
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const float mul = xmul[m];
+                    const float4 f0 = sv[m][0], f1 = sv[m][1];
+                    *reinterpret_cast<uint4*>(lds + m * TCH * 32 + threadIdx.x * 16) =
+                        make_uint4(pack_bf16(f0.x * mul, f0.y * mul), pack_bf16(f0.z * mul, f0.w * mul),
+                                   pack_bf16(f1.x * mul, f1.y * mul), pack_bf16(f1.z * mul, f1.w * mul));
+                }
+            }
+            __syncthreads();
+        } else if (!XREG) {
             // stage the tile in LDS while the weight loads are in flight:
             // [m][chunk] with XCH_BYTES per chunk, then the Q8 scales
             const int tch = nch - c0 < TCH ? nch - c0 : TCH;
@@ -346,7 +466,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
                 const int m = idx / R, r = idx % R;
                 const int64_t row = rbase + r;
                 if (row < n) {
-                    if constexpr (EPI == kEpiAdd) y[(int64_t)m * n + row] += out;
+                    if constexpr (EPI == kEpiAdd) y[(int64_t)m * n + row] = hres + out;
                     else y[(int64_t)m * n + row] = out;
                 }
             }
@@ -373,7 +493,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
 #pragma unroll
             for (int m = 0; m < M; ++m)
                 if (m == gl) { a = pa[m]; b = pb[m]; }
-            paired_epilogue<EPI>(a, b, rbase, gl, n, fa, static_cast<uint16_t*>(yv));
+            paired_epilogue<EPI>(a, b, rbase, gl, n, fa, rc, rs, static_cast<uint16_t*>(yv));
         }
     }
 }

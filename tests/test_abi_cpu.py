@@ -159,10 +159,11 @@ def test_fused_validation(lib):
     assert f(None, None, 0, 64, 1, 2, None, 3, None, 0, 0, None) == OK
     g = lib.q8_rmsnorm
     assert g(A, 2, 0, B, None) == SHAPE
-    assert g(A, -1, 8, B, None) == SHAPE
-    assert g(None, 2, 8, B, None) == NULL
-    assert g(A, 2, 8, MIS, None) == ALIGN
-    assert g(None, 0, 8, None, None) == OK
+    assert g(A, 2, 48, B, None) == SHAPE                          # k not a multiple of 32
+    assert g(A, -1, 64, B, None) == SHAPE
+    assert g(None, 2, 64, B, None) == NULL
+    assert g(A, 2, 64, MIS, None) == ALIGN
+    assert g(None, 0, 64, None, None) == OK
 
 
 def test_attn_append_validation(lib):
