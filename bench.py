@@ -337,7 +337,9 @@ def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP) -> dict:
     [P, 4096] (block-0 weights), each product graph-replayed.  P = 256 is the
     configured workload (activations with the seeded special rows); the sweep
     over P also fits time = fixed + P * slope for the three products, the
-    pages' prefill measure."""
+    pages' prefill measure, and for the products with their activation side
+    (RMSNorm + quantizer fused for qkv and gate_up, the plain quantizer for
+    down)."""
     import torch
     cfg = wl.CONFIGS["prefill_p256"]
     gemms = []
@@ -367,22 +369,39 @@ def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP) -> dict:
             tot_us += us
             ops += o
             nbytes += prefill_bytes(n, k, P)
-        qus = 0.0
+        q_us = {}
         for kk, (x_, q, d) in xs.items():
-            qus += time_graph(lambda: q8.quantize_act(x_, out=(q, d)), 20) * 1e3
+            q_us[kk] = time_graph(lambda: q8.quantize_act(x_, out=(q, d)), 20) * 1e3
+        # the activation side of qkv / gate_up: RMSNorm of the fp32 residual
+        # rows, bf16, Q8_0 -- one fused launch, or norm then quantize
+        h_ = to_dev(wl.bf16_bits_to_f32(xa), dev)
+        _, hq, hd = xs[wl.HIDDEN]
+        fused_us = time_graph(lambda: q8.quantize_act_fused(h_, q8.PRO_RMSNORM, out=(hq, hd)), 20) * 1e3
+        nrm = torch.empty_like(h_)
+        chain_us = time_graph(lambda: (q8.rmsnorm(h_, out=nrm),
+                                       q8.quantize_act_fused(nrm, q8.PRO_F32, out=(hq, hd))), 20) * 1e3
         tops = ops / tot_us / 1e6
         per_p[P] = {"us_three_gemms": tot_us, "int_ops": ops, "TOPS": tops,
                     "frac_int8_peak": tops / INT8_PEAK_TOPS, "bytes": nbytes,
-                    "us_per_token": tot_us / P, "per_gemm": rows, "quantize_act_us": qus}
-        log(f"prefill P={P}: {tot_us:.1f} us, {tops:.0f} TOPS ({100 * tops / INT8_PEAK_TOPS:.1f}% of int8 peak)")
+                    "us_per_token": tot_us / P, "per_gemm": rows,
+                    "quantize_act_us": sum(q_us.values()),
+                    "rmsnorm_quantize_fused_us": fused_us, "rmsnorm_then_quantize_us": chain_us,
+                    # qkv and gate_up read normed residual rows (fused prologue),
+                    # down reads the bf16 SwiGLU rows (plain quantizer)
+                    "us_products_with_activation_side": tot_us + 2 * fused_us + q_us[wl.INTER]}
+        log(f"prefill P={P}: {tot_us:.1f} us, {tops:.0f} TOPS ({100 * tops / INT8_PEAK_TOPS:.1f}% of int8 peak); "
+            f"norm+quantize fused {fused_us:.1f} us vs {chain_us:.1f} us in two launches")
     ps = np.array(sorted(per_p), dtype=np.float64)
     ts = np.array([per_p[int(P)]["us_three_gemms"] for P in ps])
     big = ps >= 256
-    slope, fixed = np.polyfit(ps[big], ts[big], 1)
     out = dict(per_p[256])
     out["p_sweep"] = {str(P): v for P, v in per_p.items()}
-    out["fit_p_ge_256"] = {"fixed_us": float(fixed), "slope_us_per_token": float(slope),
-                           "slope_ms_per_token": float(slope) * 1e-3}
+    if big.sum() >= 2:
+        ta = np.array([per_p[int(P)]["us_products_with_activation_side"] for P in ps])
+        for key, tt in (("fit_p_ge_256", ts), ("fit_p_ge_256_with_activation_side", ta)):
+            slope, fixed = np.polyfit(ps[big], tt[big], 1)
+            out[key] = {"fixed_us": float(fixed), "slope_us_per_token": float(slope),
+                        "slope_ms_per_token": float(slope) * 1e-3}
     return out
 
 
@@ -666,14 +685,18 @@ def main() -> int:
         cpu = cpu_baseline(oracle, wl, oq, od, x_np)
 
     torch.cuda.synchronize()
+    # HBM traffic from the committed counter passes, only while every source
+    # the kernel is built from is unchanged since they were taken
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic_lm_head_gemv.json")
     if os.path.exists(tfile):
         try:
             import hashlib
             t = json.load(open(tfile))
-            src = open(os.path.join(ROOT, "int8_weight_streaming_amd", "csrc", "q8_skinny.hip"), "rb").read()
-            if t.get("source_sha256") == hashlib.sha256(src).hexdigest():
+            h = hashlib.sha256()
+            for rel in t["source_files"]:
+                h.update(open(os.path.join(ROOT, rel), "rb").read())
+            if t.get("source_sha256") == h.hexdigest():
                 traffic = t.get("bytes_per_launch")
         except Exception:
             traffic = None

@@ -237,6 +237,19 @@ q8_status q8_gemm_fused(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t
  * products it feeds), 32 <= k < 2^31; 0 <= m < 2^31, m * k <= 2^46. */
 q8_status q8_rmsnorm(const float* x, int64_t m, int64_t k, float* y, hipStream_t stream);
 
+/* The activation side of a Q8 x Q8 prefill product in one launch: the fp32
+ * rows x [m][k] go through the prologue -- Q8_PRO_F32: rounded to bf16;
+ * Q8_PRO_RMSNORM: scaled by 1 / sqrt(mean(x^2) + 1e-6) (the reduction of
+ * q8_rmsnorm) and rounded to bf16 -- and the bf16 rows are quantized exactly
+ * as q8_quantize_act would (xq int8 [m][k], xd binary16 [m][k/32]) [Frigg
+ * README, "The model, as verified": the norm before every product that reads
+ * the residual stream; fak MODEL-BASELINE-RESULTS, ACT 5 "What moved" item 3:
+ * the activation quantizer].  Bit-identical to q8_rmsnorm, bf16 rounding and
+ * q8_quantize_act in sequence.  Other prologues return Q8_ERR_ENUM; k and m as
+ * for q8_rmsnorm; outputs must not overlap x. */
+q8_status q8_quantize_act_fused(const float* x, int64_t m, int64_t k, int prologue, int8_t* xq,
+                                uint16_t* xd, hipStream_t stream);
+
 /* ---- int4 weights ----------------------------------------------------------
  *
  * The pages price and measure an "int4 core + int8 vocab" build (Frigg README:

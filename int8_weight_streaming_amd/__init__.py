@@ -46,6 +46,7 @@ EXPORTED = (
     "q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
     "q8_gemm_prefill", "q8_block_dots", "q8_attn_decode", "q8_attn_work_words",
     "q4_quantize_weights", "q4_gemm_skinny", "q8_gemm_fused", "q8_rmsnorm", "q8_attn_decode_append",
+    "q8_quantize_act_fused",
 )
 PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words", "q8_probe_barrier",
                   "q8_probe_barrier_words")
@@ -94,11 +95,12 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q4_gemm_skinny.argtypes = [P, P, I64, I64, I64, I, P, P, P, P]
     L.q8_gemm_fused.argtypes = [P, P, I64, I64, I64, I, P, I, P, I64, I64, P]
     L.q8_rmsnorm.argtypes = [P, I64, I64, P, P]
+    L.q8_quantize_act_fused.argtypes = [P, I64, I64, I, P, P, P]
     L.q8_attn_decode_append.argtypes = [P, P, P, P, P, I64, I64, I64, I64, C.c_float, P, P, P, P, I64, P]
     L.q8_attn_decode_append.restype = I
     for name in ("q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
                  "q8_gemm_prefill", "q8_block_dots", "q4_quantize_weights", "q4_gemm_skinny",
-                 "q8_gemm_fused", "q8_rmsnorm"):
+                 "q8_gemm_fused", "q8_rmsnorm", "q8_quantize_act_fused"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -296,6 +298,21 @@ def rmsnorm(x, out=None):
     y = out if out is not None else torch.empty_like(x)
     _check("q8_rmsnorm", load_library().q8_rmsnorm(_ptr(x), m, k, _ptr(y), _stream()))
     return y
+
+
+def quantize_act_fused(x, prologue, out=None):
+    """fp32 [m][k] -> prologue (PRO_F32: bf16 rounding; PRO_RMSNORM: weightless
+    RMSNorm, then bf16 rounding) -> Q8_0 (int8 [m][k], uint16 [m][k/32]), one launch."""
+    _need(x, "x", torch.float32, 2)
+    m, k = x.shape
+    if out is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+        xd = torch.empty((m, k // 32), dtype=torch.uint16, device=x.device)
+    else:
+        xq, xd = out
+    _check("q8_quantize_act_fused", load_library().q8_quantize_act_fused(
+        _ptr(x), m, k, int(prologue), _ptr(xq), _ptr(xd), _stream()))
+    return xq, xd
 
 
 # ------------------------------------------------------------------ int4 weights

@@ -106,4 +106,71 @@ hipError_t launch_rmsnorm(const float* x, int64_t m, int64_t k, float* y, hipStr
     return hipGetLastError();
 }
 
+// ------------------------------------------- prologue fused with the quantizer
+
+// The activation side of a Q8 x Q8 prefill product in one launch: each fp32
+// row is scaled (by its inverse RMS for the norm prologue -- the reduction of
+// q8_rmsnorm -- else by 1), rounded to bf16 and coded as Q8_0 blocks with the
+// activation quantizer's rule.  One workgroup per row; thread t takes the
+// eight-value groups t, t + 256, ... of the row, so a 32-value block is four
+// consecutive threads and its maximum is combined over the quad.  A row of
+// k <= 2048 is read once (the norm's registers are the values quantized).
+template <int PRO>
+__global__ __launch_bounds__(256) void act_prologue_quantize_kernel(const float* __restrict__ x, int64_t k,
+                                                                    int8_t* __restrict__ xq,
+                                                                    uint16_t* __restrict__ xd) {
+    const int64_t row = blockIdx.x;
+    const float* xr = x + row * k;
+    const bool one = k <= kStageK;                 // uniform: the row in registers
+    float4 sv[1][2];
+    stage_load<1>(xr, k, sv);
+    float mul = 1.0f;
+    if constexpr (PRO == kProNorm) {
+        if (one) {
+            float ss[1] = {8 * (int64_t)threadIdx.x < k ? sumsq8(sv[0][0], sv[0][1], 0.0f) : 0.0f};
+            rms_finish<1>(ss, k, &mul);
+        } else {
+            row_inv_rms<1>(xr, k, &mul);
+        }
+    }
+    // k is a multiple of 32: the four threads of a quad leave the loop together
+    for (int64_t g = threadIdx.x; 8 * g < k; g += 256) {
+        float4 a = sv[0][0], b = sv[0][1];
+        if (!one) {
+            const float4* p = reinterpret_cast<const float4*>(xr + 8 * g);
+            a = p[0];
+            b = p[1];
+        }
+        float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            v[e] = __uint_as_float((uint32_t)to_bf16(v[e] * mul) << 16);
+            amax = fmaxf(amax, fabsf(v[e]));
+        }
+        amax = fmaxf(amax, dpp_f<0xB1>(amax));     // quad_perm [1,0,3,2]
+        amax = fmaxf(amax, dpp_f<0x4E>(amax));     // quad_perm [2,3,0,1]
+        const uint16_t sb = block_scale_bits(amax);
+        const float s = half_bits_to_float(sb);
+        uint32_t c[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            c[h] = ((uint32_t)block_code(v[4 * h], s) & 0xFFu) | (((uint32_t)block_code(v[4 * h + 1], s) & 0xFFu) << 8) |
+                   (((uint32_t)block_code(v[4 * h + 2], s) & 0xFFu) << 16) |
+                   ((uint32_t)block_code(v[4 * h + 3], s) << 24);
+        *reinterpret_cast<uint2*>(xq + row * k + 8 * g) = make_uint2(c[0], c[1]);
+        if ((threadIdx.x & 3) == 0) xd[row * (k / 32) + g / 4] = sb;
+    }
+}
+
+hipError_t launch_act_prologue_quantize(const float* x, int64_t m, int64_t k, int pro, int8_t* xq,
+                                        uint16_t* xd, hipStream_t stream) {
+    (void)hipGetLastError();
+    if (pro == kProNorm)
+        act_prologue_quantize_kernel<kProNorm><<<(unsigned)m, 256, 0, stream>>>(x, k, xq, xd);
+    else
+        act_prologue_quantize_kernel<kProF32><<<(unsigned)m, 256, 0, stream>>>(x, k, xq, xd);
+    return hipGetLastError();
+}
+
 }  // namespace q8

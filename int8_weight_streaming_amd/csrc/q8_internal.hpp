@@ -32,6 +32,8 @@ hipError_t launch_fused(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t
                         const void* x, int epi, void* out, int64_t rope_rows, int64_t pos,
                         const DeviceInfo& dev, hipStream_t stream);
 hipError_t launch_rmsnorm(const float* x, int64_t m, int64_t k, float* y, hipStream_t stream);
+hipError_t launch_act_prologue_quantize(const float* x, int64_t m, int64_t k, int pro, int8_t* xq,
+                                        uint16_t* xd, hipStream_t stream);
 
 // int4 weights (two codes per byte, binary16 scale per 32-element block).
 hipError_t launch_q4_quantize(const float* w, int64_t nblocks, uint8_t* q, uint16_t* d,

@@ -164,6 +164,14 @@ def test_fused_validation(lib):
     assert g(None, 2, 64, B, None) == NULL
     assert g(A, 2, 64, MIS, None) == ALIGN
     assert g(None, 0, 64, None, None) == OK
+    qf = lib.q8_quantize_act_fused
+    assert qf(A, 2, 64, 0, A, B, None) == ENUM                     # bf16 prologue: q8_quantize_act
+    assert qf(A, 2, 64, 7, A, B, None) == ENUM
+    assert qf(A, 2, 48, 2, A, B, None) == SHAPE
+    assert qf(A, -1, 64, 1, A, B, None) == SHAPE
+    assert qf(A, 2, 64, 2, None, B, None) == NULL
+    assert qf(A, 2, 64, 1, A, MIS, None) == ALIGN
+    assert qf(None, 0, 64, 2, None, None, None) == OK
 
 
 def test_attn_append_validation(lib):

@@ -165,6 +165,34 @@ def test_rope_epilogue(n, rope_rows, k, m, pos):
     assert_bf16_rounding_of(out, want, tol, f"rope n={n} m={m} pos={pos}")
 
 
+@pytest.mark.parametrize("m,k", [(1, 1536), (256, 1536), (64, 4096), (7, 96), (3, 2048), (5, 2080), (0, 1536)])
+def test_quantize_act_fused(m, k):
+    """The prologue fused with the activation quantizer: codes and scales
+    bit-exact against the oracle's quantizer applied to the bf16 rows the
+    prologue defines (F32: the seeded prefill activations with their special
+    rows; RMSNORM: q8_rmsnorm's rows rounded to bf16), and against the
+    two-launch chain on the GPU."""
+    log(f"quantize_act_fused m={m} k={k}")
+    xb = wl.prefill_act_bf16(800 + m + k, m, k)
+    x = wl.bf16_bits_to_f32(xb)
+    if m > 1:
+        x[m - 1] = 0.0                                   # a zero row: zero blocks, scale 0
+    dx = to_dev(x)
+    xq, xd = q8.quantize_act_fused(dx, q8.PRO_F32)
+    oq, od = oracle.quantize_bf16(wl.f32_to_bf16_bits(x))
+    assert np.array_equal(to_host(xq), oq) and np.array_equal(to_host(xd), od), "F32 prologue"
+    h = _resid(801 + m, m, k)
+    if m > 1:
+        h[0] = 0.0
+    dh = to_dev(h)
+    xq, xd = q8.quantize_act_fused(dh, q8.PRO_RMSNORM)
+    xb = _gpu_norm_bf16(dh)
+    oq, od = oracle.quantize_bf16(xb)
+    assert np.array_equal(to_host(xq), oq) and np.array_equal(to_host(xd), od), "RMSNORM prologue"
+    cq, cd = q8.quantize_act_fused(q8.rmsnorm(dh), q8.PRO_F32)
+    assert torch.equal(cq, xq) and torch.equal(cd, xd), "two-launch chain"
+
+
 def test_fused_repeat_and_graph_replay_bitwise():
     n, k = 4608, 1536
     perm = wl.rope_pair_rows(3072, n)
