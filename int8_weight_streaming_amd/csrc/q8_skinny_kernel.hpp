@@ -140,19 +140,27 @@ static __constant__ double kRopeInvFreq[kRopeHead / 2] = {
 // Rotation of the pair that starts at stored row `row` (rows below rope_rows):
 // pair p = row / 2 is dimension i = p % 64 of its head, turned by
 // pos * theta^(-i/64).  rope_freq reads the frequency (issued first, so its
-// latency hides under the weight loads); rope_turn forms the angle and reduces
-// it modulo 2 pi in fp64 (|angle| < 2^31 rad keeps the reduced angle accurate
-// to ~1e-9 rad; the quotient estimate only has to be within one of the
-// nearest integer) and takes its sine and cosine in fp32.
+// latency hides under the weight loads).  rope_turn forms the angle in fp64 and
+// reduces it to r in [-pi/4, pi/4] with a quadrant q (angle = q pi/2 + r; pi/2
+// in two parts, so for positions below 2^24 r is accurate to ~1e-9 rad), then
+// takes sin r and cos r from their Taylor series to r^9 and r^10 (truncation
+// error below 2e-9 on that interval) in fp32, branch-free.
 __device__ __forceinline__ double rope_freq(int64_t row, const FuseArgs& fa) {
     return row < fa.rope_rows ? kRopeInvFreq[(row >> 1) % (kRopeHead / 2)] : 0.0;
 }
 __device__ __forceinline__ void rope_turn(double freq, const FuseArgs& fa, float& c, float& s) {
     const double ang = (double)fa.pos * freq;
-    const double twopi_hi = 6.283185307179586, twopi_lo = 2.4492935982947064e-16;
-    const double kq = rint(ang * 0.15915494309189535);
-    const double red = fma(-kq, twopi_lo, fma(-kq, twopi_hi, ang));
-    sincosf((float)red, &s, &c);
+    const double q = rint(ang * 0.63661977236758134);             // 2 / pi
+    const double pio2_hi = 1.5707963267948966, pio2_lo = 6.123233995736766e-17;
+    const float r = (float)fma(-q, pio2_lo, fma(-q, pio2_hi, ang));
+    const float r2 = r * r;
+    const float sn = r * (1.0f + r2 * (-1.0f / 6 + r2 * (1.0f / 120 + r2 * (-1.0f / 5040 + r2 * (1.0f / 362880)))));
+    const float cs = 1.0f + r2 * (-0.5f + r2 * (1.0f / 24 + r2 * (-1.0f / 720 + r2 * (1.0f / 40320 +
+                                                                                       r2 * (-1.0f / 3628800)))));
+    const int qi = (int)((int64_t)q & 3);
+    // cos and sin of q pi/2 + r
+    c = qi == 0 ? cs : qi == 1 ? -sn : qi == 2 ? -cs : sn;
+    s = qi == 0 ? sn : qi == 1 ? cs : qi == 2 ? -sn : -cs;
 }
 
 template <int EPI>
@@ -226,7 +234,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
             if (row < n) hres = y[(int64_t)(gl / R) * n + row];
         }
     }
-    // RoPE epilogue: the pair's rotation, computed under the first tile's loads.
+    // RoPE epilogue: the pair's rotation, computed once the first tile's loads
+    // are issued.
     float rc = 1.0f, rs = 0.0f;
     double rfreq = 0.0;
     if constexpr (EPI == kEpiRope) rfreq = rope_freq(rbase, fa);
@@ -289,6 +298,13 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
                 sb[j][r] = srow[r][cc >> 1];
             }
         }
+        if constexpr (EPI == kEpiRope) {
+            // the pair's rotation first: its math overlaps the wait for the rows
+            if (c0 == 0 && rbase < fa.rope_rows) {
+                pin(rfreq);
+                rope_turn(rfreq, fa, rc, rs);
+            }
+        }
         if constexpr (RS) {
             // staged rows: wanted only now, after the weight loads are issued
             if (rstage) {
@@ -310,12 +326,6 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
                     rms_finish<M>(ss, k, xmul);
                 } else {
                     row_inv_rms<M>(static_cast<const float*>(xv), k, xmul);
-                }
-            }
-            if constexpr (EPI == kEpiRope) {
-                if (rbase < fa.rope_rows) {
-                    pin(rfreq);
-                    rope_turn(rfreq, fa, rc, rs);
                 }
             }
         }
