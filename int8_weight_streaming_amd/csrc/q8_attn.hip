@@ -219,34 +219,94 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
     }
 }
 
-// One workgroup per head, thread d: combine the chunks.  The chunk maxima,
-// denominators and numerators are independent loads, issued eight chunks at a
-// time so their latencies overlap; every sum runs in chunk order.
+// One workgroup per head, thread d: combine the chunks,
+//   out = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M),  M = max_c m_c,
+// every sum in chunk order.  Chunks are taken B at a time (4, 8, 16 or 32,
+// the smallest that holds them; 32 per batch above that) with all loads of a
+// batch in flight together: lane u (mod B) of each wave fetches
+// chunk u's maximum and denominator and readlane hands them to every lane
+// (uniform addresses would become scalar loads, of which few can be in
+// flight); each thread fetches its own numerators.  Up to 32 chunks (4096
+// rows) that is one round trip; longer contexts take the maximum over the
+// batches first, then the sums.
+constexpr int kCombBatch = 32;
+
+template <int B>
+struct CombBatch {
+    float m[B], l[B], o[B];
+};
+
+template <int B>
+__device__ __forceinline__ void load_batch(const float* w, int c0, int nchunks, int d, CombBatch<B>& b) {
+    const int cu = c0 + (d & (B - 1)) < nchunks ? c0 + (d & (B - 1)) : nchunks - 1;   // in bounds; weight 0 below
+    // (m, l) adjacent: one 8-byte load (kAttnPart is even, so it is aligned)
+    const float2 ml = *reinterpret_cast<const float2*>(w + cu * kAttnPart + kAttnD);
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        const int cc = c0 + u < nchunks ? c0 + u : nchunks - 1;
+        b.o[u] = w[cc * kAttnPart + d];
+    }
+    __builtin_amdgcn_sched_barrier(0);        // every load of the batch before any use
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        b.m[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.x), u));
+        b.l[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.y), u));
+    }
+}
+
+template <int B>
+__device__ __forceinline__ void sum_batch(const CombBatch<B>& b, int c0, int nchunks, float mx, float& num,
+                                          float& den) {
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        if (c0 + u < nchunks) {                 // uniform
+            const float e = expf(b.m[u] - mx);
+            num = fmaf(b.o[u], e, num);
+            den = fmaf(b.l[u], e, den);
+        }
+    }
+}
+
+// nchunks <= B: one batch, one round trip
+template <int B>
+__device__ __forceinline__ float combine_one(const float* w, int nchunks, int d) {
+    CombBatch<B> b;
+    load_batch<B>(w, 0, nchunks, d, b);
+    float mx = -INFINITY, num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int u = 0; u < B; ++u) mx = fmaxf(mx, b.m[u]);       // repeats of the last chunk change nothing
+    sum_batch<B>(b, 0, nchunks, mx, num, den);
+    return num / den;
+}
+
 __global__ __launch_bounds__(kAttnD) void attn_combine_kernel(const float* __restrict__ work,
                                                               int nchunks, float* __restrict__ out) {
     const int h = blockIdx.x, d = threadIdx.x;
     const float* w = work + (int64_t)h * nchunks * kAttnPart;
-    float mx = -INFINITY;
-#pragma unroll 8
-    for (int c = 0; c < nchunks; ++c) mx = fmaxf(mx, w[c * kAttnPart + kAttnD]);
-    float num = 0.0f, den = 0.0f;
-    for (int c = 0; c < nchunks; c += 8) {
-        float m8[8], l8[8], o8[8];
+    float r;
+    if (nchunks <= 4) {
+        r = combine_one<4>(w, nchunks, d);
+    } else if (nchunks <= 8) {
+        r = combine_one<8>(w, nchunks, d);
+    } else if (nchunks <= 16) {
+        r = combine_one<16>(w, nchunks, d);
+    } else if (nchunks <= kCombBatch) {
+        r = combine_one<kCombBatch>(w, nchunks, d);
+    } else {
+        CombBatch<kCombBatch> b;
+        float mx = -INFINITY, num = 0.0f, den = 0.0f;
+        for (int c0 = 0; c0 < nchunks; c0 += kCombBatch) {
+            load_batch<kCombBatch>(w, c0, nchunks, d, b);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int cc = c + u < nchunks ? c + u : c;          // in bounds; weight 0 below
-            m8[u] = w[cc * kAttnPart + kAttnD];
-            l8[u] = w[cc * kAttnPart + kAttnD + 1];
-            o8[u] = w[cc * kAttnPart + d];
+            for (int u = 0; u < kCombBatch; ++u) mx = fmaxf(mx, b.m[u]);
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float e = c + u < nchunks ? expf(m8[u] - mx) : 0.0f;
-            num = fmaf(o8[u], e, num);
-            den = fmaf(l8[u], e, den);
+        for (int c0 = 0; c0 < nchunks; c0 += kCombBatch) {
+            load_batch<kCombBatch>(w, c0, nchunks, d, b);
+            sum_batch<kCombBatch>(b, c0, nchunks, mx, num, den);
         }
+        r = num / den;
     }
-    out[(int64_t)h * kAttnD + d] = num / den;
+    out[(int64_t)h * kAttnD + d] = r;
 }
 
 hipError_t launch_attn_decode(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_t* vq, uint16_t* vd,
