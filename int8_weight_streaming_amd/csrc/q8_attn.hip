@@ -12,10 +12,12 @@
 // (an int8 KV read per decoded token)].
 //
 // The cache read is the cost (2 x 136 bytes per row and head), so the kernel
-// streams it once: a workgroup takes 128 rows of one head; each of its four
-// waves 32 rows, lane l the 16-byte segment l % 8 (dimensions 16 (l % 8) ..
-// + 15, inside one Q8 block) of rows 8j + l / 8, j < 4, for K and V alike, all
-// loads issued before the first use.  A score is the bf16 dot of the query
+// streams it once: a workgroup takes a chunk of 128 rows of one head (256
+// above 2048 rows of context: fewer, fuller workgroups and fewer partials to
+// combine measured faster there, slower below); each of its four waves a
+// quarter, lane l the 16-byte segment l % 8 (dimensions 16 (l % 8) .. + 15,
+// inside one Q8 block) of rows 8j + l / 8, j < RPL = 4 or 8, for K and V
+// alike, all loads issued before the first use.  A score is the bf16 dot of the query
 // segment with the exactly converted codes, times the block scale, summed over
 // the row's eight lanes by a fixed DPP tree.  The workgroup subtracts its
 // maximum score, and writes (sum_j e^(s_j - m) V_j, m, sum_j e^(s_j - m)) to a
@@ -30,7 +32,8 @@
 namespace q8 {
 
 constexpr int kAttnD = 128;                    // head dimension
-constexpr int kAttnChunk = 128;                // cache rows per workgroup
+constexpr int kAttnChunk = 128;                // cache rows per workgroup (four rows per lane)
+constexpr int64_t kAttnWideFrom = 2048;        // longer contexts: 256-row chunks (eight rows per lane)
 constexpr int kAttnPart = kAttnD + 2;          // floats per (head, chunk): o[128], m, l
 
 int64_t attn_chunks(int64_t t) { return (t + kAttnChunk - 1) / kAttnChunk; }
@@ -48,6 +51,7 @@ __device__ __forceinline__ float max32(float v) {
     return fmaxf(v, __shfl_xor(v, 16));
 }
 
+template <int RPL>
 __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restrict__ q,
                                                          int8_t* __restrict__ kq,
                                                          uint16_t* __restrict__ kd,
@@ -70,7 +74,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
     const auto rV = range_rsrc(vq + hrow * kAttnD, t * kAttnD);
     const auto rKs = range_rsrc(kd + hrow * (kAttnD / 32), t * (kAttnD / 32) * 2);
     const auto rVs = range_rsrc(vd + hrow * (kAttnD / 32), t * (kAttnD / 32) * 2);
-    const int row0 = c * kAttnChunk + wave * 32 + rsub;           // rows row0 + 8j
+    constexpr int WROWS = 8 * RPL;                                // rows per wave
+    const int row0 = c * (4 * WROWS) + wave * WROWS + rsub;       // rows row0 + 8j, j < RPL
 
     // query segment: dimensions 16 seg .. 16 seg + 15 as eight bf16 pairs
     // (fetched first: small and cache resident)
@@ -91,10 +96,10 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
         nbits = (i < kAttnD ? knew : vnew)[(int64_t)h * kAttnD + (i & (kAttnD - 1))];
     }
 
-    u32x4 kv[4], vv[4];
-    uint32_t ks[4], vs[4];
+    u32x4 kv[RPL], vv[RPL];
+    uint32_t ks[RPL], vs[RPL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < RPL; ++j) {
         const int row = row0 + 8 * j;
         kv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, row * kAttnD + 16 * seg, 0, kLoadNT));
         vv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, row * kAttnD + 16 * seg, 0, kLoadNT));
@@ -110,13 +115,13 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
         ncode[threadIdx.x] = (int8_t)block_code(v, half_bits_to_float(sb));
         if ((threadIdx.x & 31) == 0) nscale[threadIdx.x >> 5] = sb;
         __syncthreads();
-        if (wave == ((rnew & (kAttnChunk - 1)) >> 5) && rsub == (rnew & 7)) {
+        if (wave == (rnew % (4 * WROWS)) / WROWS && rsub == (rnew & 7)) {
             const u32x4 kc = *reinterpret_cast<const u32x4*>(ncode + 16 * seg);
             const u32x4 vc = *reinterpret_cast<const u32x4*>(ncode + kAttnD + 16 * seg);
             const uint16_t ksb = nscale[seg >> 1], vsb = nscale[kAttnD / 32 + (seg >> 1)];
-            const int jn = (rnew & 31) >> 3;
+            const int jn = (rnew % WROWS) >> 3;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < RPL; ++j)
                 if (j == jn) {
                     kv[j] = kc;
                     vv[j] = vc;
@@ -136,9 +141,9 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
     const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
 
     // ---- scores of the lane's four rows
-    float s[4];
+    float s[RPL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < RPL; ++j) {
         uint32_t kb[8];
         i8x4_to_bf16x4(kv[j].x, kb[0], kb[1]);
         i8x4_to_bf16x4(kv[j].y, kb[2], kb[3]);
@@ -159,7 +164,9 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
     }
 
     // ---- workgroup maximum
-    float m = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    float m = s[0];
+#pragma unroll
+    for (int j = 1; j < RPL; ++j) m = fmaxf(m, s[j]);
     m = fmaxf(m, __shfl_xor(m, 8));
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
     for (int e = 0; e < 16; ++e) o[e] = 0.0f;
     float l = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < RPL; ++j) {
         const float p = expf(s[j] - m);                 // rows past t: exp(-inf) = 0
         l += p;
         const float pv = p * half_bits_to_float((uint16_t)vs[j]);
@@ -314,10 +321,16 @@ hipError_t launch_attn_decode(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_
                               float* work, const uint16_t* knew, const uint16_t* vnew,
                               const DeviceInfo& dev, hipStream_t stream) {
     (void)dev;
-    const int nchunks = (int)attn_chunks(t);
+    const bool wide = t > kAttnWideFrom;
+    const int64_t chunk = wide ? 2 * kAttnChunk : kAttnChunk;
+    const int nchunks = (int)((t + chunk - 1) / chunk);
     (void)hipGetLastError();
-    attn_split_kernel<<<(unsigned)(heads * nchunks), 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale,
-                                                                       nchunks, work, out, knew, vnew);
+    if (wide)
+        attn_split_kernel<8><<<(unsigned)(heads * nchunks), 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale,
+                                                                              nchunks, work, out, knew, vnew);
+    else
+        attn_split_kernel<4><<<(unsigned)(heads * nchunks), 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale,
+                                                                              nchunks, work, out, knew, vnew);
     if (nchunks > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

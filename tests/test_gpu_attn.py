@@ -1,9 +1,11 @@
 """GPU parity of the decode attention over a Q8_0 key/value cache, through the
 C ABI, against the fp64 oracle (max-abs 2e-3, relative L2 1e-5 per call).
 
-Shapes cover one and several 128-row chunks with ragged ends, the pages' static
-slab (capacity 4096, 12 heads of 128) at short and full context, and rows past
-t filled with NaN scales, so that any read past t would show."""
+Shapes cover one and several chunks with ragged ends (128-row chunks up to
+2048 rows, 256-row chunks above, and more than 32 chunks, the combine's batched
+path), the pages' static slab (capacity 4096, 12 heads of 128) at short and
+full context, and rows past t filled with NaN scales, so that any read past t
+would show."""
 import math
 
 import numpy as np
@@ -56,7 +58,9 @@ def run(q, kq, kd, vq, vd, t, scale=SCALE):
 
 @pytest.mark.parametrize("heads,t,t_cap", [(1, 1, 1), (2, 5, 8), (12, 127, 128), (12, 128, 128),
                                            (12, 129, 200), (3, 1000, 1024), (5, 333, 4096),
-                                           (12, 512, 4096), (12, 2048, 4096), (12, 4096, 4096)])
+                                           (12, 512, 4096), (12, 2048, 4096), (12, 4096, 4096),
+                                           (4, 2049, 4096), (3, 3001, 4096), (2, 2300, 2400),
+                                           (2, 9000, 9000)])
 def test_attn_matches_oracle(heads, t, t_cap):
     log(f"attn heads={heads} t={t} t_cap={t_cap}")
     q, kq, kd, vq, vd = cache(9000 + heads + t, heads, t, t_cap)
@@ -145,7 +149,8 @@ def test_attn_one_workspace_across_context_lengths():
         assert torch.equal(y, q8.attn_decode(dq, dkq, dkd, dvq, dvd, t, SCALE))
 
 
-@pytest.mark.parametrize("t,t_cap", [(1, 16), (128, 256), (129, 256), (200, 200), (4096, 4096), (1500, 2048)])
+@pytest.mark.parametrize("t,t_cap", [(1, 16), (128, 256), (129, 256), (200, 200), (4096, 4096), (1500, 2048),
+                                     (2049, 2100), (2200, 4096), (3000, 3000), (9000, 9000)])
 def test_attn_append_writes_row_and_attends(t, t_cap):
     """The new key/value rows land in cache row t - 1 exactly as the activation
     quantizer writes them, nothing else in the cache changes, and the output is
