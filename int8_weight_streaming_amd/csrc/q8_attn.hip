@@ -98,12 +98,18 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
 
     u32x4 kv[RPL], vv[RPL];
     uint32_t ks[RPL], vs[RPL];
+    // keys and their scales first (the scores need only them), then values
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
         const int row = row0 + 8 * j;
         kv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, row * kAttnD + 16 * seg, 0, kLoadNT));
-        vv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, row * kAttnD + 16 * seg, 0, kLoadNT));
         ks[j] = __builtin_amdgcn_raw_buffer_load_b16(rKs, row * 8 + 2 * (seg >> 1), 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);        // (the scheduler would group loads by type)
+#pragma unroll
+    for (int j = 0; j < RPL; ++j) {
+        const int row = row0 + 8 * j;
+        vv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, row * kAttnD + 16 * seg, 0, kLoadNT));
         vs[j] = __builtin_amdgcn_raw_buffer_load_b16(rVs, row * 8 + 2 * (seg >> 1), 0, 0);
     }
     if (append) {
