@@ -46,6 +46,9 @@ def _norm_bf16(h_host):
 
 
 def test_reduced_step_op_by_op():
+    """Two consecutive tokens (context 300, then 301) of the reduced model,
+    every operation checked; the second token attends over the first one's
+    appended rows, which stay unchanged."""
     blocks, vocab, t, t_cap = 2, 4096, 300, 512
     order, module_ends = [0, 1, 0, 1], [1, 3]
     host, dev_w = {}, {}
@@ -69,10 +72,11 @@ def test_reduced_step_op_by_op():
     st.h.copy_(to_dev(h0))
     torch.cuda.synchronize()
 
-    state = {"h": h0.astype(np.float32)}
+    state = {"h": h0.astype(np.float32), "t": t}
     checked = []
 
     def hook(stage, v):
+        t = state["t"]
         torch.cuda.synchronize()
         h_prev = state["h"]
         h_now = to_host(st.h)
@@ -121,6 +125,13 @@ def test_reduced_step_op_by_op():
 
     st.run(t, hook=hook)
     assert len(checked) == 5 * len(order) + len(module_ends) + 1
+    # the next token: its attention reads the row this token appended
+    appended = [(to_host(st.kq[v][:, t - 1]), to_host(st.vd[v][:, t - 1])) for v in range(len(order))]
+    state["t"] = t + 1
+    st.run(t + 1, hook=hook)
+    assert len(checked) == 2 * (5 * len(order) + len(module_ends) + 1)
+    for v, (kq_row, vd_row) in enumerate(appended):
+        assert np.array_equal(to_host(st.kq[v][:, t - 1]), kq_row) and np.array_equal(to_host(st.vd[v][:, t - 1]), vd_row)
 
 
 def test_full_step_graph_replay_bitwise():
