@@ -137,6 +137,35 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _out(t, name: str, dtype: torch.dtype, numel: int) -> torch.Tensor:
+    """A caller-provided output buffer: dtype, device and contiguity as for
+    inputs, and exactly `numel` elements (any shape), so no kernel writes past
+    its end."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype == torch.uint16:
+        t = _as_bits16(t)
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got shape {tuple(t.shape)}")
+    return t
+
+
+def _work(work) -> int:
+    """Words of a caller-provided fp32 attention workspace (0 for None)."""
+    if work is None:
+        return 0
+    if not isinstance(work, torch.Tensor) or work.dtype != torch.float32 or not work.is_cuda \
+            or not work.is_contiguous():
+        raise ValueError("work must be a contiguous fp32 device tensor")
+    return work.numel()
+
+
 def _as_bits16(t: torch.Tensor) -> torch.Tensor:
     if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.uint16)
@@ -153,7 +182,7 @@ def quantize_weights(w: torch.Tensor, out=None):
         wq = torch.empty((n, k), dtype=torch.int8, device=w.device)
         wd = torch.empty((n, k // 32), dtype=torch.uint16, device=w.device)
     else:
-        wq, wd = out
+        wq, wd = _out(out[0], "wq", torch.int8, n * k), _out(out[1], "wd", torch.uint16, n * (k // 32))
     _check("q8_quantize_weights", load_library().q8_quantize_weights(
         _ptr(w), n, k, _ptr(wq), _ptr(wd), _stream()))
     return wq, wd
@@ -168,7 +197,7 @@ def quantize_act(x: torch.Tensor, out=None):
         xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
         xd = torch.empty((m, k // 32), dtype=torch.uint16, device=x.device)
     else:
-        xq, xd = out
+        xq, xd = _out(out[0], "xq", torch.int8, m * k), _out(out[1], "xd", torch.uint16, m * (k // 32))
     _check("q8_quantize_act", load_library().q8_quantize_act(
         _ptr(x), m, k, _ptr(xq), _ptr(xd), _stream()))
     return xq, xd
@@ -203,7 +232,8 @@ def gemm_skinny(wq, wd, x, xd=None, out=None):
     m = x.shape[0]
     if x.shape[1] != k:
         raise ValueError(f"x must have {k} columns, got {x.shape[1]}")
-    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=wq.device)
+    y = _out(out, "out", torch.float32, m * n) if out is not None else \
+        torch.empty((m, n), dtype=torch.float32, device=wq.device)
     _check("q8_gemm_skinny", load_library().q8_gemm_skinny(
         _ptr(wq), _ptr(wd), n, k, m, act, _ptr(x), _ptr(xd), _ptr(y), _stream()))
     return y
@@ -223,7 +253,8 @@ def gemv(wq, wd, x, xd=None, out=None):
         act = Q8_ACT_Q8
     if x.shape[0] != k:
         raise ValueError(f"x must have {k} elements, got {x.shape[0]}")
-    y = out if out is not None else torch.empty((n,), dtype=torch.float32, device=wq.device)
+    y = _out(out, "out", torch.float32, n) if out is not None else \
+        torch.empty((n,), dtype=torch.float32, device=wq.device)
     _check("q8_gemv", load_library().q8_gemv(
         _ptr(wq), _ptr(wd), n, k, act, _ptr(x), _ptr(xd), _ptr(y), _stream()))
     return y
@@ -238,7 +269,8 @@ def gemm_prefill(wq, wd, xq, xd, out=None):
     p = xq.shape[0]
     if xq.shape[1] != k or tuple(xd.shape) != (p, k // 32):
         raise ValueError("xq must be [p][k] and xd [p][k/32]")
-    y = out if out is not None else torch.empty((p, n), dtype=torch.float32, device=wq.device)
+    y = _out(out, "out", torch.float32, p * n) if out is not None else \
+        torch.empty((p, n), dtype=torch.float32, device=wq.device)
     _check("q8_gemm_prefill", load_library().q8_gemm_prefill(
         _ptr(wq), _ptr(wd), n, k, p, _ptr(xq), _ptr(xd), _ptr(y), _stream()))
     return y
@@ -252,7 +284,8 @@ def block_dots(wq, xq, out=None):
     m = xq.shape[0]
     if xq.shape[1] != k:
         raise ValueError("xq must be [m][k]")
-    isum = out if out is not None else torch.empty((m, n, k // 32), dtype=torch.int32, device=wq.device)
+    isum = _out(out, "out", torch.int32, m * n * (k // 32)) if out is not None else \
+        torch.empty((m, n, k // 32), dtype=torch.int32, device=wq.device)
     _check("q8_block_dots", load_library().q8_block_dots(
         _ptr(wq), n, k, m, _ptr(xq), _ptr(isum), _stream()))
     return isum
@@ -276,15 +309,14 @@ def gemm_fused(wq, wd, x, prologue: int, epilogue: int, out=None, rope_rows: int
     m = x.shape[0]
     if x.shape[1] != k:
         raise ValueError(f"x must have {k} columns, got {x.shape[1]}")
+    fp32_out = epilogue in (EPI_F32, EPI_ADD)
+    shape = (m, n // 2) if epilogue == EPI_SWIGLU else (m, n)
     if out is None:
         if epilogue == EPI_ADD:
             raise ValueError("EPI_ADD needs the residual buffer as `out`")
-        if epilogue == EPI_F32:
-            out = torch.empty((m, n), dtype=torch.float32, device=wq.device)
-        elif epilogue == EPI_SWIGLU:
-            out = torch.empty((m, n // 2), dtype=torch.uint16, device=wq.device)
-        else:
-            out = torch.empty((m, n), dtype=torch.uint16, device=wq.device)
+        out = torch.empty(shape, dtype=torch.float32 if fp32_out else torch.uint16, device=wq.device)
+    else:
+        out = _out(out, "out", torch.float32 if fp32_out else torch.uint16, shape[0] * shape[1])
     _check("q8_gemm_fused", load_library().q8_gemm_fused(
         _ptr(wq), _ptr(wd), n, k, m, int(prologue), _ptr(x), int(epilogue), _ptr(out),
         int(rope_rows), int(pos), _stream()))
@@ -295,7 +327,7 @@ def rmsnorm(x, out=None):
     """Weightless RMSNorm (eps 1e-6) of the fp32 rows of x; `out` may be x."""
     _need(x, "x", torch.float32, 2)
     m, k = x.shape
-    y = out if out is not None else torch.empty_like(x)
+    y = _out(out, "out", torch.float32, m * k) if out is not None else torch.empty_like(x)
     _check("q8_rmsnorm", load_library().q8_rmsnorm(_ptr(x), m, k, _ptr(y), _stream()))
     return y
 
@@ -309,7 +341,7 @@ def quantize_act_fused(x, prologue, out=None):
         xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
         xd = torch.empty((m, k // 32), dtype=torch.uint16, device=x.device)
     else:
-        xq, xd = out
+        xq, xd = _out(out[0], "xq", torch.int8, m * k), _out(out[1], "xd", torch.uint16, m * (k // 32))
     _check("q8_quantize_act_fused", load_library().q8_quantize_act_fused(
         _ptr(x), m, k, int(prologue), _ptr(xq), _ptr(xd), _stream()))
     return xq, xd
@@ -325,7 +357,7 @@ def q4_quantize_weights(w: torch.Tensor, out=None):
         wq = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
         wd = torch.empty((n, k // 32), dtype=torch.uint16, device=w.device)
     else:
-        wq, wd = out
+        wq, wd = _out(out[0], "wq", torch.uint8, n * (k // 2)), _out(out[1], "wd", torch.uint16, n * (k // 32))
     _check("q4_quantize_weights", load_library().q4_quantize_weights(
         _ptr(w), n, k, _ptr(wq), _ptr(wd), _stream()))
     return wq, wd
@@ -354,7 +386,8 @@ def q4_gemm_skinny(wq, wd, x, xd=None, out=None):
     m = x.shape[0]
     if x.shape[1] != k:
         raise ValueError(f"x must have {k} columns, got {x.shape[1]}")
-    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=wq.device)
+    y = _out(out, "out", torch.float32, m * n) if out is not None else \
+        torch.empty((m, n), dtype=torch.float32, device=wq.device)
     _check("q4_gemm_skinny", load_library().q4_gemm_skinny(
         _ptr(wq), _ptr(wd), n, k, m, act, _ptr(x), _ptr(xd), _ptr(y), _stream()))
     return y
@@ -385,8 +418,9 @@ def attn_decode(q, kq, kd, vq, vd, t: int, scale: float, work=None, out=None):
     need = attn_work_words(heads, t) if 1 <= t <= t_cap else 0
     if work is None and need > 0:
         work = torch.empty((need,), dtype=torch.float32, device=kq.device)
-    y = out if out is not None else torch.empty((heads, d), dtype=torch.float32, device=kq.device)
-    words = work.numel() if work is not None else 0
+    y = _out(out, "out", torch.float32, heads * d) if out is not None else \
+        torch.empty((heads, d), dtype=torch.float32, device=kq.device)
+    words = _work(work)
     _check("q8_attn_decode", load_library().q8_attn_decode(
         _ptr(q), _ptr(kq), _ptr(kd), _ptr(vq), _ptr(vd), heads, int(t), t_cap, d, float(scale),
         _ptr(y), _ptr(work), words, _stream()))
@@ -413,8 +447,9 @@ def attn_decode_append(q, kq, kd, vq, vd, t: int, scale: float, knew, vnew, work
     need = attn_work_words(heads, t) if 1 <= t <= t_cap else 0
     if work is None and need > 0:
         work = torch.empty((need,), dtype=torch.float32, device=kq.device)
-    y = out if out is not None else torch.empty((heads, d), dtype=torch.float32, device=kq.device)
-    words = work.numel() if work is not None else 0
+    y = _out(out, "out", torch.float32, heads * d) if out is not None else \
+        torch.empty((heads, d), dtype=torch.float32, device=kq.device)
+    words = _work(work)
     _check("q8_attn_decode_append", load_library().q8_attn_decode_append(
         _ptr(q), _ptr(kq), _ptr(kd), _ptr(vq), _ptr(vd), heads, int(t), t_cap, d, float(scale),
         _ptr(knew), _ptr(vnew), _ptr(y), _ptr(work), words, _stream()))
@@ -428,8 +463,11 @@ def probe_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Ten
     if not buf.is_cuda or not buf.is_contiguous():
         raise ValueError("buf must be a contiguous device tensor")
     L = load_library()
+    words = max(1, L.q8_probe_sink_words())
     if sink is None:
-        sink = torch.empty((max(1, L.q8_probe_sink_words()),), dtype=torch.int32, device=buf.device)
+        sink = torch.empty((words,), dtype=torch.int32, device=buf.device)
+    elif sink.dtype != torch.int32 or not sink.is_cuda or not sink.is_contiguous() or sink.numel() < words:
+        raise ValueError(f"sink must be a contiguous int32 device tensor of >= {words} words")
     nbytes = buf.numel() * buf.element_size()
     _check("q8_probe_read", L.q8_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream()))
     return sink
