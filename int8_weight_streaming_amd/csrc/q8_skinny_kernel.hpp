@@ -261,6 +261,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
+    // staged activation pieces of a tile (batch 3-8), see below
+    constexpr bool XPRE = !XREG && PRO == kProBf16;
+    constexpr int XP = XPRE ? (M * TCH * (XCH_BYTES / 16) + 255) / 256 : 1;
+    constexpr int XS = XPRE && ACT == 1 ? (M * (TCH / 2) + 255) / 256 : 1;
+    u32x4 xst[XP];
+    uint16_t xsb[XS];
     for (int c0 = 0; c0 < nch; c0 += TCH) {
         // ---- activations held in registers: fetched first (small, cache
         // resident), so their latency hides under the weight stream
@@ -282,6 +288,39 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
                     }
                 }
             }
+        }
+        // ---- bf16 / Q8 activations staged in LDS (batch 3-8): this thread's
+        // pieces of the tile are fetched now, before the weights, and written
+        // to LDS once the weight loads are in flight (loads return in order:
+        // fetched after the weights, writing them would wait for the whole
+        // weight tile)
+        const int tch = nch - c0 < TCH ? nch - c0 : TCH;          // chunks in this tile
+        const int pieces = M * tch * (XCH_BYTES / 16);
+        if constexpr (XPRE) {
+            // unconditional loads (indices past the tile clamped to its last
+            // piece): a load inside a divergent branch is waited for at once
+#pragma unroll
+            for (int u = 0; u < XP; ++u) {
+                const int i0 = threadIdx.x + 256 * u;
+                const int i = i0 < pieces ? i0 : pieces - 1;
+                const int q = ACT == 0 ? (i & 1) : 0;
+                const int rest = ACT == 0 ? (i >> 1) : i;
+                const int ch = rest % tch, m = rest / tch;
+                const unsigned char* src = static_cast<const unsigned char*>(xv) +
+                    ((int64_t)m * k + (int64_t)(c0 + ch) * 16) * (ACT == 0 ? 2 : 1) + q * 16;
+                xst[u] = *reinterpret_cast<const u32x4*>(src);
+            }
+            if constexpr (ACT == 1) {
+                const int nsc = M * (tch >> 1);
+#pragma unroll
+                for (int u = 0; u < XS; ++u) {
+                    const int i0 = threadIdx.x + 256 * u;
+                    const int i = i0 < nsc ? i0 : nsc - 1;
+                    const int bl = i % (tch >> 1), m = i / (tch >> 1);
+                    xsb[u] = xdp[(int64_t)m * nb + (c0 >> 1) + bl];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // ---- weights and their block scales (raw binary16, converted at use)
         u32x4 w[CPL][R];
@@ -346,31 +385,40 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
         } else if (!XREG) {
             // stage the tile in LDS while the weight loads are in flight:
             // [m][chunk] with XCH_BYTES per chunk, then the Q8 scales
-            const int tch = nch - c0 < TCH ? nch - c0 : TCH;
             __syncthreads();
-            const int pieces = M * tch * (XCH_BYTES / 16);
-            for (int i = threadIdx.x; i < pieces; i += 256) {
-                const int q = ACT == 0 ? (i & 1) : 0;
-                const int rest = ACT == 0 ? (i >> 1) : i;
-                const int ch = rest % tch, m = rest / tch;
-                uint4 piece;
-                if constexpr (PRO == kProBf16) {
-                    const unsigned char* src = static_cast<const unsigned char*>(xv) +
-                        ((int64_t)m * k + (int64_t)(c0 + ch) * 16) * (ACT == 0 ? 2 : 1) + q * 16;
-                    piece = *reinterpret_cast<const uint4*>(src);
-                } else {
+            if constexpr (XPRE) {
+                // (indices clamped as for the loads: a lane past the tile
+                // writes its last piece again, with the same bytes)
+#pragma unroll
+                for (int u = 0; u < XP; ++u) {
+                    const int i0 = threadIdx.x + 256 * u;
+                    const int i = i0 < pieces ? i0 : pieces - 1;
+                    const int q = ACT == 0 ? (i & 1) : 0;
+                    const int rest = ACT == 0 ? (i >> 1) : i;
+                    const int ch = rest % tch, m = rest / tch;
+                    *reinterpret_cast<u32x4*>(lds + (m * TCH + ch) * XCH_BYTES + q * 16) = xst[u];
+                }
+                if constexpr (ACT == 1) {
+                    float* sc = reinterpret_cast<float*>(lds + M * TCH * XCH_BYTES);
+                    const int nsc = M * (tch >> 1);
+#pragma unroll
+                    for (int u = 0; u < XS; ++u) {
+                        const int i0 = threadIdx.x + 256 * u;
+                        const int i = i0 < nsc ? i0 : nsc - 1;
+                        const int bl = i % (tch >> 1), m = i / (tch >> 1);
+                        sc[m * (TCH / 2) + bl] = half_bits_to_float(xsb[u]);
+                    }
+                }
+            } else {
+                // fp32 rows (fused prologues above batch 2): scaled and rounded here
+                for (int i = threadIdx.x; i < pieces; i += 256) {
+                    const int q = i & 1;
+                    const int ch = (i >> 1) % tch, m = (i >> 1) / tch;
                     float mul = 1.0f;
 #pragma unroll
                     for (int mm = 0; mm < M; ++mm) mul = mm == m ? xmul[mm] : mul;
-                    piece = load_x8_f32(static_cast<const float*>(xv) + (int64_t)m * k + (int64_t)(c0 + ch) * 16 + q * 8, mul);
-                }
-                *reinterpret_cast<uint4*>(lds + (m * TCH + ch) * XCH_BYTES + q * 16) = piece;
-            }
-            if (ACT == 1) {
-                float* sc = reinterpret_cast<float*>(lds + M * TCH * XCH_BYTES);
-                for (int i = threadIdx.x; i < M * (tch >> 1); i += 256) {
-                    const int bl = i % (tch >> 1), m = i / (tch >> 1);
-                    sc[m * (TCH / 2) + bl] = half_bits_to_float(xdp[(int64_t)m * nb + (c0 >> 1) + bl]);
+                    *reinterpret_cast<uint4*>(lds + (m * TCH + ch) * XCH_BYTES + q * 16) =
+                        load_x8_f32(static_cast<const float*>(xv) + (int64_t)m * k + (int64_t)(c0 + ch) * 16 + q * 8, mul);
                 }
             }
             __syncthreads();
