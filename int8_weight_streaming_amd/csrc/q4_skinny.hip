@@ -121,7 +121,41 @@ __global__ __launch_bounds__(256) void q4_skinny_kernel(const uint8_t* __restric
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
+    // LDS-staged activations: each thread's 16-byte pieces of a tile (and the
+    // Q8 scales) are fetched before the weights and written to LDS once the
+    // weight loads are issued (loads return in order: fetched after the
+    // weights, writing them would wait for the whole weight tile)
+    constexpr int PIECES = XW / 4;               // 16-byte pieces per block and row
+    constexpr int XP = XREG ? 1 : (M * TCH * PIECES + 255) / 256;
+    constexpr int XS = XREG || ACT == 0 ? 1 : (M * TCH + 255) / 256;
+    u32x4 xst[XP];
+    uint16_t xsb[XS];
     for (int c0 = 0; c0 < nb; c0 += TCH) {
+        const int tch = nb - c0 < TCH ? nb - c0 : TCH;   // blocks in this tile
+        const int pieces = M * tch * PIECES;
+        if constexpr (!XREG) {
+            // unconditional loads, indices past the tile clamped to its last
+            // piece (a load under a divergent branch is waited for at once)
+#pragma unroll
+            for (int u = 0; u < XP; ++u) {
+                const int i0 = threadIdx.x + 256 * u;
+                const int i = i0 < pieces ? i0 : pieces - 1;
+                const int q = i % PIECES, rest = i / PIECES;
+                const int ch = rest % tch, m = rest / tch;
+                const unsigned char* src = static_cast<const unsigned char*>(xv) +
+                    ((int64_t)m * k + (int64_t)(c0 + ch) * 32) * (ACT == 0 ? 2 : 1) + q * 16;
+                xst[u] = *reinterpret_cast<const u32x4*>(src);
+            }
+            if constexpr (ACT == 1) {
+#pragma unroll
+                for (int u = 0; u < XS; ++u) {
+                    const int i0 = threadIdx.x + 256 * u;
+                    const int i = i0 < M * tch ? i0 : M * tch - 1;
+                    xsb[u] = xdp[(int64_t)(i / tch) * nb + c0 + i % tch];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         uint32_t xr[XREG ? M : 1][XREG ? CPL : 1][XW];
         float xsr[XREG ? M : 1][XREG ? CPL : 1];
         if constexpr (XREG) {
@@ -160,26 +194,25 @@ __global__ __launch_bounds__(256) void q4_skinny_kernel(const uint8_t* __restric
             }
         }
         if constexpr (!XREG) {
-            // stage the tile's activations in LDS while the weights stream in:
-            // [m][block] with XW words each, then the Q8 scales as fp32
-            const int tch = nb - c0 < TCH ? nb - c0 : TCH;
+            // the tile's activations into LDS, [m][block] with XW words each,
+            // then the Q8 scales as fp32 (a lane past the tile writes its
+            // clamped piece again, with the same bytes)
             __syncthreads();
-            constexpr int PIECES = XW / 4;       // 16-byte pieces per block and row
-            const int pieces = M * tch * PIECES;
-            for (int i = threadIdx.x; i < pieces; i += 256) {
-                const int q = i % PIECES;
-                const int rest = i / PIECES;
+#pragma unroll
+            for (int u = 0; u < XP; ++u) {
+                const int i0 = threadIdx.x + 256 * u;
+                const int i = i0 < pieces ? i0 : pieces - 1;
+                const int q = i % PIECES, rest = i / PIECES;
                 const int ch = rest % tch, m = rest / tch;
-                const unsigned char* src = static_cast<const unsigned char*>(xv) +
-                    ((int64_t)m * k + (int64_t)(c0 + ch) * 32) * (ACT == 0 ? 2 : 1) + q * 16;
-                *reinterpret_cast<uint4*>(lds + ((m * TCH + ch) * PIECES + q) * 16) =
-                    *reinterpret_cast<const uint4*>(src);
+                *reinterpret_cast<u32x4*>(lds + ((m * TCH + ch) * PIECES + q) * 16) = xst[u];
             }
-            if (ACT == 1) {
+            if constexpr (ACT == 1) {
                 float* sc = reinterpret_cast<float*>(lds + M * TCH * 32);
-                for (int i = threadIdx.x; i < M * tch; i += 256) {
-                    const int bl = i % tch, m = i / tch;
-                    sc[m * TCH + bl] = half_bits_to_float(xdp[(int64_t)m * nb + c0 + bl]);
+#pragma unroll
+                for (int u = 0; u < XS; ++u) {
+                    const int i0 = threadIdx.x + 256 * u;
+                    const int i = i0 < M * tch ? i0 : M * tch - 1;
+                    sc[(i / tch) * TCH + i % tch] = half_bits_to_float(xsb[u]);
                 }
             }
             __syncthreads();
