@@ -48,7 +48,7 @@ __device__ __forceinline__ float max32(float v) {
     v = fmaxf(v, dpp_f<0x4E>(v));
     v = fmaxf(v, dpp_f<0x141>(v));
     v = fmaxf(v, dpp_f<0x140>(v));
-    return fmaxf(v, __shfl_xor(v, 16));
+    return xor16_max(v);
 }
 
 template <int RPL>
@@ -173,9 +173,9 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
     float m = s[0];
 #pragma unroll
     for (int j = 1; j < RPL; ++j) m = fmaxf(m, s[j]);
-    m = fmaxf(m, __shfl_xor(m, 8));
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = fmaxf(m, dpp_f<0x128>(m));              // row_ror:8 = lane ^ 8 inside a row
+    m = xor16_max(m);
+    m = xor32_max(m);
     if (lane == 0) red[wave][kAttnD] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0][kAttnD], red[1][kAttnD]), fmaxf(red[2][kAttnD], red[3][kAttnD]));
@@ -202,13 +202,13 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
     // the eight row groups of the wave (lanes with equal seg), fixed tree
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        o[e] += __shfl_xor(o[e], 8);
-        o[e] += __shfl_xor(o[e], 16);
-        o[e] += __shfl_xor(o[e], 32);
+        o[e] += dpp_f<0x128>(o[e]);
+        o[e] = xor16_sum(o[e]);
+        o[e] = xor32_sum(o[e]);
     }
-    l += __shfl_xor(l, 8);
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l += dpp_f<0x128>(l);
+    l = xor16_sum(l);
+    l = xor32_sum(l);
     if (rsub == 0) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) red[wave][16 * seg + e] = o[e];

@@ -116,12 +116,40 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// Lane l and its partner l ^ 16 (l ^ 32) through the gfx950 permlane swaps,
+// which exchange the halves of every 32-lane (64-lane) group in the vector
+// ALU instead of through LDS: with both operands v, the two results hold the
+// lower and the upper partner's value on every lane, so a sum adds the same
+// two values in the same order on both partners (identical bits, and the same
+// as v + shfl_xor(v, 16 or 32), fp32 addition being commutative).
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+// The value of lane l ^ 32.
+__device__ __forceinline__ float xor32_value(float v) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? s[0] : s[1]);
+}
+
 // Sum over groups of G lanes (G = 16, 32 or 64), same fixed order everywhere.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
     v = row16_sum(v);
-    if (G >= 32) v += __shfl_xor(v, 16);
-    if (G >= 64) v += __shfl_xor(v, 32);
+    if (G >= 32) v = xor16_sum(v);
+    if (G >= 64) v = xor32_sum(v);
     return v;
 }
 

@@ -540,7 +540,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
         } else {
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const float other = __shfl_xor(acc[0][m], 32);
+                const float other = xor32_value(acc[0][m]);
                 pa[m] = grp == 0 ? acc[0][m] : other;
                 pb[m] = grp == 0 ? other : acc[0][m];
             }
