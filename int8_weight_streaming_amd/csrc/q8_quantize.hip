@@ -4,7 +4,7 @@
 // wave covers 8 blocks: the fp32 input is read as one 1 KB contiguous span per
 // wave instruction (bf16: 512 B), codes are written as one 256 B span and the
 // eight binary16 scales as 16 B.  The block's largest magnitude is combined over
-// the 8 lanes with xor shuffles, then each lane rounds its own 4 values
+// the 8 lanes by DPP, then each lane rounds its own 4 values
 // [fak MODEL-BASELINE-RESULTS, ACT 3 item 1 (format), ACT 4 "Correctness" and
 // ACT 5 "What moved" item 3 (round half away from zero)].  HBM-bound.
 #include "q8_device.hpp"
@@ -35,9 +35,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ src
         float v[4];
         load4(src + b * 32 + sub * 4, v);
         float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-        a = fmaxf(a, __shfl_xor(a, 1, 8));
-        a = fmaxf(a, __shfl_xor(a, 2, 8));
-        a = fmaxf(a, __shfl_xor(a, 4, 8));
+        // maximum over the block's 8 lanes by DPP: xor 1 and xor 2 inside the
+        // quad, then the half-row mirror (lane i of 8 with lane 7 - i, in the
+        // other quad); a maximum is exact in any order
+        a = fmaxf(a, dpp_f<0xB1>(a));
+        a = fmaxf(a, dpp_f<0x4E>(a));
+        a = fmaxf(a, dpp_f<0x141>(a));
         const uint16_t sb = block_scale_bits(a);
         const float s = half_bits_to_float(sb);
         const uint32_t c0 = (uint32_t)block_code(v[0], s) & 0xFFu;
