@@ -488,9 +488,10 @@ def bench_mimir_with_kv(q8, wl, dev, weights, slabs, t: int = 512, replays: int 
 def bench_fused_step(q8, wl, dev, weights, t: int, replays: int = 10) -> dict:
     """One batch-1 decode token of the whole block -- the glue fused into the
     products (RMSNorm, RoPE, SwiGLU, residual adds), attention that appends the
-    token's key and value to its int8 cache, a final norm per module run, the
-    lm_head -- captured once into a graph and replayed (context t, one cache of
-    t rows per virtual layer).  Bytes per token = weights + KV read."""
+    token's key and value to its int8 cache (its combine folded into the o
+    product up to 1024 rows), a final norm per module run, the lm_head --
+    captured once into a graph and replayed (context t, one cache of t rows
+    per virtual layer).  Bytes per token = weights + KV read."""
     import torch
     from int8_weight_streaming_amd.decode_step import DecodeStep
     order = [blk for blk, _ in wl.mimir_step_order()[:-1:4]]
@@ -500,7 +501,9 @@ def bench_fused_step(q8, wl, dev, weights, t: int, replays: int = 10) -> dict:
                     wl.rope_pair_rows(2 * wl.HIDDEN, 3 * wl.HIDDEN), wl.swiglu_pair_rows(2 * wl.INTER))
     st.h.copy_(to_dev(wl.bf16_bits_to_f32(wl.normal_act_bf16(9901, 1, wl.HIDDEN)), dev))
     ms = time_graph(lambda: st.run(t), 1, reps=replays)
-    launches = len(order) * (5 + (1 if t > 128 else 0)) + len(module_ends) + 1
+    # per layer: qkv, attention, o, gate/up, down, and the attention's combine
+    # launch where it is not folded into the o product (contexts above 1024)
+    launches = len(order) * (5 + (1 if t > 1024 else 0)) + len(module_ends) + 1
     nbytes = mimir_step_bytes(wl, 1) + 128 * attn_bytes(t)
     del st
     torch.cuda.empty_cache()

@@ -190,6 +190,35 @@ q8_status q8_attn_decode_append(const uint16_t* q, int8_t* kq, uint16_t* kd, int
                                 const uint16_t* knew, const uint16_t* vnew, float* out, float* work,
                                 int64_t work_words, hipStream_t stream);
 
+/* The attention of q8_attn_decode_append without its combine step, for
+ * q8_gemm_attn_residual: the token's key and value rows are appended as there,
+ * and the per-chunk partials -- per head and chunk of cache rows, a record of
+ * 132 floats: the numerator sum_j e^(s_j - m) V_j [128], the chunk's largest
+ * score m, the denominator sum_j e^(s_j - m), 2 unused -- are left in `work`
+ * (also when one chunk covers the context); nothing else is written.  work:
+ * fp32, at least q8_attn_partial_words(heads, t) words (-1 when out of range).
+ * Other arguments and errors as q8_attn_decode_append, without `out`. */
+int64_t q8_attn_partial_words(int64_t heads, int64_t t);
+q8_status q8_attn_decode_append_partials(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_t* vq,
+                                         uint16_t* vd, int64_t heads, int64_t t, int64_t t_cap,
+                                         int64_t head_dim, float scale, const uint16_t* knew,
+                                         const uint16_t* vnew, float* work, int64_t work_words,
+                                         hipStream_t stream);
+
+/* The attention output projection with its residual add, reading the
+ * attention partials directly [Frigg README, Findings 3 and 8: every launch of a
+ * batch-1 step costs; this one saves the combine launch]:
+ *   h[j] += sum_i W[j][i] * bf16(a[i]),   a = the attention output [k/128][128],
+ * where a is combined from the partials q8_attn_decode_append_partials left in
+ * `work` for the same (heads = k / 128, t), exactly as q8_attn_decode combines
+ * them (bit for bit).  wq/wd Q8_0 [n][k]; h fp32 [n], read and written.  k a
+ * multiple of 128 with 128 <= k <= 2048 (the row is combined once per
+ * workgroup); 1 <= t <= 1024 (at most 8 chunks of cache rows); work_words at
+ * least q8_attn_partial_words(k / 128, t); Q8_ERR_SHAPE otherwise.  Other
+ * conventions as q8_gemm_fused with Q8_EPI_ADD at m = 1. */
+q8_status q8_gemm_attn_residual(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, const float* work,
+                                int64_t work_words, int64_t t, float* h, hipStream_t stream);
+
 /* ---- decode-step glue fused into the W8A16 products ---------------------------
  *
  * A decode block [Frigg README, "The model, as verified": pre-norm blocks,

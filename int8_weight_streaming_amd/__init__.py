@@ -46,7 +46,8 @@ EXPORTED = (
     "q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
     "q8_gemm_prefill", "q8_block_dots", "q8_attn_decode", "q8_attn_work_words",
     "q4_quantize_weights", "q4_gemm_skinny", "q8_gemm_fused", "q8_rmsnorm", "q8_attn_decode_append",
-    "q8_quantize_act_fused",
+    "q8_quantize_act_fused", "q8_attn_partial_words", "q8_attn_decode_append_partials",
+    "q8_gemm_attn_residual",
 )
 PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words", "q8_probe_barrier",
                   "q8_probe_barrier_words")
@@ -96,6 +97,12 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q8_gemm_fused.argtypes = [P, P, I64, I64, I64, I, P, I, P, I64, I64, P]
     L.q8_rmsnorm.argtypes = [P, I64, I64, P, P]
     L.q8_quantize_act_fused.argtypes = [P, I64, I64, I, P, P, P]
+    L.q8_attn_partial_words.argtypes = [I64, I64]
+    L.q8_attn_partial_words.restype = I64
+    L.q8_attn_decode_append_partials.argtypes = [P, P, P, P, P, I64, I64, I64, I64, C.c_float, P, P, P, I64, P]
+    L.q8_attn_decode_append_partials.restype = I
+    L.q8_gemm_attn_residual.argtypes = [P, P, I64, I64, P, I64, I64, P, P]
+    L.q8_gemm_attn_residual.restype = I
     L.q8_attn_decode_append.argtypes = [P, P, P, P, P, I64, I64, I64, I64, C.c_float, P, P, P, P, I64, P]
     L.q8_attn_decode_append.restype = I
     for name in ("q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
@@ -454,6 +461,47 @@ def attn_decode_append(q, kq, kd, vq, vd, t: int, scale: float, knew, vnew, work
         _ptr(q), _ptr(kq), _ptr(kd), _ptr(vq), _ptr(vd), heads, int(t), t_cap, d, float(scale),
         _ptr(knew), _ptr(vnew), _ptr(y), _ptr(work), words, _stream()))
     return y
+
+
+def attn_partial_words(heads: int, t: int) -> int:
+    """fp32 words of the per-chunk attention partials for (heads, t)."""
+    return int(load_library().q8_attn_partial_words(int(heads), int(t)))
+
+
+def attn_decode_append_partials(q, kq, kd, vq, vd, t: int, scale: float, knew, vnew, work=None):
+    """attn_decode_append without the combine: the per-chunk partials are left
+    in `work` (fp32, attn_partial_words(heads, t) words), which is returned."""
+    q, kd, vd, knew, vnew = (_as_bits16(a) for a in (q, kd, vd, knew, vnew))
+    _need(q, "q", torch.uint16, 2)
+    _need(knew, "knew", torch.uint16, 2)
+    _need(vnew, "vnew", torch.uint16, 2)
+    _need(kq, "kq", torch.int8, 3)
+    _need(vq, "vq", torch.int8, 3)
+    _need(kd, "kd", torch.uint16, 3)
+    _need(vd, "vd", torch.uint16, 3)
+    heads, t_cap, d = kq.shape
+    if tuple(q.shape) != (heads, d) or tuple(knew.shape) != (heads, d) or tuple(vnew.shape) != (heads, d):
+        raise ValueError("q, knew and vnew must be [heads][d]")
+    if tuple(vq.shape) != (heads, t_cap, d) or tuple(kd.shape) != (heads, t_cap, d // 32) or \
+            tuple(vd.shape) != tuple(kd.shape):
+        raise ValueError("cache shapes disagree")
+    need = attn_partial_words(heads, t) if 1 <= t <= t_cap else 0
+    if work is None:
+        work = torch.empty((max(need, 1),), dtype=torch.float32, device=kq.device)
+    _check("q8_attn_decode_append_partials", load_library().q8_attn_decode_append_partials(
+        _ptr(q), _ptr(kq), _ptr(kd), _ptr(vq), _ptr(vd), heads, int(t), t_cap, d, float(scale),
+        _ptr(knew), _ptr(vnew), _ptr(work), _work(work), _stream()))
+    return work
+
+
+def gemm_attn_residual(wq, wd, work, t: int, h):
+    """h (fp32 [1][n] or [n]) += W * bf16(a), a the attention output combined from
+    the partials in `work` (attn_decode_append_partials with heads = k / 128, t)."""
+    wd, n, k = _weights(wq, wd)
+    h = _out(h, "h", torch.float32, n)
+    _check("q8_gemm_attn_residual", load_library().q8_gemm_attn_residual(
+        _ptr(wq), _ptr(wd), n, k, _ptr(work), _work(work), int(t), _ptr(h), _stream()))
+    return h
 
 
 # ------------------------------------------------------------------ measurement utility

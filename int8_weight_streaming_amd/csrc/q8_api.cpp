@@ -337,4 +337,44 @@ q8_status q8_attn_decode_append(const uint16_t* q, int8_t* kq, uint16_t* kd, int
                                          *dev, stream));
 }
 
+int64_t q8_attn_partial_words(int64_t heads, int64_t t) {
+    if (heads < 0 || heads > kMaxAttnHeads || t < 1 || t > kMaxAttnRows) return -1;
+    return q8::attn_partial_floats(heads, t);
+}
+
+q8_status q8_attn_decode_append_partials(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_t* vq, uint16_t* vd,
+                                         int64_t heads, int64_t t, int64_t t_cap, int64_t head_dim, float scale,
+                                         const uint16_t* knew, const uint16_t* vnew, float* work,
+                                         int64_t work_words, hipStream_t stream) {
+    if (head_dim != 128) return Q8_ERR_SHAPE;
+    if (heads < 0 || heads > kMaxAttnHeads || t < 1 || t > t_cap || t_cap > kMaxAttnRows)
+        return Q8_ERR_SHAPE;
+    if (!(scale == scale) || scale - scale != 0.0f) return Q8_ERR_SHAPE;
+    if (heads == 0) return Q8_OK;
+    if (work_words < q8::attn_partial_floats(heads, t)) return Q8_ERR_SHAPE;
+    if (!q || !kq || !kd || !vq || !vd || !knew || !vnew || !work) return Q8_ERR_NULL;
+    if (!aligned16(q) || !aligned16(kq) || !aligned16(kd) || !aligned16(vq) || !aligned16(vd) ||
+        !aligned16(knew) || !aligned16(vnew) || !aligned16(work))
+        return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_attn_decode(q, kq, kd, vq, vd, heads, t, t_cap, scale, nullptr, work, knew, vnew,
+                                         *dev, stream));
+}
+
+q8_status q8_gemm_attn_residual(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, const float* work,
+                                int64_t work_words, int64_t t, float* h, hipStream_t stream) {
+    if (k < 128 || k % 128 != 0 || k > 2048) return Q8_ERR_SHAPE;
+    Q8_TRY(check_rows(n, k));
+    if (t < 1 || t > 1024) return Q8_ERR_SHAPE;
+    const int64_t chunks = q8::attn_split_chunks(t);
+    if (work_words < q8::attn_partial_floats(k / 128, t)) return Q8_ERR_SHAPE;
+    if (n == 0) return Q8_OK;
+    if (!wq || !wd || !work || !h) return Q8_ERR_NULL;
+    if (!aligned16(wq) || !aligned16(wd) || !aligned16(work) || !aligned16(h)) return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_attn_residual(wq, wd, n, k, work, (int)chunks, h, *dev, stream));
+}
+
 }  // extern "C"

@@ -34,13 +34,20 @@ namespace q8 {
 constexpr int kAttnD = 128;                    // head dimension
 constexpr int kAttnChunk = 128;                // cache rows per workgroup (four rows per lane)
 constexpr int64_t kAttnWideFrom = 2048;        // longer contexts: 256-row chunks (eight rows per lane)
-constexpr int kAttnPart = kAttnD + 2;          // floats per (head, chunk): o[128], m, l
+constexpr int kAttnPart = kAttnPartFloats;      // floats per (head, chunk): o[128], m, l, 2 pad (16-byte records)
+static_assert(kAttnPartFloats == kAttnD + 4, "partial record layout");
 
 int64_t attn_chunks(int64_t t) { return (t + kAttnChunk - 1) / kAttnChunk; }
 int64_t attn_work_floats(int64_t heads, int64_t t) {
     const int64_t c = attn_chunks(t);
     return c > 1 ? heads * c * kAttnPart : 0;
 }
+// chunks the split actually uses for context t (256-row chunks above kAttnWideFrom)
+int64_t attn_split_chunks(int64_t t) {
+    const int64_t chunk = t > kAttnWideFrom ? 2 * kAttnChunk : kAttnChunk;
+    return (t + chunk - 1) / chunk;
+}
+int64_t attn_partial_floats(int64_t heads, int64_t t) { return heads * attn_split_chunks(t) * kAttnPart; }
 
 // Maximum over each group of 32 lanes (exact in any order).
 __device__ __forceinline__ float max32(float v) {
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(const uint16_t* __restr
         const int d = threadIdx.x;
         const float od = ((red[0][d] + red[1][d]) + red[2][d]) + red[3][d];
         const float ls = ((red[0][kAttnD + 1] + red[1][kAttnD + 1]) + red[2][kAttnD + 1]) + red[3][kAttnD + 1];
-        if (nchunks == 1) {
+        if (nchunks == 1 && out != nullptr) {
             out[(int64_t)h * kAttnD + d] = od / ls;
         } else {
             float* part = work + ((int64_t)h * nchunks + c) * kAttnPart;
@@ -328,8 +335,7 @@ hipError_t launch_attn_decode(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_
                               const DeviceInfo& dev, hipStream_t stream) {
     (void)dev;
     const bool wide = t > kAttnWideFrom;
-    const int64_t chunk = wide ? 2 * kAttnChunk : kAttnChunk;
-    const int nchunks = (int)((t + chunk - 1) / chunk);
+    const int nchunks = (int)attn_split_chunks(t);
     (void)hipGetLastError();
     if (wide)
         attn_split_kernel<8><<<(unsigned)(heads * nchunks), 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale,
@@ -337,7 +343,7 @@ hipError_t launch_attn_decode(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_
     else
         attn_split_kernel<4><<<(unsigned)(heads * nchunks), 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale,
                                                                               nchunks, work, out, knew, vnew);
-    if (nchunks > 1) {
+    if (nchunks > 1 && out != nullptr) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         attn_combine_kernel<<<(unsigned)heads, kAttnD, 0, stream>>>(work, nchunks, out);

@@ -86,6 +86,21 @@ hipError_t launch_fused(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t
     return hipErrorInvalidValue;
 }
 
+// The output projection reading the attention partials directly (batch 1,
+// residual add): the prologue combines the row once per workgroup, so the
+// whole row must fit one K tile -- only such shapes are used.
+hipError_t launch_attn_residual(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, const float* work,
+                                int nchunks, float* y, const DeviceInfo& dev, hipStream_t stream) {
+    (void)hipGetLastError();
+    const int nb = (int)(k / 32);
+    const FuseArgs fa{0, 0, nchunks};
+    const int64_t tall_wgs = (n + 31) / 32;
+    if (tall_wgs >= (int64_t)dev.cu_count && k <= 16 * 6 * 16)
+        return fused_cfg<1, 16, 2, 6, kProAttn, kEpiAdd>(wq, wd, n, nb, work, y, fa, stream);
+    if (nb <= 48) return fused_cfg<1, 32, 1, 3, kProAttn, kEpiAdd>(wq, wd, n, nb, work, y, fa, stream);
+    return fused_cfg<1, 32, 1, 8, kProAttn, kEpiAdd>(wq, wd, n, nb, work, y, fa, stream);
+}
+
 // ------------------------------------------------------------------ RMSNorm
 
 // One workgroup per row: y = x * inv_rms(x), with the product prologue's own

@@ -32,6 +32,10 @@ hipError_t launch_fused(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t
                         const void* x, int epi, void* out, int64_t rope_rows, int64_t pos,
                         const DeviceInfo& dev, hipStream_t stream);
 hipError_t launch_rmsnorm(const float* x, int64_t m, int64_t k, float* y, hipStream_t stream);
+// y[n] += W * bf16(a): a = the attention output combined from the partials in
+// `work` (heads = k / 128, nchunks <= 8 of them per head).
+hipError_t launch_attn_residual(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, const float* work,
+                                int nchunks, float* y, const DeviceInfo& dev, hipStream_t stream);
 hipError_t launch_act_prologue_quantize(const float* x, int64_t m, int64_t k, int pro, int8_t* xq,
                                         uint16_t* xd, hipStream_t stream);
 
@@ -56,8 +60,16 @@ hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
 // (0 when one chunk covers the context).
 int64_t attn_chunks(int64_t t);
 int64_t attn_work_floats(int64_t heads, int64_t t);
+// The chunks the split uses for context t, and the floats of their partials:
+// per (head, chunk) a record of kAttnPartFloats floats (numerator [128], max,
+// denominator, padding), heads outer.
+int64_t attn_split_chunks(int64_t t);
+int64_t attn_partial_floats(int64_t heads, int64_t t);
+constexpr int kAttnPartFloats = 132;
 // With knew / vnew (bf16 [heads][128]) the key and value rows t - 1 are first
-// quantized into the cache; NULL leaves the cache untouched.
+// quantized into the cache; NULL leaves the cache untouched.  With out == NULL
+// the per-chunk partials are left in `work` (also for a single chunk) and not
+// combined.
 hipError_t launch_attn_decode(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_t* vq, uint16_t* vd,
                               int64_t heads, int64_t t, int64_t t_cap, float scale, float* out,
                               float* work, const uint16_t* knew, const uint16_t* vnew,

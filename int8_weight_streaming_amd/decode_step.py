@@ -9,6 +9,9 @@ applied in the order L L L H L L L H -- with the glue fused into the products:
     qkv      q8_gemm_fused  RMSNORM prologue, ROPE epilogue      -> bf16 q | k | v
     attn     q8_attn_decode_append (k, v appended at row t - 1)   -> fp32 [12][128]
     o        q8_gemm_fused  F32 prologue, ADD epilogue            -> h += o(attn)
+             (contexts up to 1024 rows: q8_attn_decode_append_partials leaves the
+             chunk partials and q8_gemm_attn_residual combines them in its
+             prologue -- one launch fewer, the same bits)
     gate_up  q8_gemm_fused  RMSNORM prologue, SWIGLU epilogue     -> bf16 s
     down     q8_gemm_fused  BF16 prologue, ADD epilogue           -> h += down(s)
     (end of a module run: q8_rmsnorm(h) in place)
@@ -31,6 +34,7 @@ import int8_weight_streaming_amd as q8
 
 HEADS = 12
 HEAD_DIM = 128
+FOLD_MAX_T = 1024          # contexts whose attention combine q8_gemm_attn_residual takes over
 
 
 class DecodeStep:
@@ -41,7 +45,8 @@ class DecodeStep:
     module_ends: the virtual layers after which the module-final norm runs;
     t_cap: cache rows per virtual layer."""
 
-    def __init__(self, weights, lm_head, order, module_ends, t_cap: int, rope_perm, swiglu_perm):
+    def __init__(self, weights, lm_head, order, module_ends, t_cap: int, rope_perm, swiglu_perm,
+                 fold_combine: bool = True):
         dev = lm_head[0].device
         self.order = list(order)
         self.module_ends = set(module_ends)
@@ -69,13 +74,18 @@ class DecodeStep:
         self.s = torch.empty((1, inter), dtype=torch.uint16, device=dev)
         self.logits = torch.empty((1, lm_head[0].shape[0]), dtype=torch.float32, device=dev)
         self.work = torch.empty((max(1, q8.attn_work_words(HEADS, t_cap)),), dtype=torch.float32, device=dev)
+        self.fold = fold_combine
+        self.pwork = torch.empty((q8.attn_partial_words(HEADS, min(t_cap, FOLD_MAX_T)),), dtype=torch.float32,
+                                 device=dev)
         self.scale = 1.0 / math.sqrt(HEAD_DIM)
 
     def run(self, t: int, hook=None):
         """Issue one step for the token at position t - 1 (context t, 1 <= t <=
         t_cap) on the current stream, reading and updating self.h.  hook(stage,
         v), if given, is called after every operation (for checking; not under
-        graph capture)."""
+        graph capture; the "attn" stage only where the attention output is
+        formed, i.e. not when the combine is folded into the o product)."""
+        fold = self.fold and t <= FOLD_MAX_T
         hidden = self.h.shape[1]
         q = self.qkv[0, :hidden].view(HEADS, HEAD_DIM)
         knew = self.qkv[0, hidden:2 * hidden].view(HEADS, HEAD_DIM)
@@ -85,11 +95,16 @@ class DecodeStep:
             q8.gemm_fused(wq, wd, self.h, q8.PRO_RMSNORM, q8.EPI_ROPE, out=self.qkv,
                           rope_rows=2 * hidden, pos=t - 1)
             hook and hook("qkv", v)
-            q8.attn_decode_append(q, self.kq[v], self.kd[v], self.vq[v], self.vd[v], t, self.scale,
-                                  knew, vnew, work=self.work, out=self.attn)
-            hook and hook("attn", v)
             wq, wd = self.w[(blk, 1)]
-            q8.gemm_fused(wq, wd, self.attn.view(1, hidden), q8.PRO_F32, q8.EPI_ADD, out=self.h)
+            if fold:
+                q8.attn_decode_append_partials(q, self.kq[v], self.kd[v], self.vq[v], self.vd[v], t, self.scale,
+                                               knew, vnew, work=self.pwork)
+                q8.gemm_attn_residual(wq, wd, self.pwork, t, self.h)
+            else:
+                q8.attn_decode_append(q, self.kq[v], self.kd[v], self.vq[v], self.vd[v], t, self.scale,
+                                      knew, vnew, work=self.work, out=self.attn)
+                hook and hook("attn", v)
+                q8.gemm_fused(wq, wd, self.attn.view(1, hidden), q8.PRO_F32, q8.EPI_ADD, out=self.h)
             hook and hook("o", v)
             wq, wd = self.w[(blk, 2)]
             q8.gemm_fused(wq, wd, self.h, q8.PRO_RMSNORM, q8.EPI_SWIGLU, out=self.s)

@@ -174,6 +174,39 @@ def test_fused_validation(lib):
     assert qf(None, 0, 64, 2, None, None, None) == OK
 
 
+def test_attn_partials_and_residual_validation(lib):
+    pw = lib.q8_attn_partial_words
+    assert pw(12, 512) == 12 * 4 * 132 and pw(12, 1) == 12 * 132 and pw(12, 4096) == 12 * 16 * 132
+    assert pw(-1, 5) == -1 and pw(2, 0) == -1
+    f = lib.q8_attn_decode_append_partials
+    need = pw(2, 200)
+    base = [A, B, A, B, A, 2, 200, 256, 128, 0.088, A, B, A, need, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a8=64) == SHAPE
+    assert call(a6=300) == SHAPE
+    assert call(a13=need - 1) == SHAPE
+    assert call(a12=None) == NULL                      # work is required (even for one chunk)
+    assert call(a10=None) == NULL
+    assert call(a12=MIS) == ALIGN
+    assert call(a5=0) == OK
+    g = lib.q8_gemm_attn_residual
+    wneed = pw(12, 512)
+    assert g(A, B, 1536, 1536, A, wneed, 512, A, None) != SHAPE
+    assert g(A, B, 1536, 1600, A, wneed, 512, A, None) == SHAPE   # k not a multiple of 128
+    assert g(A, B, 1536, 4096, A, 1 << 20, 512, A, None) == SHAPE # k > 2048
+    assert g(A, B, 1536, 1536, A, wneed, 1025, A, None) == SHAPE  # more than 8 chunks
+    assert g(A, B, 1536, 1536, A, wneed, 0, A, None) == SHAPE
+    assert g(A, B, 1536, 1536, A, wneed - 1, 512, A, None) == SHAPE
+    assert g(A, B, 1536, 1536, None, wneed, 512, A, None) == NULL
+    assert g(A, B, 1536, 1536, A, wneed, 512, MIS, None) == ALIGN
+    assert g(None, None, 0, 1536, None, wneed, 512, None, None) == OK
+
+
 def test_attn_append_validation(lib):
     f = lib.q8_attn_decode_append
     need = lib.q8_attn_work_words(2, 200)
@@ -218,9 +251,9 @@ def test_probe_validation(lib):
 def test_attn_validation(lib):
     f = lib.q8_attn_decode                                 # prototype set by load_library()
     need = lib.q8_attn_work_words(2, 200)
-    assert need == 2 * 2 * 130
+    assert need == 2 * 2 * 132
     assert lib.q8_attn_work_words(12, 128) == 0
-    assert lib.q8_attn_work_words(12, 4096) == 12 * 32 * 130
+    assert lib.q8_attn_work_words(12, 4096) == 12 * 32 * 132
     assert lib.q8_attn_work_words(1, 0) == -1
     args = lambda **kw: dict(dict(q=A, kq=B, kd=A, vq=B, vd=A, heads=2, t=200, t_cap=256, d=128,
                                   scale=0.088, out=A, work=B, words=need), **kw)

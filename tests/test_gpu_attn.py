@@ -182,3 +182,31 @@ def test_attn_rejects_bad_arguments():
     assert e.value.status == 2
     with pytest.raises(q8.Q8Error):
         q8.attn_decode(dq, dkq, dkd, dvq, dvd, 0, SCALE)
+
+
+@pytest.mark.parametrize("t", [1, 100, 128, 129, 512, 1000, 1024])
+def test_partials_and_folded_combine_match_two_launches(t):
+    """attn_decode_append_partials + gemm_attn_residual (the combine done in the
+    o product's prologue) give bit for bit the residual of attn_decode_append
+    followed by the fp32-prologue product with the residual add, and the same
+    cache rows."""
+    heads, t_cap, n = 12, 1024, 1536
+    log(f"attn partials + folded combine t={t}")
+    q, kq, kd, vq, vd = cache(9900 + t, heads, t_cap, t_cap)
+    g = wl.rng(9901 + t)
+    knew = to_dev(wl.f32_to_bf16_bits(g.standard_normal((heads, D)).astype(np.float32)))
+    vnew = to_dev(wl.f32_to_bf16_bits(g.standard_normal((heads, D)).astype(np.float32)))
+    wq, wd = q8.quantize_weights(to_dev(wl.normal_weights(9902, n, heads * D)))
+    h0 = to_dev(g.standard_normal((1, n)).astype(np.float32))
+    c1 = [to_dev(a) for a in (q, kq, kd, vq, vd)]
+    c2 = [to_dev(a) for a in (q, kq, kd, vq, vd)]
+    h1, h2 = h0.clone(), h0.clone()
+    a = q8.attn_decode_append(*c1, t, SCALE, knew, vnew)
+    q8.gemm_fused(wq, wd, a.view(1, -1), q8.PRO_F32, q8.EPI_ADD, out=h1)
+    work = torch.full((q8.attn_partial_words(heads, t),), float("nan"), dtype=torch.float32, device=DEV)
+    q8.attn_decode_append_partials(*c2, t, SCALE, knew, vnew, work=work)
+    q8.gemm_attn_residual(wq, wd, work, t, h2)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
+    for x1, x2 in zip(c1, c2):
+        assert torch.equal(x1, x2)

@@ -59,7 +59,7 @@ def test_reduced_step_op_by_op():
             dev_w[(blk, proj)] = (to_dev(wq), to_dev(wd))
     lq, ld = oracle.quantize_f32(wl.normal_weights(wl.LM_HEAD_SEED, vocab, wl.HIDDEN))
     rp, sp = _perms()
-    st = DecodeStep(dev_w, (to_dev(lq), to_dev(ld)), order, module_ends, t_cap, rp, sp)
+    st = DecodeStep(dev_w, (to_dev(lq), to_dev(ld)), order, module_ends, t_cap, rp, sp, fold_combine=False)
     # a context of t - 1 cached rows per virtual layer
     g = wl.rng(77)
     for v in range(len(order)):
@@ -177,3 +177,36 @@ def test_full_step_graph_replay_bitwise():
         torch.cuda.synchronize()
         assert torch.equal(st.logits, ref)
         assert torch.equal(st.kq, ref_k)
+
+
+@pytest.mark.parametrize("t", [1, 129, 300, 1024])
+def test_folded_combine_same_bits(t):
+    """The step with the attention combine folded into the o product
+    (contexts up to 1024 rows) gives the same bits -- residual stream, caches,
+    logits -- as the step with the separate combine launch."""
+    blocks, vocab, t_cap = 2, 4096, 1100
+    order, module_ends = [0, 1, 0, 1], [1, 3]
+    dev_w = {}
+    for blk in range(blocks):
+        for proj, (_, n, k) in enumerate(wl.BLOCK_SHAPES):
+            dev_w[(blk, proj)] = q8.quantize_weights(to_dev(wl.normal_weights(wl.mimir_weight_seed(blk, proj), n, k)))
+    lm = q8.quantize_weights(to_dev(wl.normal_weights(wl.LM_HEAD_SEED, vocab, wl.HIDDEN)))
+    rp, sp = _perms()
+    steps = [DecodeStep(dev_w, lm, order, module_ends, t_cap, rp, sp, fold_combine=f) for f in (False, True)]
+    g = wl.rng(500 + t)
+    kq = torch.from_numpy(g.integers(-127, 128, size=(len(order), HEADS, t_cap, HEAD_DIM), dtype=np.int8)).to(DEV)
+    kd = to_dev((g.random((len(order), HEADS, t_cap, HEAD_DIM // 32)) * 0.02 + 0.005).astype(np.float16).view(np.uint16))
+    h0 = to_dev(g.standard_normal((1, wl.HIDDEN)).astype(np.float32))
+    for st in steps:
+        for c in (st.kq, st.vq):
+            c.copy_(kq)
+        for c in (st.kd, st.vd):
+            c.copy_(kd)
+        st.h.copy_(h0)
+        st.run(t)
+        st.run(t + 1)
+    torch.cuda.synchronize()
+    a, b = steps
+    assert torch.equal(a.h, b.h) and torch.equal(a.logits, b.logits)
+    assert torch.equal(a.kq, b.kq) and torch.equal(a.kd, b.kd) and torch.equal(a.vq, b.vq) and torch.equal(a.vd, b.vd)
+    assert torch.isfinite(a.logits).all()
