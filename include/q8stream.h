@@ -213,7 +213,7 @@ q8_status q8_attn_decode_append_partials(const uint16_t* q, int8_t* kq, uint16_t
  * `work` for the same (heads = k / 128, t), exactly as q8_attn_decode combines
  * them (bit for bit).  wq/wd Q8_0 [n][k]; h fp32 [n], read and written.  k a
  * multiple of 128 with 128 <= k <= 2048 (the row is combined once per
- * workgroup); 1 <= t <= 1024 (at most 8 chunks of cache rows); work_words at
+ * workgroup); 1 <= t <= 4096 (at most 16 chunks of cache rows); work_words at
  * least q8_attn_partial_words(k / 128, t); Q8_ERR_SHAPE otherwise.  Other
  * conventions as q8_gemm_fused with Q8_EPI_ADD at m = 1. */
 q8_status q8_gemm_attn_residual(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, const float* work,

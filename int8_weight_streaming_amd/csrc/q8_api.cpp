@@ -366,8 +366,8 @@ q8_status q8_gemm_attn_residual(const int8_t* wq, const uint16_t* wd, int64_t n,
                                 int64_t work_words, int64_t t, float* h, hipStream_t stream) {
     if (k < 128 || k % 128 != 0 || k > 2048) return Q8_ERR_SHAPE;
     Q8_TRY(check_rows(n, k));
-    if (t < 1 || t > 1024) return Q8_ERR_SHAPE;
-    const int64_t chunks = q8::attn_split_chunks(t);
+    if (t < 1 || t > 4096) return Q8_ERR_SHAPE;
+    const int64_t chunks = q8::attn_split_chunks(t);       // <= 16
     if (work_words < q8::attn_partial_floats(k / 128, t)) return Q8_ERR_SHAPE;
     if (n == 0) return Q8_OK;
     if (!wq || !wd || !work || !h) return Q8_ERR_NULL;

@@ -86,6 +86,17 @@ hipError_t launch_fused(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t
     return hipErrorInvalidValue;
 }
 
+template <int PRO>
+static hipError_t attn_residual_pro(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int nb,
+                                    const float* work, float* y, const FuseArgs& fa, const DeviceInfo& dev,
+                                    hipStream_t stream) {
+    const int64_t tall_wgs = (n + 31) / 32;
+    if (tall_wgs >= (int64_t)dev.cu_count && k <= 16 * 6 * 16)
+        return fused_cfg<1, 16, 2, 6, PRO, kEpiAdd>(wq, wd, n, nb, work, y, fa, stream);
+    if (nb <= 48) return fused_cfg<1, 32, 1, 3, PRO, kEpiAdd>(wq, wd, n, nb, work, y, fa, stream);
+    return fused_cfg<1, 32, 1, 8, PRO, kEpiAdd>(wq, wd, n, nb, work, y, fa, stream);
+}
+
 // The output projection reading the attention partials directly (batch 1,
 // residual add): the prologue combines the row once per workgroup, so the
 // whole row must fit one K tile -- only such shapes are used.
@@ -94,11 +105,8 @@ hipError_t launch_attn_residual(const int8_t* wq, const uint16_t* wd, int64_t n,
     (void)hipGetLastError();
     const int nb = (int)(k / 32);
     const FuseArgs fa{0, 0, nchunks};
-    const int64_t tall_wgs = (n + 31) / 32;
-    if (tall_wgs >= (int64_t)dev.cu_count && k <= 16 * 6 * 16)
-        return fused_cfg<1, 16, 2, 6, kProAttn, kEpiAdd>(wq, wd, n, nb, work, y, fa, stream);
-    if (nb <= 48) return fused_cfg<1, 32, 1, 3, kProAttn, kEpiAdd>(wq, wd, n, nb, work, y, fa, stream);
-    return fused_cfg<1, 32, 1, 8, kProAttn, kEpiAdd>(wq, wd, n, nb, work, y, fa, stream);
+    if (nchunks <= 8) return attn_residual_pro<kProAttn>(wq, wd, n, k, nb, work, y, fa, dev, stream);
+    return attn_residual_pro<kProAttn16>(wq, wd, n, k, nb, work, y, fa, dev, stream);
 }
 
 // ------------------------------------------------------------------ RMSNorm

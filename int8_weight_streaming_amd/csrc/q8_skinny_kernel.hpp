@@ -14,7 +14,7 @@ namespace q8 {
 // default rotary embedding (theta 10,000) on the query and key rows, SwiGLU
 // between the gate/up and down products, residual adds after the output and
 // down products].
-enum { kProBf16 = 0, kProF32 = 1, kProNorm = 2, kProAttn = 3 };
+enum { kProBf16 = 0, kProF32 = 1, kProNorm = 2, kProAttn = 3, kProAttn16 = 4 };
 enum { kEpiF32 = 0, kEpiAdd = 1, kEpiSwiglu = 2, kEpiRope = 3 };
 constexpr float kRmsEps = 1e-6f;
 constexpr double kRopeTheta = 10000.0;
@@ -124,15 +124,15 @@ __device__ __forceinline__ void stage_load(const float* x, int64_t k, float4 v[M
 // as the attention's own combine does it:
 //   a[h][d] = sum_c o_c[d] e^(m_c - M) / sum_c l_c e^(m_c - M),  M = max_c m_c,
 // the sums in chunk order.  Thread t takes values 8t .. 8t + 7 (head t / 16);
-// all partials of up to kAttnCombine chunks are fetched at once (indices past
-// the last chunk repeat it and get weight zero).
-constexpr int kAttnCombine = 8;
-__device__ __forceinline__ void attn_parts_load(const float* w, int64_t k, int nchunks,
-                                                float4 ao[kAttnCombine][2], float2 aml[kAttnCombine]) {
+// all partials of up to NC chunks (8, or 16 for kProAttn16) are fetched at once
+// (indices past the last chunk repeat it and get weight zero).
+template <int NC>
+__device__ __forceinline__ void attn_parts_load(const float* w, int64_t k, int nchunks, float4 ao[NC][2],
+                                                float2 aml[NC]) {
     const int t = 8 * (int64_t)threadIdx.x < k ? (int)threadIdx.x : 0;
     const int h = t >> 4, d0 = (8 * t) & 127;
 #pragma unroll
-    for (int c = 0; c < kAttnCombine; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const int cc = c < nchunks ? c : nchunks - 1;
         const float* part = w + ((int64_t)h * nchunks + cc) * kAttnPartFloats;
         ao[c][0] = *reinterpret_cast<const float4*>(part + d0);
@@ -140,16 +140,17 @@ __device__ __forceinline__ void attn_parts_load(const float* w, int64_t k, int n
         aml[c] = *reinterpret_cast<const float2*>(part + 128);
     }
 }
-__device__ __forceinline__ void attn_combine(const float4 ao[kAttnCombine][2], const float2 aml[kAttnCombine],
-                                             int nchunks, float4 out[2]) {
+template <int NC>
+__device__ __forceinline__ void attn_combine(const float4 ao[NC][2], const float2 aml[NC], int nchunks,
+                                             float4 out[2]) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < kAttnCombine; ++c) mx = fmaxf(mx, aml[c].x);
+    for (int c = 0; c < NC; ++c) mx = fmaxf(mx, aml[c].x);
     float num[8], den = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) num[e] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kAttnCombine; ++c) {
+    for (int c = 0; c < NC; ++c) {
         if (c < nchunks) {                       // uniform
             const float e = expf(aml[c].x - mx);
             const float v[8] = {ao[c][0].x, ao[c][0].y, ao[c][0].z, ao[c][0].w,
@@ -292,11 +293,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
     constexpr bool RS = PRO != kProBf16 && M <= 2;
     const bool rstage = RS && k <= kStageK && k <= (int64_t)TCH * 16;
     float4 sv[RS ? M : 1][2];
-    constexpr bool AT = PRO == kProAttn;
+    constexpr bool AT = PRO == kProAttn || PRO == kProAttn16;
+    constexpr int NC = PRO == kProAttn16 ? 16 : 8;           // chunks the prologue combines
     static_assert(!AT || M == 1, "the attention prologue is a batch-1 prologue");
-    float4 ao[AT ? kAttnCombine : 1][2];
-    float2 aml[AT ? kAttnCombine : 1];
-    if constexpr (AT) attn_parts_load(static_cast<const float*>(xv), k, (int)fa.attn_chunks, ao, aml);
+    float4 ao[AT ? NC : 1][2];
+    float2 aml[AT ? NC : 1];
+    if constexpr (AT) attn_parts_load<NC>(static_cast<const float*>(xv), k, (int)fa.attn_chunks, ao, aml);
     else if constexpr (RS) stage_load<M>(static_cast<const float*>(xv), k, sv);
 
     const int8_t* wrow[R];
@@ -399,14 +401,14 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
         if constexpr (AT) {
             // the attention partials: combined now, after the weight loads are issued
 #pragma unroll
-            for (int c = 0; c < kAttnCombine; ++c) {
+            for (int c = 0; c < NC; ++c) {
                 pin(aml[c].x); pin(aml[c].y);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     pin(ao[c][h].x); pin(ao[c][h].y); pin(ao[c][h].z); pin(ao[c][h].w);
                 }
             }
-            attn_combine(ao, aml, (int)fa.attn_chunks, sv[0]);
+            attn_combine<NC>(ao, aml, (int)fa.attn_chunks, sv[0]);
         } else if constexpr (RS) {
             // staged rows: wanted only now, after the weight loads are issued
             if (rstage) {

@@ -199,7 +199,7 @@ def test_attn_partials_and_residual_validation(lib):
     assert g(A, B, 1536, 1536, A, wneed, 512, A, None) != SHAPE
     assert g(A, B, 1536, 1600, A, wneed, 512, A, None) == SHAPE   # k not a multiple of 128
     assert g(A, B, 1536, 4096, A, 1 << 20, 512, A, None) == SHAPE # k > 2048
-    assert g(A, B, 1536, 1536, A, wneed, 1025, A, None) == SHAPE  # more than 8 chunks
+    assert g(A, B, 1536, 1536, A, 1 << 20, 4097, A, None) == SHAPE  # more than 16 chunks
     assert g(A, B, 1536, 1536, A, wneed, 0, A, None) == SHAPE
     assert g(A, B, 1536, 1536, A, wneed - 1, 512, A, None) == SHAPE
     assert g(A, B, 1536, 1536, None, wneed, 512, A, None) == NULL

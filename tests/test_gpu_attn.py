@@ -184,13 +184,13 @@ def test_attn_rejects_bad_arguments():
         q8.attn_decode(dq, dkq, dkd, dvq, dvd, 0, SCALE)
 
 
-@pytest.mark.parametrize("t", [1, 100, 128, 129, 512, 1000, 1024])
+@pytest.mark.parametrize("t", [1, 100, 128, 129, 512, 1000, 1024, 1025, 2048, 2049, 3001, 4096])
 def test_partials_and_folded_combine_match_two_launches(t):
     """attn_decode_append_partials + gemm_attn_residual (the combine done in the
     o product's prologue) give bit for bit the residual of attn_decode_append
     followed by the fp32-prologue product with the residual add, and the same
     cache rows."""
-    heads, t_cap, n = 12, 1024, 1536
+    heads, t_cap, n = 12, 4096, 1536
     log(f"attn partials + folded combine t={t}")
     q, kq, kd, vq, vd = cache(9900 + t, heads, t_cap, t_cap)
     g = wl.rng(9901 + t)

@@ -179,12 +179,12 @@ def test_full_step_graph_replay_bitwise():
         assert torch.equal(st.kq, ref_k)
 
 
-@pytest.mark.parametrize("t", [1, 129, 300, 1024])
+@pytest.mark.parametrize("t", [1, 129, 300, 1024, 2048, 4095])
 def test_folded_combine_same_bits(t):
     """The step with the attention combine folded into the o product
-    (contexts up to 1024 rows) gives the same bits -- residual stream, caches,
+    (contexts up to 4096 rows) gives the same bits -- residual stream, caches,
     logits -- as the step with the separate combine launch."""
-    blocks, vocab, t_cap = 2, 4096, 1100
+    blocks, vocab, t_cap = 2, 4096, 4100
     order, module_ends = [0, 1, 0, 1], [1, 3]
     dev_w = {}
     for blk in range(blocks):
