@@ -190,41 +190,48 @@ def bench_gemv_1536(q8, wl, dev, copies: int = 256, iters: int = 2000) -> dict:
     return out
 
 
-def bench_q4_lm_head(q8, wl, dev, w, m_list=(1, 2, 4, 8), per_graph: int = 20, reps: int = 10) -> dict:
-    """The lm_head shape in int4 (262144 x 1536, 226 MB per copy), two copies
-    alternated so no call finds its weights in cache; graph-replayed, HIP events
-    on the launch stream."""
+def bench_lm_head_batches(q8, wl, dev, w, q8_copies, m_list=(1, 2, 4, 8), per_graph: int = 20,
+                          reps: int = 10) -> dict:
+    """The lm_head shape (262144 x 1536) at batch 1/2/4/8 with bf16 and with Q8
+    activations, in int4 (226 MB per copy) and in Q8_0 (429 MB per copy, the
+    headline's two copies), in the same run; two copies alternated so no call
+    finds its weights in cache; graph-replayed, HIP events on the launch
+    stream.  Returns {"int4": {...}, "q8_0": {...}}."""
     import torch
     cfg = wl.CONFIGS["lm_head_gemv_262144x1536_b1"]
     n, k = w.shape
-    copies = [q8.q4_quantize_weights(w)]
-    copies.append((copies[0][0].clone(), copies[0][1].clone()))
-    out = {}
-    for act in ("bf16", "q8"):
-        for m in m_list:
-            xb = wl.rms_unit_act_bf16(cfg["x_seed"], k) if m == 1 else wl.normal_act_bf16(9800 + m, m, k)
-            x = to_dev(xb, dev)
-            xa = (x,) if act == "bf16" else q8.quantize_act(x)
-            y = torch.empty((m, n), dtype=torch.float32, device=dev)
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s):
-                for i in range(4):
-                    q8.q4_gemm_skinny(*copies[i & 1], *xa, out=y)
-            torch.cuda.current_stream().wait_stream(s)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(per_graph):
-                    q8.q4_gemm_skinny(*copies[i & 1], *xa, out=y)
-            g.replay()
-            torch.cuda.synchronize()
-            ms, _ = time_events(lambda i: g.replay(), reps)
-            us = ms * 1e3 / per_graph
-            nbytes = q4_gemv_bytes(n, k, m) - (m * k if act == "q8" else 0) + (m * k // 16 if act == "q8" else 0)
-            out[f"{act}_b{m}"] = {"us_per_call": us, "bytes_per_call": nbytes, "GBps": nbytes / us / 1e3,
-                                  "frac_hbm_peak": nbytes / us / 1e3 / HBM_PEAK_GBPS,
-                                  "weights_per_s": n * k / us * 1e6}
-            log(f"int4 lm_head {act} m={m}: {us:.2f} us, {nbytes / us / 1e3:.0f} GB/s")
+    q4_copies = [q8.q4_quantize_weights(w)]
+    q4_copies.append((q4_copies[0][0].clone(), q4_copies[0][1].clone()))
+    out = {"int4": {}, "q8_0": {}}
+    for fmt, copies, fn, wbytes in (("int4", q4_copies, q8.q4_gemm_skinny, lambda m: q4_gemv_bytes(n, k, m)),
+                                    ("q8_0", q8_copies, q8.gemm_skinny, lambda m: gemv_bytes(n, k, m))):
+        for act in ("bf16", "q8"):
+            for m in m_list:
+                xb = wl.rms_unit_act_bf16(cfg["x_seed"], k) if m == 1 else wl.normal_act_bf16(9800 + m, m, k)
+                x = to_dev(xb, dev)
+                xa = (x,) if act == "bf16" else q8.quantize_act(x)
+                y = torch.empty((m, n), dtype=torch.float32, device=dev)
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    for i in range(4):
+                        fn(*copies[i & 1], *xa, out=y)
+                torch.cuda.current_stream().wait_stream(s)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(per_graph):
+                        fn(*copies[i & 1], *xa, out=y)
+                g.replay()
+                torch.cuda.synchronize()
+                ms, _ = time_events(lambda i: g.replay(), reps)
+                us = ms * 1e3 / per_graph
+                nbytes = wbytes(m) - (m * k if act == "q8" else 0) + (m * k // 16 if act == "q8" else 0)
+                out[fmt][f"{act}_b{m}"] = {"us_per_call": us, "bytes_per_call": nbytes,
+                                           "GBps": nbytes / us / 1e3,
+                                           "frac_hbm_peak": nbytes / us / 1e3 / HBM_PEAK_GBPS,
+                                           "weights_per_s": n * k / us * 1e6}
+                log(f"{fmt} lm_head {act} m={m}: {us:.2f} us, {nbytes / us / 1e3:.0f} GB/s")
+                del g
     return out
 
 
@@ -630,9 +637,9 @@ def main() -> int:
     oq, od = oracle.quantize_f32(w_np)
     q4_lm = None
     if not args.metric_only:
-        log("int4 lm_head products")
+        log("lm_head products at batch 1-8, int4 and Q8_0")
         w_dev = to_dev(w_np, dev)
-        q4_lm = bench_q4_lm_head(q8, wl, dev, w_dev)
+        q4_lm = bench_lm_head_batches(q8, wl, dev, w_dev, copies)
         del w_dev
         torch.cuda.empty_cache()
     del w_np
@@ -653,7 +660,7 @@ def main() -> int:
     log(f"copy probe: {extras['copy_probe']['GBps_read_plus_write']:.1f} GB/s (read + write)")
 
     if q4_lm is not None:
-        extras["q4_lm_head"] = q4_lm
+        extras["lm_head_batches"] = q4_lm
     if not args.metric_only:
         log("gemv 1536x1536")
         extras["gemv_1536x1536_b1"] = bench_gemv_1536(q8, wl, dev)
