@@ -210,3 +210,31 @@ def test_partials_and_folded_combine_match_two_launches(t):
     assert torch.equal(h1, h2)
     for x1, x2 in zip(c1, c2):
         assert torch.equal(x1, x2)
+
+
+@pytest.mark.parametrize("heads,n,t", [(2, 300, 5), (2, 300, 700), (16, 4096, 900), (16, 4096, 3000)])
+def test_folded_combine_other_widths(heads, n, t):
+    """The folded combine for other head counts: 2 heads (k = 256) with a
+    ragged number of output rows, and 16 heads (k = 2048, the widest row, a
+    256-chunk K tile), against the two-launch form, bit for bit."""
+    t_cap, k = 4096, heads * D
+    log(f"folded combine heads={heads} n={n} t={t}")
+    q, kq, kd, vq, vd = cache(9950 + heads + t, heads, t_cap, t_cap)
+    g = wl.rng(9951 + t)
+    knew = to_dev(wl.f32_to_bf16_bits(g.standard_normal((heads, D)).astype(np.float32)))
+    vnew = to_dev(wl.f32_to_bf16_bits(g.standard_normal((heads, D)).astype(np.float32)))
+    wq, wd = q8.quantize_weights(to_dev(wl.normal_weights(9952 + heads, n, k)))
+    h0 = to_dev(g.standard_normal((1, n)).astype(np.float32))
+    c1 = [to_dev(a) for a in (q, kq, kd, vq, vd)]
+    c2 = [to_dev(a) for a in (q, kq, kd, vq, vd)]
+    h1, h2 = h0.clone(), h0.clone()
+    a = q8.attn_decode_append(*c1, t, SCALE, knew, vnew)
+    q8.gemm_fused(wq, wd, a.view(1, -1), q8.PRO_F32, q8.EPI_ADD, out=h1)
+    work = q8.attn_decode_append_partials(*c2, t, SCALE, knew, vnew)
+    q8.gemm_attn_residual(wq, wd, work, t, h2)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
+    # and against the oracle: the product of the bf16 attention output
+    ref = h0.cpu().numpy().astype(np.float64) + oracle.w8a16(to_host(wq), to_host(wd),
+                                                              wl.f32_to_bf16_bits(to_host(a).reshape(1, -1)))
+    assert_close(to_host(h2), ref, f"folded combine heads={heads} t={t}")
