@@ -4,9 +4,13 @@
  * The library computes the int8 weight-streaming hot path of LLM decode and
  * prefill: block quantization of weights and activations, the batch-1..8
  * matrix-vector / skinny products over int8 weights, the Q8 x Q8 prefill
- * product, decode attention over a Q8_0 key/value cache, and the int4-weight
- * variant of the quantizer and the batch-1..8 products.  Every call is a
- * hand-written HIP kernel enqueued on the caller's stream.
+ * product, decode attention over a Q8_0 key/value cache, the int4-weight
+ * variant of the quantizer and the batch-1..8 products, and the glue of a
+ * decode block fused into those calls (RMSNorm, rotary embedding, SwiGLU and
+ * residual prologues/epilogues; attention that appends its key/value row; the
+ * attention combine inside the output projection; the prefill activation side
+ * in one launch).  Every call is a hand-written HIP kernel enqueued on the
+ * caller's stream.
  *
  * Format (Q8_0) [fak MODEL-BASELINE-RESULTS, ACT 3, "How it was closed",
  * item 1]: a row of K values (K % 32 == 0) is cut into K/32 blocks of 32
