@@ -270,36 +270,42 @@ __global__ __launch_bounds__(256) void prefill_stream_kernel(const int8_t* __res
     for (int j = 0; j < 4; ++j) voff[j] = (8 * j + cr) * (int)k + cb;
     const int soffA = pl * nb * 2, soffB = i * nb * 2;
 
-    // fetch cursor: the step whose loads are issued next (wave-uniform)
+    // fetch cursor: the step whose loads are issued next (wave-uniform).  The
+    // four buffer descriptors cover the cursor's tile (its rows of codes and
+    // scales from column 0; an empty range once the workgroup's tiles are
+    // done) and are rebuilt only when the cursor enters the next tile; a step
+    // is addressed by the scalar offset of its first block, which stays below
+    // the row length, so rows past the matrix read zero either way.
     int fs = 0, ft = 0, fm = jw;
-    int fp0 = (fm % ntp) * 32, fn0 = (tn_lo + fm / ntp) * 32;
-    auto issue = [&](StreamStage& st) {
+    __amdgpu_buffer_rsrc_t rA, rB, rsA, rsB;
+    auto enter_tile = [&]() {
         const bool live = ft < T;
-        const int blk0 = wave * 4 * S + 4 * fs;
-        const int64_t adv = (int64_t)blk0 * 32;
+        const int fp0 = (fm % ntp) * 32, fn0 = (tn_lo + fm / ntp) * 32;
         // ranges below 2^31 (rows <= 32, K <= 2^24): 32-bit range arithmetic
         const int pv = (int)(p - fp0 < 32 ? p - fp0 : 32);
         const int nv = (int)(n - fn0 < 32 ? n - fn0 : 32);
-        const int64_t ra = live ? (int64_t)fp0 * k + adv : 0, rb = live ? (int64_t)fn0 * k + adv : 0;
-        const int64_t rsa = live ? (int64_t)fp0 * nb + blk0 : 0, rsb = live ? (int64_t)fn0 * nb + blk0 : 0;
-        const int kk = (int)k, ad = (int)adv;
-        const auto rA = range_rsrc32(xq + ra, live ? pv * kk - ad : 0);
-        const auto rB = range_rsrc32(wq + rb, live ? nv * kk - ad : 0);
-        const auto rsA = range_rsrc32(xd + rsa, live ? (pv * nb - blk0) * 2 : 0);
-        const auto rsB = range_rsrc32(wd + rsb, live ? (nv * nb - blk0) * 2 : 0);
+        const int kk = (int)k;
+        rA = range_rsrc32(xq + (live ? (int64_t)fp0 * k : 0), live ? pv * kk : 0);
+        rB = range_rsrc32(wq + (live ? (int64_t)fn0 * k : 0), live ? nv * kk : 0);
+        rsA = range_rsrc32(xd + (live ? (int64_t)fp0 * nb : 0), live ? pv * nb * 2 : 0);
+        rsB = range_rsrc32(wd + (live ? (int64_t)fn0 * nb : 0), live ? nv * nb * 2 : 0);
+    };
+    enter_tile();
+    auto issue = [&](StreamStage& st) {
+        const int blk0 = wave * 4 * S + 4 * fs;
+        const int so = blk0 * 32, ss = blk0 * 2;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            st.a[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff[j], 0, 0));
-            st.b[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, voff[j], 0, 0));
+            st.a[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff[j], so, 0));
+            st.b[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, voff[j], so, 0));
         }
-        st.sa = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rsA, soffA, 0, 0));
-        st.sb = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rsB, soffB, 0, 0));
+        st.sa = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rsA, soffA, ss, 0));
+        st.sb = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rsB, soffB, ss, 0));
         if (++fs == S) {
             fs = 0;
             ++ft;
             fm += gx;
-            fp0 = (fm % ntp) * 32;
-            fn0 = (tn_lo + fm / ntp) * 32;
+            enter_tile();
         }
     };
 
@@ -317,7 +323,8 @@ __global__ __launch_bounds__(256) void prefill_stream_kernel(const int8_t* __res
     // step q + 1 (scheduling barriers keep every load in issue order, so the
     // compiler's counted waits stay exact), then multiply step q.  LDS
     // operations of one wave stay in order, so the previous step's reads are
-    // done before this write.
+    // done before this write.  (Two or three steps in flight measured slower
+    // at every P: the kernel is not waiting on memory.)
     StreamStage st;
     issue(st);
     for (int q = 0; q < Q; ++q) {
