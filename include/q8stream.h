@@ -170,7 +170,7 @@ q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m,
  * [heads][128].  head_dim must be 128 (Q8_ERR_SHAPE otherwise); 1 <= t <= t_cap
  * <= 2^24 - 128; heads <= 65536 (0 is a no-op); scale finite.
  * `work`: caller-owned fp32 workspace of at least q8_attn_work_words(heads, t)
- * words (0 when t <= 128, and then `work` may be NULL); its contents on entry
+ * words (0 when t <= 64, and then `work` may be NULL); its contents on entry
  * do not matter and are overwritten.  Rows past t are never read.  fp32
  * accumulation; results are bitwise reproducible for a given (heads, t). */
 q8_status q8_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd,
@@ -178,7 +178,9 @@ q8_status q8_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd
                          int64_t t_cap, int64_t head_dim, float scale, float* out,
                          float* work, int64_t work_words, hipStream_t stream);
 
-/* Workspace words q8_attn_decode needs for (heads, t); -1 when out of range. */
+/* Workspace words q8_attn_decode needs for (heads, t), enough for every context
+ * up to t (the count never decreases with t, so a workspace sized for t_cap
+ * serves every call on that cache); -1 when out of range. */
 int64_t q8_attn_work_words(int64_t heads, int64_t t);
 
 /* Decode attention that first appends the token's own key and value: knew and
@@ -200,7 +202,8 @@ q8_status q8_attn_decode_append(const uint16_t* q, int8_t* kq, uint16_t* kd, int
  * 132 floats: the numerator sum_j e^(s_j - m) V_j [128], the chunk's largest
  * score m, the denominator sum_j e^(s_j - m), 2 unused -- are left in `work`
  * (also when one chunk covers the context); nothing else is written.  work:
- * fp32, at least q8_attn_partial_words(heads, t) words (-1 when out of range).
+ * fp32, at least q8_attn_partial_words(heads, t) words (-1 when out of range;
+ * like q8_attn_work_words it covers every context up to t).
  * Other arguments and errors as q8_attn_decode_append, without `out`. */
 int64_t q8_attn_partial_words(int64_t heads, int64_t t);
 q8_status q8_attn_decode_append_partials(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_t* vq,

@@ -12,12 +12,13 @@
 // (an int8 KV read per decoded token)].
 //
 // The cache read is the cost (2 x 136 bytes per row and head), so the kernel
-// streams it once: a workgroup takes a chunk of 128 rows of one head (256
-// above 2048 rows of context: fewer, fuller workgroups and fewer partials to
-// combine measured faster there, slower below); each of its four waves a
-// quarter, lane l the 16-byte segment l % 8 (dimensions 16 (l % 8) .. + 15,
-// inside one Q8 block) of rows 8j + l / 8, j < RPL = 4 or 8, for K and V
-// alike, all loads issued before the first use.  A score is the bf16 dot of the query
+// streams it once: a workgroup takes a chunk of 64 rows of one head up to 512
+// rows of context, 128 up to 2048 and 256 above (more, smaller workgroups
+// measured faster at short contexts, fewer partials to combine at long ones);
+// each of its four waves a quarter, lane l the 16-byte segment l % 8
+// (dimensions 16 (l % 8) .. + 15, inside one Q8 block) of rows 8j + l / 8,
+// j < RPL = 2, 4 or 8, for K and V alike, all loads issued before the first
+// use.  A score is the bf16 dot of the query
 // segment with the exactly converted codes, times the block scale, summed over
 // the row's eight lanes by a fixed DPP tree.  The workgroup subtracts its
 // maximum score, and writes (sum_j e^(s_j - m) V_j, m, sum_j e^(s_j - m)) to a
@@ -32,22 +33,27 @@
 namespace q8 {
 
 constexpr int kAttnD = 128;                    // head dimension
-constexpr int kAttnChunk = 128;                // cache rows per workgroup (four rows per lane)
-constexpr int64_t kAttnWideFrom = 2048;        // longer contexts: 256-row chunks (eight rows per lane)
+constexpr int64_t kAttnNarrowTo = 512;         // contexts up to here: 64-row chunks (two rows per lane)
+constexpr int64_t kAttnWideFrom = 2048;        // above: 256-row chunks (eight); between: 128 (four)
 constexpr int kAttnPart = kAttnPartFloats;      // floats per (head, chunk): o[128], m, l, 2 pad (16-byte records)
 static_assert(kAttnPartFloats == kAttnD + 4, "partial record layout");
 
-int64_t attn_chunks(int64_t t) { return (t + kAttnChunk - 1) / kAttnChunk; }
+static int64_t attn_chunk_rows(int64_t t) { return t <= kAttnNarrowTo ? 64 : t <= kAttnWideFrom ? 128 : 256; }
+// chunks the split uses for context t
+int64_t attn_split_chunks(int64_t t) { return (t + attn_chunk_rows(t) - 1) / attn_chunk_rows(t); }
+// the most chunks of any context up to t (8 at 512 rows, 16 at 2048), so a
+// workspace sized for the longest context serves every shorter one
+static int64_t attn_max_chunks(int64_t t) {
+    int64_t c = attn_split_chunks(t);
+    if (t > kAttnNarrowTo && c < attn_split_chunks(kAttnNarrowTo)) c = attn_split_chunks(kAttnNarrowTo);
+    if (t > kAttnWideFrom && c < attn_split_chunks(kAttnWideFrom)) c = attn_split_chunks(kAttnWideFrom);
+    return c;
+}
 int64_t attn_work_floats(int64_t heads, int64_t t) {
-    const int64_t c = attn_chunks(t);
+    const int64_t c = attn_max_chunks(t);
     return c > 1 ? heads * c * kAttnPart : 0;
 }
-// chunks the split actually uses for context t (256-row chunks above kAttnWideFrom)
-int64_t attn_split_chunks(int64_t t) {
-    const int64_t chunk = t > kAttnWideFrom ? 2 * kAttnChunk : kAttnChunk;
-    return (t + chunk - 1) / chunk;
-}
-int64_t attn_partial_floats(int64_t heads, int64_t t) { return heads * attn_split_chunks(t) * kAttnPart; }
+int64_t attn_partial_floats(int64_t heads, int64_t t) { return heads * attn_max_chunks(t) * kAttnPart; }
 
 // Maximum over each group of 32 lanes (exact in any order).
 __device__ __forceinline__ float max32(float v) {
@@ -334,15 +340,19 @@ hipError_t launch_attn_decode(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_
                               float* work, const uint16_t* knew, const uint16_t* vnew,
                               const DeviceInfo& dev, hipStream_t stream) {
     (void)dev;
-    const bool wide = t > kAttnWideFrom;
+    const int64_t rows = attn_chunk_rows(t);
     const int nchunks = (int)attn_split_chunks(t);
+    const unsigned grid = (unsigned)(heads * nchunks);
     (void)hipGetLastError();
-    if (wide)
-        attn_split_kernel<8><<<(unsigned)(heads * nchunks), 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale,
-                                                                              nchunks, work, out, knew, vnew);
+    if (rows == 64)
+        attn_split_kernel<2><<<grid, 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale, nchunks, work, out, knew,
+                                                       vnew);
+    else if (rows == 128)
+        attn_split_kernel<4><<<grid, 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale, nchunks, work, out, knew,
+                                                       vnew);
     else
-        attn_split_kernel<4><<<(unsigned)(heads * nchunks), 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale,
-                                                                              nchunks, work, out, knew, vnew);
+        attn_split_kernel<8><<<grid, 256, 0, stream>>>(q, kq, kd, vq, vd, t, t_cap, scale, nchunks, work, out, knew,
+                                                       vnew);
     if (nchunks > 1 && out != nullptr) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

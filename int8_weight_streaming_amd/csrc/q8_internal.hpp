@@ -55,14 +55,13 @@ hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
                           const int8_t* xq, const uint16_t* xd, float* y,
                           const DeviceInfo& dev, hipStream_t stream);
 
-// Decode attention over a Q8_0 key/value cache (head dimension 128): chunks of
-// cache rows per workgroup, and the workspace floats the chunk partials need
-// (0 when one chunk covers the context).
-int64_t attn_chunks(int64_t t);
+// Decode attention over a Q8_0 key/value cache (head dimension 128): the
+// workspace floats the chunk partials of any context up to t need (0 when one
+// chunk covers every such context).
 int64_t attn_work_floats(int64_t heads, int64_t t);
-// The chunks the split uses for context t, and the floats of their partials:
-// per (head, chunk) a record of kAttnPartFloats floats (numerator [128], max,
-// denominator, padding), heads outer.
+// The chunks the split uses for context t, and the floats of the partials of
+// any context up to t: per (head, chunk) a record of kAttnPartFloats floats
+// (numerator [128], max, denominator, padding), heads outer.
 int64_t attn_split_chunks(int64_t t);
 int64_t attn_partial_floats(int64_t heads, int64_t t);
 constexpr int kAttnPartFloats = 132;

@@ -176,7 +176,10 @@ def test_fused_validation(lib):
 
 def test_attn_partials_and_residual_validation(lib):
     pw = lib.q8_attn_partial_words
-    assert pw(12, 512) == 12 * 4 * 132 and pw(12, 1) == 12 * 132 and pw(12, 4096) == 12 * 16 * 132
+    assert pw(12, 512) == 12 * 8 * 132 and pw(12, 1) == 12 * 132 and pw(12, 4096) == 12 * 16 * 132
+    # sizes cover every shorter context (8 chunks of 64 rows at 512, 16 of 128 at 2048)
+    assert pw(12, 600) == 12 * 8 * 132 and pw(12, 2049) == 12 * 16 * 132 and pw(12, 1500) == 12 * 12 * 132
+    assert all(pw(3, t) <= pw(3, t + 1) for t in range(1, 4200))
     assert pw(-1, 5) == -1 and pw(2, 0) == -1
     f = lib.q8_attn_decode_append_partials
     need = pw(2, 200)
@@ -251,9 +254,10 @@ def test_probe_validation(lib):
 def test_attn_validation(lib):
     f = lib.q8_attn_decode                                 # prototype set by load_library()
     need = lib.q8_attn_work_words(2, 200)
-    assert need == 2 * 2 * 132
-    assert lib.q8_attn_work_words(12, 128) == 0
-    assert lib.q8_attn_work_words(12, 4096) == 12 * 32 * 132
+    assert need == 2 * 4 * 132
+    assert lib.q8_attn_work_words(12, 64) == 0 and lib.q8_attn_work_words(12, 65) == 12 * 2 * 132
+    assert lib.q8_attn_work_words(12, 4096) == 12 * 16 * 132
+    assert all(lib.q8_attn_work_words(3, t) <= lib.q8_attn_work_words(3, t + 1) for t in range(1, 4200))
     assert lib.q8_attn_work_words(1, 0) == -1
     args = lambda **kw: dict(dict(q=A, kq=B, kd=A, vq=B, vd=A, heads=2, t=200, t_cap=256, d=128,
                                   scale=0.088, out=A, work=B, words=need), **kw)
@@ -271,7 +275,8 @@ def test_attn_validation(lib):
     assert call(args(kd=MIS)) == ALIGN
     assert call(args(heads=0, q=None, kq=None, kd=None, vq=None, vd=None, out=None, work=None)) == OK
     # one chunk: no workspace needed
-    assert call(args(t=100, work=None, words=0)) in (DEVICE, OK)
+    assert call(args(t=64, work=None, words=0)) in (DEVICE, OK)   # one chunk: no workspace
+    assert call(args(t=65, work=None, words=0)) == SHAPE
     import torch
     if not torch.cuda.is_available():
         assert call(args()) == DEVICE

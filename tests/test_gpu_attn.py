@@ -1,9 +1,9 @@
 """GPU parity of the decode attention over a Q8_0 key/value cache, through the
 C ABI, against the fp64 oracle (max-abs 2e-3, relative L2 1e-5 per call).
 
-Shapes cover one and several chunks with ragged ends (128-row chunks up to
-2048 rows, 256-row chunks above, and more than 32 chunks, the combine's batched
-path), the pages' static slab (capacity 4096, 12 heads of 128) at short and
+Shapes cover one and several chunks with ragged ends (64-row chunks up to
+512 rows, 128-row chunks up to 2048, 256-row chunks above, each side of both
+boundaries, and more than 32 chunks, the combine's batched path), the pages' static slab (capacity 4096, 12 heads of 128) at short and
 full context, and rows past t filled with NaN scales, so that any read past t
 would show."""
 import math
@@ -56,7 +56,8 @@ def run(q, kq, kd, vq, vd, t, scale=SCALE):
     return to_host(y)
 
 
-@pytest.mark.parametrize("heads,t,t_cap", [(1, 1, 1), (2, 5, 8), (12, 127, 128), (12, 128, 128),
+@pytest.mark.parametrize("heads,t,t_cap", [(1, 1, 1), (2, 5, 8), (12, 64, 64), (12, 65, 128), (12, 127, 128),
+                                           (12, 128, 128), (12, 511, 512), (12, 513, 1024),
                                            (12, 129, 200), (3, 1000, 1024), (5, 333, 4096),
                                            (12, 512, 4096), (12, 2048, 4096), (12, 4096, 4096),
                                            (4, 2049, 4096), (3, 3001, 4096), (2, 2300, 2400),
@@ -149,7 +150,8 @@ def test_attn_one_workspace_across_context_lengths():
         assert torch.equal(y, q8.attn_decode(dq, dkq, dkd, dvq, dvd, t, SCALE))
 
 
-@pytest.mark.parametrize("t,t_cap", [(1, 16), (128, 256), (129, 256), (200, 200), (4096, 4096), (1500, 2048),
+@pytest.mark.parametrize("t,t_cap", [(1, 16), (64, 64), (65, 100), (128, 256), (129, 256), (200, 200),
+                                     (513, 600), (4096, 4096), (1500, 2048),
                                      (2049, 2100), (2200, 4096), (3000, 3000), (9000, 9000)])
 def test_attn_append_writes_row_and_attends(t, t_cap):
     """The new key/value rows land in cache row t - 1 exactly as the activation
@@ -184,7 +186,8 @@ def test_attn_rejects_bad_arguments():
         q8.attn_decode(dq, dkq, dkd, dvq, dvd, 0, SCALE)
 
 
-@pytest.mark.parametrize("t", [1, 100, 128, 129, 512, 1000, 1024, 1025, 2048, 2049, 3001, 4096])
+@pytest.mark.parametrize("t", [1, 64, 65, 100, 128, 129, 511, 512, 513, 1000, 1024, 1025, 2048, 2049, 3001,
+                               4096])
 def test_partials_and_folded_combine_match_two_launches(t):
     """attn_decode_append_partials + gemm_attn_residual (the combine done in the
     o product's prologue) give bit for bit the residual of attn_decode_append
