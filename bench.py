@@ -190,6 +190,25 @@ def bench_gemv_1536(q8, wl, dev, copies: int = 256, iters: int = 2000) -> dict:
     return out
 
 
+def bench_quantize_weights(q8, w, reps: int = 20):
+    """The weight quantizer on the resident fp32 lm_head matrix (read 4 B,
+    write 1 B code + 1/16 B scale per weight), graph-replayed.  Returns the
+    figures and (rows, codes, scales) of 4096 sampled rows of its output, which
+    the CPU leg checks bit for bit."""
+    import torch
+    n, k = w.shape
+    wq = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    wd = torch.empty((n, k // 32), dtype=torch.uint16, device=w.device)
+    us = time_graph(lambda: q8.quantize_weights(w, out=(wq, wd)), reps) * 1e3
+    nbytes = n * k * 4 + n * k + n * (k // 32) * 2
+    rows = np.random.Generator(np.random.PCG64(78)).choice(n, size=4096, replace=False)
+    ridx = torch.as_tensor(rows, device=w.device)
+    sample = (rows, wq.index_select(0, ridx).cpu().numpy(), wd.index_select(0, ridx).cpu().numpy())
+    return ({"us_per_call": us, "bytes_per_call": nbytes, "GBps": nbytes / us / 1e3,
+             "frac_hbm_peak": nbytes / us / 1e3 / HBM_PEAK_GBPS, "weights_per_s": n * k / us * 1e6},
+            sample)
+
+
 def bench_lm_head_batches(q8, wl, dev, w, q8_copies, m_list=(1, 2, 4, 8), per_graph: int = 20,
                           reps: int = 10) -> dict:
     """The lm_head shape (262144 x 1536) at batch 1/2/4/8 with bf16 and with Q8
@@ -548,9 +567,27 @@ def bench_sync_probe(q8, dev) -> dict:
     return out
 
 
-def cpu_baseline(oracle, wl, oq, od, x, seconds: float = 10.0) -> dict:
+def cpu_baseline(w_np, x, y_rows, y_sample, wq_sample=None, seconds: float = 10.0):
+    """The CPU leg, the only use of the oracle here: it quantizes the lm_head
+    weights, checks GPU results sampled from the timed runs (the GEMV's output
+    rows within the fp32 tolerance; the weight quantizer's codes and scales bit
+    for bit), and its fp64 W8A16 GEMV is timed on the host cores.  Returns
+    (baseline, parity)."""
+    import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     oracle.set_threads(threads)
+    oq, od = oracle.quantize_f32(w_np)
+    y_ref = oracle.w8a16(oq, od, x, rows=y_rows)[0]
+    parity = {"rows_checked": int(y_rows.size),
+              "max_abs": float(np.max(np.abs(y_sample - y_ref))),
+              "rel_l2": float(np.linalg.norm(y_sample - y_ref) / np.linalg.norm(y_ref))}
+    parity["ok"] = parity["max_abs"] <= 2e-3 and parity["rel_l2"] <= 1e-5
+    if wq_sample is not None:
+        rows, q, d = wq_sample
+        exact = bool(np.array_equal(q, oq[rows]) and np.array_equal(d, od[rows]))
+        parity["weight_quantizer_rows_checked"] = int(rows.size)
+        parity["weight_quantizer_bit_exact"] = exact
+        parity["ok"] = parity["ok"] and exact
     n, k = oq.shape
     nbytes = gemv_bytes(n, k)
     times = []
@@ -560,10 +597,10 @@ def cpu_baseline(oracle, wl, oq, od, x, seconds: float = 10.0) -> dict:
         oracle.w8a16(oq, od, x)
         times.append(time.perf_counter() - t0)
     best = min(times)
-    return {"value": nbytes / best / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 oracle W8A16 GEMV over all {n} x {k} rows of the lm_head workload, "
-                      f"{len(times)} runs, best {best * 1e3:.1f} ms",
-            "host_cpus_visible": os.cpu_count()}
+    return ({"value": nbytes / best / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+             "sample": f"fp64 oracle W8A16 GEMV over all {n} x {k} rows of the lm_head workload, "
+                       f"{len(times)} runs, best {best * 1e3:.1f} ms",
+             "host_cpus_visible": os.cpu_count()}, parity)
 
 
 # ------------------------------------------------------------------ main
@@ -631,25 +668,18 @@ def main() -> int:
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     log(f"lm_head gemv: {kern_ms * 1e3:.2f} us/kernel, {achieved:.1f} GB/s kernel, {value:.1f} GB/s wall")
 
-    # sampled parity on the timed output
-    import oracle
-    oracle.set_threads(max(1, min(16, len(os.sched_getaffinity(0)))))
-    oq, od = oracle.quantize_f32(w_np)
-    q4_lm = None
+    # rows of the timed output, checked against the oracle by the CPU leg
+    y_rows = np.random.Generator(np.random.PCG64(77)).choice(n, size=4096, replace=False)
+    y_sample = y.cpu().numpy()[y_rows].astype(np.float64)
+    q4_lm = wquant = wq_sample = None
     if not args.metric_only:
         log("lm_head products at batch 1-8, int4 and Q8_0")
         w_dev = to_dev(w_np, dev)
         q4_lm = bench_lm_head_batches(q8, wl, dev, w_dev, copies)
+        wquant, wq_sample = bench_quantize_weights(q8, w_dev)
+        log(f"weight quantizer: {wquant['us_per_call']:.1f} us for {n}x{k} fp32, {wquant['GBps']:.0f} GB/s")
         del w_dev
         torch.cuda.empty_cache()
-    del w_np
-    rows = np.random.Generator(np.random.PCG64(77)).choice(n, size=4096, replace=False)
-    y_host = y.cpu().numpy()[rows].astype(np.float64)
-    y_ref = oracle.w8a16(oq, od, x_np, rows=rows)[0]
-    parity = {"rows_checked": int(rows.size),
-              "max_abs": float(np.max(np.abs(y_host - y_ref))),
-              "rel_l2": float(np.linalg.norm(y_host - y_ref) / np.linalg.norm(y_ref))}
-    parity["ok"] = parity["max_abs"] <= 2e-3 and parity["rel_l2"] <= 1e-5
 
     extras = {}
     probe = bench_read_probe(q8, dev)
@@ -661,6 +691,8 @@ def main() -> int:
 
     if q4_lm is not None:
         extras["lm_head_batches"] = q4_lm
+    if wquant is not None:
+        extras["weight_quantize_262144x1536"] = wquant
     if not args.metric_only:
         log("gemv 1536x1536")
         extras["gemv_1536x1536_b1"] = bench_gemv_1536(q8, wl, dev)
@@ -689,10 +721,11 @@ def main() -> int:
         log("decode synchronization probe")
         extras["sync_probe"] = bench_sync_probe(q8, dev)
 
-    cpu = None
+    cpu = parity = None
     if not args.metric_only and not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        cpu = cpu_baseline(oracle, wl, oq, od, x_np)
+        log("cpu baseline (oracle): sampled parity of the timed outputs, then the oracle GEMV timed")
+        cpu, parity = cpu_baseline(w_np, x_np, y_rows, y_sample, wq_sample)
+    del w_np
 
     torch.cuda.synchronize()
     # HBM traffic from the committed counter passes, only while every source
@@ -742,7 +775,7 @@ def main() -> int:
     if "mimir_step_b1" in extras:
         result["mimir_tok_s"] = round(extras["mimir_step_b1"]["tok_per_s"], 1)
     print(json.dumps(result), flush=True)
-    return 0 if parity["ok"] else 1
+    return 0 if parity is None or parity["ok"] else 1
 
 
 if __name__ == "__main__":
