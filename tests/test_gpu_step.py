@@ -184,7 +184,19 @@ def test_folded_combine_same_bits(t):
     """The step with the attention combine folded into the o product
     (contexts up to 4096 rows) gives the same bits -- residual stream, caches,
     logits -- as the step with the separate combine launch."""
-    blocks, vocab, t_cap = 2, 4096, 4100
+    _folded_same_bits(t, 4100)
+
+
+@pytest.mark.parametrize("t", [511, 512])
+def test_folded_combine_tier_boundary(t):
+    """A cache capacity between the attention's chunk tiers (600 rows: the
+    workspaces are sized once from it) and two tokens across the 512-row
+    boundary, where the chunk count drops from 8 to 5."""
+    _folded_same_bits(t, 600)
+
+
+def _folded_same_bits(t, t_cap):
+    blocks, vocab = 2, 4096
     order, module_ends = [0, 1, 0, 1], [1, 3]
     dev_w = {}
     for blk in range(blocks):
