@@ -263,7 +263,6 @@ __global__ __launch_bounds__(256) void prefill_stream_kernel(const int8_t* __res
     const int cr = lane >> 3, cb = (lane & 7) * 16;
     unsigned char* slA = lds + wave * kStreamSlice;    // [32 rows][kPitch]
     unsigned char* slB = slA + 32 * kPitch;
-    unsigned char* slS = slB + 32 * kPitch;            // [64 lanes][xd 8 B, wd 8 B]
 
     int voff[4];
 #pragma unroll
@@ -329,8 +328,8 @@ __global__ __launch_bounds__(256) void prefill_stream_kernel(const int8_t* __res
     issue(st);
     for (int q = 0; q < Q; ++q) {
         __builtin_amdgcn_sched_barrier(0);
-        *reinterpret_cast<i32x2*>(slS + lane * 16) = st.sa;
-        *reinterpret_cast<i32x2*>(slS + lane * 16 + 8) = st.sb;
+        // the lane's own scales (its operand rows) stay in registers
+        const i32x2 ssa = st.sa, ssb = st.sb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             *reinterpret_cast<i32x4*>(slA + (8 * j + cr) * kPitch + cb) = st.a[j];
@@ -344,10 +343,9 @@ __global__ __launch_bounds__(256) void prefill_stream_kernel(const int8_t* __res
         // activation scales in k = 0..3 (k = 4..15 zero), operand B the weight
         // scale of block u in k = u only (zero on lanes 32..63, which carry
         // k = 8..15), so the single product is xs_u * ws_u.
-        const i32x4 sc = *reinterpret_cast<const i32x4*>(slS + lane * 16);
-        sta[0] = sc[0];
-        sta[1] = sc[1];
-        const int sb0 = h ? 0 : sc[2], sb1 = h ? 0 : sc[3];
+        sta[0] = ssa[0];
+        sta[1] = ssa[1];
+        const int sb0 = h ? 0 : ssb[0], sb1 = h ? 0 : ssb[1];
         i32x4 av[4], bv[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
