@@ -34,7 +34,8 @@
  *  - Ownership: the caller allocates and frees every buffer.  The library never
  *    allocates, frees or caches device memory and keeps no per-call state, so
  *    calls may be made from several host threads and may be captured into a
- *    HIP graph.  Outputs must not alias inputs.
+ *    HIP graph.  (One exception: q8_attn_decode_noalloc keeps its partials in a
+ *    fixed static array per GPU, see there.)  Outputs must not alias inputs.
  *  - Asynchrony: a call validates its arguments, enqueues kernels on `stream`
  *    (NULL = the current device's null stream) and returns.  Results are valid
  *    once the stream has been synchronized.  Calls never synchronize.
@@ -177,6 +178,25 @@ q8_status q8_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd
                          const int8_t* vq, const uint16_t* vd, int64_t heads, int64_t t,
                          int64_t t_cap, int64_t head_dim, float scale, float* out,
                          float* work, int64_t work_words, hipStream_t stream);
+
+/* For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): q8_attn_decode with the chunk partials kept in a static scratch
+ * array of Q8_ATTN_SCRATCH_WORDS fp32 words (1 MiB) that the library holds on
+ * each GPU it runs on until the process ends.  The call allocates and frees
+ * nothing.  Arguments, results and errors are those of q8_attn_decode without
+ * `work`; a (heads, t) whose q8_attn_work_words exceeds Q8_ATTN_SCRATCH_WORDS
+ * returns Q8_ERR_SHAPE (checked before any HIP call, nothing enqueued), e.g.
+ * 12 heads fit contexts up to 42,240 rows.  Every call on one GPU shares that
+ * GPU's scratch and keeps no state in it between calls (each call writes the
+ * partials it reads), but calls that overlap on one GPU -- on different
+ * streams, or from several host threads without ordering -- race on it and
+ * must not be issued. */
+#define Q8_ATTN_SCRATCH_WORDS 262144
+q8_status q8_attn_decode_noalloc(const uint16_t* q, const int8_t* kq, const uint16_t* kd,
+                                 const int8_t* vq, const uint16_t* vd, int64_t heads, int64_t t,
+                                 int64_t t_cap, int64_t head_dim, float scale, float* out,
+                                 hipStream_t stream);
 
 /* Workspace words q8_attn_decode needs for (heads, t), enough for every context
  * up to t (the count never decreases with t, so a workspace sized for t_cap

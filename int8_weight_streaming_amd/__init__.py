@@ -47,8 +47,9 @@ EXPORTED = (
     "q8_gemm_prefill", "q8_block_dots", "q8_attn_decode", "q8_attn_work_words",
     "q4_quantize_weights", "q4_gemm_skinny", "q8_gemm_fused", "q8_rmsnorm", "q8_attn_decode_append",
     "q8_quantize_act_fused", "q8_attn_partial_words", "q8_attn_decode_append_partials",
-    "q8_gemm_attn_residual",
+    "q8_gemm_attn_residual", "q8_attn_decode_noalloc",
 )
+ATTN_SCRATCH_WORDS = 262144
 PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words", "q8_probe_barrier",
                   "q8_probe_barrier_words")
 
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q8_block_dots.argtypes = [P, I64, I64, I64, P, P, P]
     L.q8_attn_decode.argtypes = [P, P, P, P, P, I64, I64, I64, I64, C.c_float, P, P, I64, P]
     L.q8_attn_decode.restype = I
+    L.q8_attn_decode_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, C.c_float, P, P]
+    L.q8_attn_decode_noalloc.restype = I
     L.q8_attn_work_words.argtypes = [I64, I64]
     L.q8_attn_work_words.restype = I64
     L.q8_probe_read.argtypes = [P, I64, P, P]
@@ -431,6 +434,30 @@ def attn_decode(q, kq, kd, vq, vd, t: int, scale: float, work=None, out=None):
     _check("q8_attn_decode", load_library().q8_attn_decode(
         _ptr(q), _ptr(kq), _ptr(kd), _ptr(vq), _ptr(vd), heads, int(t), t_cap, d, float(scale),
         _ptr(y), _ptr(work), words, _stream()))
+    return y
+
+
+def attn_decode_noalloc(q, kq, kd, vq, vd, t: int, scale: float, out=None):
+    """attn_decode without a workspace: the library keeps the chunk partials in
+    its static per-GPU scratch (calls on one GPU must not overlap)."""
+    q = _as_bits16(q)
+    kd = _as_bits16(kd)
+    vd = _as_bits16(vd)
+    _need(q, "q", torch.uint16, 2)
+    _need(kq, "kq", torch.int8, 3)
+    _need(vq, "vq", torch.int8, 3)
+    _need(kd, "kd", torch.uint16, 3)
+    _need(vd, "vd", torch.uint16, 3)
+    heads, t_cap, d = kq.shape
+    if tuple(vq.shape) != (heads, t_cap, d) or tuple(q.shape) != (heads, d):
+        raise ValueError("q [heads][d], kq and vq [heads][t_cap][d] must agree")
+    if tuple(kd.shape) != (heads, t_cap, d // 32) or tuple(vd.shape) != tuple(kd.shape):
+        raise ValueError("kd and vd must be [heads][t_cap][d/32]")
+    y = _out(out, "out", torch.float32, heads * d) if out is not None else \
+        torch.empty((heads, d), dtype=torch.float32, device=kq.device)
+    _check("q8_attn_decode_noalloc", load_library().q8_attn_decode_noalloc(
+        _ptr(q), _ptr(kq), _ptr(kd), _ptr(vq), _ptr(vd), heads, int(t), t_cap, d, float(scale),
+        _ptr(y), _stream()))
     return y
 
 

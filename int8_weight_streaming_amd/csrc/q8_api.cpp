@@ -70,6 +70,7 @@ q8_status device_for(hipStream_t stream, const q8::DeviceInfo** info) {
                             (prop.gcnArchName[6] == 0 || prop.gcnArchName[6] == ':');
             g_dev_info[dev].cu_count = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
             g_dev_info[dev].max_lds = prop.sharedMemPerBlock > 0 ? (size_t)prop.sharedMemPerBlock : 65536;
+            g_dev_info[dev].ordinal = dev;
             if (ok && g_dev_info[dev].max_lds > 65536 &&
                 q8::prefill_prepare(g_dev_info[dev]) != hipSuccess) {
                 (void)hipGetLastError();
@@ -335,6 +336,32 @@ q8_status q8_attn_decode_append(const uint16_t* q, int8_t* kq, uint16_t* kd, int
     Q8_TRY(device_for(stream, &dev));
     return finish(q8::launch_attn_decode(q, kq, kd, vq, vd, heads, t, t_cap, scale, out, work, knew, vnew,
                                          *dev, stream));
+}
+
+q8_status q8_attn_decode_noalloc(const uint16_t* q, const int8_t* kq, const uint16_t* kd, const int8_t* vq,
+                                 const uint16_t* vd, int64_t heads, int64_t t, int64_t t_cap, int64_t head_dim,
+                                 float scale, float* out, hipStream_t stream) {
+    if (head_dim != 128) return Q8_ERR_SHAPE;
+    if (heads < 0 || heads > kMaxAttnHeads || t < 1 || t > t_cap || t_cap > kMaxAttnRows)
+        return Q8_ERR_SHAPE;
+    if (!(scale == scale) || scale - scale != 0.0f) return Q8_ERR_SHAPE;
+    if (heads == 0) return Q8_OK;
+    const int64_t need = q8::attn_work_floats(heads, t);
+    if (need > q8::kAttnScratchFloats) return Q8_ERR_SHAPE;
+    if (!q || !kq || !kd || !vq || !vd || !out) return Q8_ERR_NULL;
+    if (!aligned16(q) || !aligned16(kq) || !aligned16(kd) || !aligned16(vq) || !aligned16(vd) ||
+        !aligned16(out))
+        return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    float* work = nullptr;
+    if (need > 0) {
+        const hipError_t e = q8::attn_scratch(*dev, &work);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return finish(q8::launch_attn_decode(q, const_cast<int8_t*>(kq), const_cast<uint16_t*>(kd),
+                                         const_cast<int8_t*>(vq), const_cast<uint16_t*>(vd), heads, t,
+                                         t_cap, scale, out, work, nullptr, nullptr, *dev, stream));
 }
 
 int64_t q8_attn_partial_words(int64_t heads, int64_t t) {

@@ -30,6 +30,8 @@
 #include "q8_device.hpp"
 #include "q8_internal.hpp"
 
+#include <mutex>
+
 namespace q8 {
 
 constexpr int kAttnD = 128;                    // head dimension
@@ -359,6 +361,33 @@ hipError_t launch_attn_decode(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_
         attn_combine_kernel<<<(unsigned)heads, kAttnD, 0, stream>>>(work, nchunks, out);
     }
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ static scratch
+
+// The chunk partials of the allocation-free entry point live here instead of a
+// caller workspace.  Host code never passes this name to a kernel or a copy:
+// on the host it only names the symbol, so its device address is looked up
+// once per device (with that device current) and that address is used.
+static __device__ __align__(256) float scratch[kAttnScratchFloats];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+hipError_t attn_scratch(const DeviceInfo& dev, float** ptr) {
+    if (dev.ordinal < 0 || dev.ordinal >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev.ordinal] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev.ordinal] = static_cast<float*>(p);
+    }
+    *ptr = g_scratch_ptr[dev.ordinal];
+    return hipSuccess;
 }
 
 }  // namespace q8

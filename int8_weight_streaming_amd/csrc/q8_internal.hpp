@@ -10,6 +10,7 @@ namespace q8 {
 struct DeviceInfo {
     int cu_count;
     size_t max_lds;   // largest LDS allocation of one workgroup, bytes
+    int ordinal;      // HIP device index
 };
 
 // Each launcher enqueues on `stream` and returns the launch's hipError_t.
@@ -73,5 +74,11 @@ hipError_t launch_attn_decode(const uint16_t* q, int8_t* kq, uint16_t* kd, int8_
                               int64_t heads, int64_t t, int64_t t_cap, float scale, float* out,
                               float* work, const uint16_t* knew, const uint16_t* vnew,
                               const DeviceInfo& dev, hipStream_t stream);
+
+// The library's static attention scratch (kAttnScratchFloats floats, a
+// file-scope device array, one copy per GPU): its device address on dev,
+// looked up once per device with that device current and kept.
+constexpr int64_t kAttnScratchFloats = 262144;          // 1 MiB
+hipError_t attn_scratch(const DeviceInfo& dev, float** ptr);
 
 }  // namespace q8

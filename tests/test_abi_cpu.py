@@ -280,3 +280,34 @@ def test_attn_validation(lib):
     import torch
     if not torch.cuda.is_available():
         assert call(args()) == DEVICE
+
+
+def test_attn_noalloc_validation(lib):
+    """The allocation-free attention checks its arguments, and that the partials
+    of (heads, t) fit its static scratch, before any device call."""
+    f = lib.q8_attn_decode_noalloc
+    assert q8.ATTN_SCRATCH_WORDS == 262144
+    hdr = open(HEADER).read()
+    assert "#define Q8_ATTN_SCRATCH_WORDS 262144" in hdr
+    args = lambda **kw: dict(dict(q=A, kq=B, kd=A, vq=B, vd=A, heads=12, t=4096, t_cap=4096, d=128,
+                                  scale=0.088, out=A), **kw)
+    call = lambda a: f(a["q"], a["kq"], a["kd"], a["vq"], a["vd"], a["heads"], a["t"], a["t_cap"],
+                       a["d"], a["scale"], a["out"], None)
+    assert call(args(d=64)) == SHAPE
+    assert call(args(t=0)) == SHAPE
+    assert call(args(t=5000)) == SHAPE                     # t > t_cap
+    assert call(args(scale=float("nan"))) == SHAPE
+    assert call(args(q=None)) == NULL
+    assert call(args(out=None)) == NULL
+    assert call(args(vd=MIS)) == ALIGN
+    assert call(args(heads=0, q=None, kq=None, kd=None, vq=None, vd=None, out=None)) == OK
+    # the largest context of 12 heads whose partials fit, and the next one
+    big = 1 << 20
+    fits = [t for t in (42240, 42241) if lib.q8_attn_work_words(12, t) <= q8.ATTN_SCRATCH_WORDS]
+    assert fits == [42240]
+    assert call(args(t=42241, t_cap=big)) == SHAPE
+    assert call(args(heads=1, t=(1 << 24) - 128, t_cap=(1 << 24) - 128)) == SHAPE
+    import torch
+    if not torch.cuda.is_available():
+        assert call(args(t=42240, t_cap=big)) == DEVICE
+        assert call(args()) == DEVICE
