@@ -150,9 +150,26 @@ q8_status q8_gemm_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
  * be compared bit for bit: isum[t][j][b] = sum_{i<32} wq[j][32b+i] * xq[t][32b+i]
  * for t < m (m = 0..8), j < n, b < k/32 [fak MODEL-BASELINE-RESULTS, ACT 3
  * item 3: signed x signed int8 block dot].  Uses the same block-dot routine as
- * the Q8-activation decode products.  isum is int32 [m][n][k/32]. */
+ * the Q8-activation decode products (each half block on its own lane with
+ * v_dot4_i32_i8, the two halves added across the lane pair); the prefill
+ * product takes its block sums from the int8 matrix cores instead.  isum is
+ * int32 [m][n][k/32]. */
 q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m,
                         const int8_t* xq, int32_t* isum, hipStream_t stream);
+
+/* Diagnostics: the kernel (with its compile-time layout) that a product call
+ * with these extents launches on the current device, so that a test can show
+ * which code path a shape exercises.  op Q8_OP_SKINNY: q8_gemm_skinny with
+ * m = rows and activation type act (also q8_gemv at rows = 1); Q8_OP_PREFILL:
+ * q8_gemm_prefill with p = rows (act ignored); Q8_OP_Q4_SKINNY: q4_gemm_skinny.
+ * Writes a NUL-terminated name such as "skinny_kernel<1,0,16,2,6>" (batch,
+ * activation type, lanes per group, rows per group, chunks per lane) or
+ * "prefill_tile64_kernel<2>" into buf, "none" for an empty call.  Extents are
+ * validated as by those calls (Q8_ERR_ENUM, Q8_ERR_SHAPE, Q8_ERR_BATCH); buf
+ * NULL gives Q8_ERR_NULL, a name longer than buf_len - 1 bytes Q8_ERR_SHAPE;
+ * no device gives Q8_ERR_DEVICE.  Enqueues nothing. */
+typedef enum { Q8_OP_SKINNY = 0, Q8_OP_PREFILL = 1, Q8_OP_Q4_SKINNY = 2 } q8_op;
+q8_status q8_kernel_name(int op, int64_t n, int64_t k, int64_t rows, int act, char* buf, int64_t buf_len);
 
 /* Decode attention over a Q8_0 key/value cache, one query row per head and no
  * mask [Frigg README: "Masks" (decode passes no mask: one query against the

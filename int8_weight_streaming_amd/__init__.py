@@ -47,8 +47,9 @@ EXPORTED = (
     "q8_gemm_prefill", "q8_block_dots", "q8_attn_decode", "q8_attn_work_words",
     "q4_quantize_weights", "q4_gemm_skinny", "q8_gemm_fused", "q8_rmsnorm", "q8_attn_decode_append",
     "q8_quantize_act_fused", "q8_attn_partial_words", "q8_attn_decode_append_partials",
-    "q8_gemm_attn_residual", "q8_attn_decode_noalloc",
+    "q8_gemm_attn_residual", "q8_attn_decode_noalloc", "q8_kernel_name",
 )
+OP_SKINNY, OP_PREFILL, OP_Q4_SKINNY = 0, 1, 2
 ATTN_SCRATCH_WORDS = 262144
 PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words", "q8_probe_barrier",
                   "q8_probe_barrier_words")
@@ -87,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q8_attn_decode.restype = I
     L.q8_attn_decode_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, C.c_float, P, P]
     L.q8_attn_decode_noalloc.restype = I
+    L.q8_kernel_name.argtypes = [I, I64, I64, I64, I, P, I64]
+    L.q8_kernel_name.restype = I
     L.q8_attn_work_words.argtypes = [I64, I64]
     L.q8_attn_work_words.restype = I64
     L.q8_probe_read.argtypes = [P, I64, P, P]
@@ -529,6 +532,15 @@ def gemm_attn_residual(wq, wd, work, t: int, h):
     _check("q8_gemm_attn_residual", load_library().q8_gemm_attn_residual(
         _ptr(wq), _ptr(wd), n, k, _ptr(work), _work(work), int(t), _ptr(h), _stream()))
     return h
+
+
+def kernel_name(op: int, n: int, k: int, rows: int, act: int = Q8_ACT_BF16) -> str:
+    """The kernel a product call with these extents launches on the current
+    device (op OP_SKINNY, OP_PREFILL or OP_Q4_SKINNY; rows = m or p)."""
+    buf = C.create_string_buffer(96)
+    _check("q8_kernel_name", load_library().q8_kernel_name(
+        int(op), int(n), int(k), int(rows), int(act), C.cast(buf, C.c_void_p), len(buf)))
+    return buf.value.decode()
 
 
 # ------------------------------------------------------------------ measurement utility

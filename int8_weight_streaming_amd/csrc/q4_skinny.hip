@@ -343,39 +343,52 @@ static hipError_t q4_launch_cfg(const uint8_t* wq, const uint16_t* wd, int64_t n
     return hipGetLastError();
 }
 
+// Configurations measured on the Mimir shapes and the 262144 x 1536 lm_head
+// (graph replay, weights rotated past the caches, batch 1, 2, 4 and 8).  The
+// bf16 form is bound by its arithmetic (unpack, convert, dot), so lane
+// occupancy decides more than for the Q8_0 products:
+//  * at least 4 workgroups of 64 rows per compute unit: 16-lane groups; at
+//    batch 1 two rows each and 16-block K tiles (bf16) or 48-block tiles
+//    (Q8); above that four rows each with the activation tile in LDS;
+//  * from half a workgroup of 32 rows per compute unit: 16-lane groups of
+//    two rows, 48-block tiles (K = 1536 in one tile);
+//  * shorter matrices: one row per 32-lane group, 64-block tiles; for K
+//    above 2048 at batch 1-2 a 128-block tile, above that one wave per row
+//    with 128-block tiles staged in LDS.
+Q4Layout q4_layout(int64_t n, int64_t k, int m, int act, int cu_count) {
+    const int64_t nb = k / 32;
+    if ((n + 63) / 64 >= 4 * (int64_t)cu_count) {
+        if (m == 1) return act == 0 ? Q4Layout{16, 2, 1, 0} : Q4Layout{16, 2, 3, 0};
+        return {16, 4, 3, 1};
+    }
+    if (2 * ((n + 31) / 32) >= (int64_t)cu_count) return {16, 2, 3, m > 2};
+    if (nb <= 64) return {32, 1, 2, m > 2};
+    if (m <= 2) return {32, 1, 4, 0};
+    return {64, 1, 2, 1};
+}
+
 template <int M, int ACT>
 static hipError_t q4_launch_m(const uint8_t* wq, const uint16_t* wd, int64_t n, int nb,
                               const void* x, const uint16_t* xd, float* y,
                               const DeviceInfo& dev, hipStream_t stream) {
     (void)hipGetLastError();
-    // Configurations measured on the Mimir shapes and the 262144 x 1536 lm_head
-    // (graph replay, weights rotated past the caches, batch 1, 2, 4 and 8).  The
-    // bf16 form is bound by its arithmetic (unpack, convert, dot), so lane
-    // occupancy decides more than for the Q8_0 products:
-    //  * at least 4 workgroups of 64 rows per compute unit: 16-lane groups; at
-    //    batch 1 two rows each and 16-block K tiles (bf16) or 48-block tiles
-    //    (Q8); above that four rows each with the activation tile in LDS;
-    //  * from half a workgroup of 32 rows per compute unit: 16-lane groups of
-    //    two rows, 48-block tiles (K = 1536 in one tile);
-    //  * shorter matrices: one row per 32-lane group, 64-block tiles; for K
-    //    above 2048 at batch 1-2 a 128-block tile, above that one wave per row
-    //    with 128-block tiles staged in LDS.
-    if ((n + 63) / 64 >= 4 * (int64_t)dev.cu_count) {
-        if constexpr (M == 1) {
-            if constexpr (ACT == 0) return q4_launch_cfg<M, ACT, 16, 2, 1, 0>(wq, wd, n, nb, x, xd, y, stream);
-            else return q4_launch_cfg<M, ACT, 16, 2, 3, 0>(wq, wd, n, nb, x, xd, y, stream);
-        } else {
-            return q4_launch_cfg<M, ACT, 16, 4, 3, 1>(wq, wd, n, nb, x, xd, y, stream);
-        }
+    const Q4Layout L = q4_layout(n, (int64_t)nb * 32, M, ACT, dev.cu_count);
+    if (L.g == 16 && L.r == 2 && L.cpl == 1) {
+        if constexpr (M == 1 && ACT == 0) return q4_launch_cfg<M, ACT, 16, 2, 1, 0>(wq, wd, n, nb, x, xd, y, stream);
+    } else if (L.g == 16 && L.r == 2 && L.cpl == 3 && L.xl == 0) {
+        if constexpr (M <= 2) return q4_launch_cfg<M, ACT, 16, 2, 3, 0>(wq, wd, n, nb, x, xd, y, stream);
+    } else if (L.g == 16 && L.r == 2 && L.cpl == 3) {
+        if constexpr (M > 2) return q4_launch_cfg<M, ACT, 16, 2, 3, 1>(wq, wd, n, nb, x, xd, y, stream);
+    } else if (L.g == 16 && L.r == 4) {
+        if constexpr (M > 1) return q4_launch_cfg<M, ACT, 16, 4, 3, 1>(wq, wd, n, nb, x, xd, y, stream);
+    } else if (L.g == 32 && L.cpl == 2) {
+        return q4_launch_cfg<M, ACT, 32, 1, 2, (M > 2)>(wq, wd, n, nb, x, xd, y, stream);
+    } else if (L.g == 32 && L.cpl == 4) {
+        if constexpr (M <= 2) return q4_launch_cfg<M, ACT, 32, 1, 4, 0>(wq, wd, n, nb, x, xd, y, stream);
+    } else if (L.g == 64) {
+        if constexpr (M > 2) return q4_launch_cfg<M, ACT, 64, 1, 2, 1>(wq, wd, n, nb, x, xd, y, stream);
     }
-    if (2 * ((n + 31) / 32) >= (int64_t)dev.cu_count)
-        return q4_launch_cfg<M, ACT, 16, 2, 3, (M > 2)>(wq, wd, n, nb, x, xd, y, stream);
-    if (nb <= 64) return q4_launch_cfg<M, ACT, 32, 1, 2, (M > 2)>(wq, wd, n, nb, x, xd, y, stream);
-    if constexpr (M <= 2) {
-        return q4_launch_cfg<M, ACT, 32, 1, 4, 0>(wq, wd, n, nb, x, xd, y, stream);
-    } else {
-        return q4_launch_cfg<M, ACT, 64, 1, 2, 1>(wq, wd, n, nb, x, xd, y, stream);
-    }
+    return hipErrorInvalidValue;                 // no layout is chosen outside the cases above
 }
 
 template <int ACT>

@@ -10,6 +10,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 
@@ -287,6 +288,42 @@ q8_status q4_gemm_skinny(const uint8_t* wq, const uint16_t* wd, int64_t n, int64
     const q8::DeviceInfo* dev = nullptr;
     Q8_TRY(device_for(stream, &dev));
     return finish(q8::launch_q4_skinny(wq, wd, n, k, (int)m, act, x, xd, y, *dev, stream));
+}
+
+q8_status q8_kernel_name(int op, int64_t n, int64_t k, int64_t rows, int act, char* buf, int64_t buf_len) {
+    if (op != Q8_OP_SKINNY && op != Q8_OP_PREFILL && op != Q8_OP_Q4_SKINNY) return Q8_ERR_ENUM;
+    if (op != Q8_OP_PREFILL && act != Q8_ACT_BF16 && act != Q8_ACT_Q8) return Q8_ERR_ENUM;
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(n, k));
+    if (op == Q8_OP_PREFILL) {
+        Q8_TRY(check_rows(rows, k));
+        if (rows > kMaxPrefillRows) return Q8_ERR_SHAPE;
+    } else if (rows < 0 || rows > Q8_MAX_BATCH) {
+        return Q8_ERR_BATCH;
+    }
+    if (!buf) return Q8_ERR_NULL;
+    if (buf_len < 1) return Q8_ERR_SHAPE;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(nullptr, &dev));
+    char name[96];
+    if (n == 0 || rows == 0) {
+        std::snprintf(name, sizeof name, "none");
+    } else if (op == Q8_OP_SKINNY) {
+        const q8::SkinnyLayout L = q8::skinny_layout(n, k, (int)rows, dev->cu_count);
+        std::snprintf(name, sizeof name, "skinny_kernel<%d,%d,%d,%d,%d>", (int)rows, act, L.g, L.r, L.cpl);
+    } else if (op == Q8_OP_Q4_SKINNY) {
+        const q8::Q4Layout L = q8::q4_layout(n, k, (int)rows, act, dev->cu_count);
+        std::snprintf(name, sizeof name, "q4_skinny_kernel<%d,%d,%d,%d,%d,%d>", (int)rows, act, L.g, L.r, L.cpl,
+                      L.xl);
+    } else {
+        static const char* const kinds[] = {"prefill_tile64_kernel<1>", "prefill_tile64_kernel<2>",
+                                            "prefill_stream_kernel", "prefill_kernel"};
+        std::snprintf(name, sizeof name, "%s", kinds[q8::prefill_kind(n, k, rows, dev->cu_count)]);
+    }
+    const size_t len = std::strlen(name);
+    if ((int64_t)len + 1 > buf_len) return Q8_ERR_SHAPE;
+    std::memcpy(buf, name, len + 1);
+    return Q8_OK;
 }
 
 int64_t q8_attn_work_words(int64_t heads, int64_t t) {

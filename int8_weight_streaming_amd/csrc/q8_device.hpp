@@ -61,15 +61,20 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                           __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// Exact int32 dot of one 32-element Q8 block (8 dwords of codes on each side)
+// Exact int32 dot of one 32-element Q8 block split over a lane pair (lanes 2i
+// and 2i + 1): each lane holds one 16-byte half of the weight and activation
+// codes, takes its four signed v_dot4_i32_i8, and one DPP step adds the
+// partner's half; both lanes end with the block's sum
 // [fak MODEL-BASELINE-RESULTS, ACT 3 item 3: signed x signed int8 block dot].
-// |sum| <= 32 * 127 * 127 = 516,128, far inside int32.
-__device__ __forceinline__ int block_dot_i8(const uint32_t w[8], const uint32_t x[8]) {
+// |sum| <= 32 * 127 * 127 = 516,128, far inside int32.  Every lane of the
+// wave must execute it (the DPP step reads the partner's register).
+__device__ __forceinline__ int block_dot_halves(const u32x4& w, const u32x4& x) {
     int s = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        s = __builtin_amdgcn_sdot4((int)w[i], (int)x[i], s, false);
-    return s;
+    s = __builtin_amdgcn_sdot4((int)w.x, (int)x.x, s, false);
+    s = __builtin_amdgcn_sdot4((int)w.y, (int)x.y, s, false);
+    s = __builtin_amdgcn_sdot4((int)w.z, (int)x.z, s, false);
+    s = __builtin_amdgcn_sdot4((int)w.w, (int)x.w, s, false);
+    return s + __builtin_amdgcn_update_dpp(0, s, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
 }
 
 // ---------------------------------------------------------------- buffer loads

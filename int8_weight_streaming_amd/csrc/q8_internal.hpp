@@ -19,6 +19,14 @@ hipError_t launch_quantize_f32(const float* w, int64_t nblocks, int8_t* q, uint1
 hipError_t launch_quantize_bf16(const uint16_t* x, int64_t nblocks, int8_t* q, uint16_t* d,
                                 const DeviceInfo& dev, hipStream_t stream);
 
+// Lane-group layout of the decode product kernel for (n, k, m) on a device
+// with cu_count compute units: G lanes per group, R rows per group, CPL
+// 16-byte chunks per lane per K tile.
+struct SkinnyLayout {
+    int g, r, cpl;
+};
+SkinnyLayout skinny_layout(int64_t n, int64_t k, int m, int cu_count);
+
 hipError_t launch_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int m,
                          int act, const void* x, const uint16_t* xd, float* y,
                          const DeviceInfo& dev, hipStream_t stream);
@@ -46,6 +54,18 @@ hipError_t launch_q4_quantize(const float* w, int64_t nblocks, uint8_t* q, uint1
 hipError_t launch_q4_skinny(const uint8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int m,
                             int act, const void* x, const uint16_t* xd, float* y,
                             const DeviceInfo& dev, hipStream_t stream);
+
+// The prefill kernel chosen for (n, k, p) on a device with cu_count compute
+// units: prefill_tile64_kernel<1> / <2>, prefill_stream_kernel, prefill_kernel.
+enum { kPrefillTile64x1 = 0, kPrefillTile64x2 = 1, kPrefillStream = 2, kPrefillTile32 = 3 };
+int prefill_kind(int64_t n, int64_t k, int64_t p, int cu_count);
+
+// Layout of the int4 product kernel: as SkinnyLayout, plus whether the
+// activation tile is staged in LDS.
+struct Q4Layout {
+    int g, r, cpl, xl;
+};
+Q4Layout q4_layout(int64_t n, int64_t k, int m, int act, int cu_count);
 
 // LDS the prefill kernel chosen for this shape needs, and the one-time
 // per-device setup that lets it use up to dev.max_lds.

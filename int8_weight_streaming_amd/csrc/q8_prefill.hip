@@ -635,6 +635,11 @@ static int tile64_split(int64_t n, int64_t k, int64_t p, int cu_count) {
     return 0;
 }
 
+int prefill_kind(int64_t n, int64_t k, int64_t p, int cu_count) {
+    if (const int ks = tile64_split(n, k, p, cu_count)) return ks == 1 ? kPrefillTile64x1 : kPrefillTile64x2;
+    return use_stream(n, k, p) ? kPrefillStream : kPrefillTile32;
+}
+
 size_t prefill_lds_bytes(int64_t n, int64_t k, int64_t p, const DeviceInfo& dev) {
     if (const int ks = tile64_split(n, k, p, dev.cu_count)) return (size_t)ks * kT64Lds;
     if (k % 512 == 0 && k <= kStreamMaxK) return (size_t)kStreamLds;

@@ -50,25 +50,32 @@ static hipError_t launch_cfg(const int8_t* wq, const uint16_t* wd, int64_t n, in
     return hipGetLastError();
 }
 
+// Configurations measured per Mimir shape and batch (graph replay, weights
+// rotated past the caches, batch 1, 2, 4 and 8):
+//  * tall matrices: 16-lane groups, 2 rows per group, 6 chunks per lane per
+//    K tile (K = 1536 in one tile) -- at batch 1-2 from 32 rows per compute
+//    unit on, above batch 2 only from 128 (below that one workgroup per
+//    compute unit leaves the per-lane arithmetic of 3-8 rows exposed);
+//  * shorter matrices need smaller row tiles to cover every compute unit:
+//    32-lane groups, one row each, K tile = 96 chunks (K = 1536 in one tile);
+//    for longer K, 32-lane groups with a 256-chunk tile at batch 1-2
+//    (activations in registers) and one wave per row above that.
+SkinnyLayout skinny_layout(int64_t n, int64_t k, int m, int cu_count) {
+    const int64_t tall_wgs = (n + 31) / 32;
+    if (tall_wgs >= (int64_t)cu_count * (m <= 2 ? 1 : 4)) return {16, 2, 6};
+    if (k / 32 <= 48) return {32, 1, 3};
+    if (m <= 2) return {32, 1, 8};
+    return {64, 1, 2};
+}
+
 template <int M, int ACT>
 static hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int nb,
                            const void* x, const uint16_t* xd, float* y,
                            const DeviceInfo& dev, hipStream_t stream) {
     (void)hipGetLastError();
-    // Configurations measured per Mimir shape and batch (graph replay, weights
-    // rotated past the caches, batch 1, 2, 4 and 8):
-    //  * tall matrices: 16-lane groups, 2 rows per group, 6 chunks per lane per
-    //    K tile (K = 1536 in one tile) -- at batch 1-2 from 32 rows per compute
-    //    unit on, above batch 2 only from 128 (below that one workgroup per
-    //    compute unit leaves the per-lane arithmetic of 3-8 rows exposed);
-    //  * shorter matrices need smaller row tiles to cover every compute unit:
-    //    32-lane groups, one row each, K tile = 96 chunks (K = 1536 in one tile);
-    //    for longer K, 32-lane groups with a 256-chunk tile at batch 1-2
-    //    (activations in registers) and one wave per row above that.
-    const int64_t tall_wgs = (n + 31) / 32;
-    if (tall_wgs >= (int64_t)dev.cu_count * (M <= 2 ? 1 : 4))
-        return launch_cfg<M, ACT, 16, 2, 6>(wq, wd, n, nb, x, xd, y, stream);
-    if (nb <= 48) return launch_cfg<M, ACT, 32, 1, 3>(wq, wd, n, nb, x, xd, y, stream);
+    const SkinnyLayout L = skinny_layout(n, (int64_t)nb * 32, M, dev.cu_count);
+    if (L.g == 16) return launch_cfg<M, ACT, 16, 2, 6>(wq, wd, n, nb, x, xd, y, stream);
+    if (L.cpl == 3) return launch_cfg<M, ACT, 32, 1, 3>(wq, wd, n, nb, x, xd, y, stream);
     if constexpr (M <= 2) {
         return launch_cfg<M, ACT, 32, 1, 8>(wq, wd, n, nb, x, xd, y, stream);
     } else {
@@ -103,32 +110,37 @@ hipError_t launch_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_
 
 // ------------------------------------------------------------------ block dots
 
-// isum[t][j][b] for t < m: one thread per (t, j, b), using the whole-block
-// int8 dot routine.
+// isum[t][j][b] for t < m: a lane pair per (t, j, b), each lane one 16-byte
+// half of the block, summed by block_dot_halves -- the routine the
+// Q8-activation decode products use.  The loop bound is uniform per
+// workgroup and a lane past the end computes a clamped pair without storing,
+// so both lanes of every pair reach the DPP step together.
 __global__ __launch_bounds__(256) void block_dots_kernel(const int8_t* __restrict__ wq, int64_t n, int nb,
                                                          int m, const int8_t* __restrict__ xq,
                                                          int32_t* __restrict__ isum) {
     const int64_t total = (int64_t)m * n * nb;
     const int64_t k = (int64_t)nb * 32;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < 2 * total;
+         base += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t li = base + threadIdx.x;
+        const bool live = li < 2 * total;
+        const int64_t i = live ? li >> 1 : 0;
+        const int half = (int)(li & 1);
         const int b = (int)(i % nb);
         const int64_t j = (i / nb) % n;
         const int t = (int)(i / ((int64_t)nb * n));
-        const uint4* wp = reinterpret_cast<const uint4*>(wq + j * k + (int64_t)b * 32);
-        const uint4* xp = reinterpret_cast<const uint4*>(xq + t * k + (int64_t)b * 32);
-        const uint4 w0 = wp[0], w1 = wp[1], x0 = xp[0], x1 = xp[1];
-        const uint32_t wc[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        const uint32_t xc[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        isum[i] = block_dot_i8(wc, xc);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(wq + j * k + (int64_t)b * 32 + 16 * half);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(xq + t * k + (int64_t)b * 32 + 16 * half);
+        const int s = block_dot_halves(w, x);
+        if (live && half == 0) isum[i] = s;
     }
 }
 
 hipError_t launch_block_dots(const int8_t* wq, int64_t n, int64_t k, int m, const int8_t* xq,
                              int32_t* isum, const DeviceInfo& dev, hipStream_t stream) {
     const int nb = (int)(k / 32);
-    const int64_t total = (int64_t)m * n * nb;
-    int64_t grid = (total + 255) / 256;
+    const int64_t lanes = 2 * (int64_t)m * n * nb;
+    int64_t grid = (lanes + 255) / 256;
     const int64_t cap = (int64_t)dev.cu_count * 16;
     if (grid > cap) grid = cap;
     (void)hipGetLastError();

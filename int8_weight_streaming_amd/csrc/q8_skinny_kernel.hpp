@@ -550,13 +550,9 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
                     }
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        int s = 0;
-                        s = __builtin_amdgcn_sdot4((int)w[j][r].x, (int)xc[0], s, false);
-                        s = __builtin_amdgcn_sdot4((int)w[j][r].y, (int)xc[1], s, false);
-                        s = __builtin_amdgcn_sdot4((int)w[j][r].z, (int)xc[2], s, false);
-                        s = __builtin_amdgcn_sdot4((int)w[j][r].w, (int)xc[3], s, false);
-                        // exact int32 block sum: add the neighbouring lane's half
-                        s += __builtin_amdgcn_update_dpp(0, s, 0xB1, 0xF, 0xF, true);
+                        // exact int32 block sum: this lane's half and its neighbour's
+                        const u32x4 xv = {xc[0], xc[1], xc[2], xc[3]};
+                        const int s = block_dot_halves(w[j][r], xv);
                         const float t = even ? ws[j][r] * xs : 0.0f;
                         acc[r][m] = fmaf((float)s, t, acc[r][m]);
                     }

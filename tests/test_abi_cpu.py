@@ -311,3 +311,23 @@ def test_attn_noalloc_validation(lib):
     if not torch.cuda.is_available():
         assert call(args(t=42240, t_cap=big)) == DEVICE
         assert call(args()) == DEVICE
+
+
+def test_kernel_name_validation(lib):
+    f = lib.q8_kernel_name
+    import ctypes
+    buf = ctypes.create_string_buffer(96)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    assert f(3, 8, 64, 1, 0, p, 96) == ENUM                  # unknown op
+    assert f(0, 8, 64, 1, 2, p, 96) == ENUM                  # unknown activation type
+    assert f(0, 8, 48, 1, 0, p, 96) == SHAPE
+    assert f(0, 8, 64, 9, 0, p, 96) == BATCH
+    assert f(2, 8, 64, -1, 1, p, 96) == BATCH
+    assert f(1, 8, 64, -1, 0, p, 96) == SHAPE                # negative p
+    assert f(1, 8, 64, 65535 * 64 + 1, 0, p, 96) == SHAPE
+    assert f(0, 8, 64, 1, 0, None, 96) == NULL
+    assert f(0, 8, 64, 1, 0, p, 0) == SHAPE
+    import torch
+    if not torch.cuda.is_available():
+        assert f(0, 8, 64, 1, 0, p, 96) == DEVICE
+        assert f(1, 8, 64, 5, 7, p, 96) == DEVICE            # act is ignored for prefill
