@@ -1,4 +1,3 @@
-#!/usr/bin/env python3
 """Benchmark of the Q8_0 weight-streaming hot path on one MI355X.
 
 Headline (one JSON line on stdout): the batch-1 W8A16 GEMV at the lm_head shape
@@ -8,20 +7,25 @@ over K steps after W warm-up steps.  `value` is algorithmic bytes per call
 (int8 codes + binary16 scales + bf16 x + fp32 y = 428,870,656 B) times K over
 the synchronized wall time of the timed region, in GB/s.  The same line carries
 the roofline of that kernel (HIP-event kernel durations on the launch stream),
-the measured HBM read peak, the CPU oracle timed on the host, and the other
-workloads: the 1536 x 1536 GEMV, the Mimir-shaped decode step (513 GEMVs,
-graph-replayed), the batch 2/4/8 skinny step and the P=256 prefill GEMMs.
+the measured peaks (HBM read probe, device copy, int8 matrix-core probe), the
+CPU oracle timed on the host (one thread and all cores), and a summary of the
+other workloads: the 1536 x 1536 GEMV, the Mimir-shaped decode step (513
+products, graph-replayed) at batch 1/2/4/8, the fused decode step, decode
+attention over the int8 cache and the P = 256 prefill products.  Every figure
+outside the contract's timed region is the median of at least five trials,
+with their min and max; the full per-figure details go to stderr (and to
+--details PATH).
 
 Inputs are synthetic and seeded (module ``workloads``).  The pages' own figures
 (338.7 GB/s for a bf16 GEMV of this shape on an RTX 3060; 46.7 tok/s int8
-decode) are other hardware and another precision: context only.
+decode; 7.7 ms/token single-thread Q8 decode and a 0.346 ms/token prefill slope
+on a 16-core Zen5) are other hardware and other precisions: context only.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -35,6 +39,7 @@ METRIC = "Q8 GEMV HBM GB/s (% of peak) at 1536x262144 b=1; Mimir-shape tok/s"
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 INT8_PEAK_TOPS = 5000.0         # MI355X published dense int8 MFMA rate
 Q8_BPW = 1.0625                 # bytes per weight: 1 code + 2/32 scale
+TRIALS = 5
 
 
 def log(msg: str) -> None:
@@ -46,8 +51,23 @@ def gemv_bytes(n: int, k: int, m: int = 1) -> int:
     return n * k + n * (k // 32) * 2 + m * k * 2 + m * n * 4
 
 
+def q4_gemv_bytes(n: int, k: int, m: int = 1) -> int:
+    """Algorithmic bytes of one int4 product: 4-bit codes + binary16 scales,
+    m bf16 activation rows, m fp32 output rows."""
+    return n * k // 2 + n * (k // 32) * 2 + m * k * 2 + m * n * 4
+
+
 def prefill_bytes(n: int, k: int, p: int) -> int:
     return n * k + n * (k // 32) * 2 + p * k + p * (k // 32) * 2 + p * n * 4
+
+
+def stats(vals) -> dict:
+    a = np.asarray(list(vals), dtype=np.float64)
+    return {"median": float(np.median(a)), "min": float(a.min()), "max": float(a.max()), "n": int(a.size)}
+
+
+def r4(x):
+    return None if x is None else float(f"{x:.4g}")
 
 
 def gpu_state() -> dict | None:
@@ -94,7 +114,7 @@ def quantize_on_device(q8, w_np, dev):
 
 
 def time_region(fn, iters: int) -> tuple[float, float]:
-    """(mean per-call time from one pair of HIP events around `iters` back-to-back
+    """(mean per-call ms from one pair of HIP events around `iters` back-to-back
     calls on the launch stream, wall s)."""
     import torch
     start = torch.cuda.Event(enable_timing=True)
@@ -110,38 +130,57 @@ def time_region(fn, iters: int) -> tuple[float, float]:
     return start.elapsed_time(end) / iters, wall
 
 
-def time_events(fn, iters: int) -> tuple[float, float]:
-    """(mean per-call kernel time from HIP events on the launch stream, wall s)."""
+def capture(fn, per_graph: int):
+    """`fn` captured `per_graph` times into one HIP graph (after one warm-up call
+    on a side stream), replayed once."""
     import torch
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(iters):
-        starts[i].record()
-        fn(i)
-        ends[i].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return float(np.mean(ms)), wall
+    return g
 
 
-# ------------------------------------------------------------------ workloads
+def graph_us(fn, per_graph: int, reps: int = 3, trials: int = TRIALS) -> dict:
+    """Per-call microseconds of `fn` captured `per_graph` times into one graph:
+    `trials` timed regions of `reps` replays each (HIP events on the launch
+    stream), as median / min / max over the trials."""
+    g = capture(fn, per_graph)
+    out = stats(time_region(lambda i: g.replay(), reps)[0] * 1e3 / per_graph for _ in range(trials))
+    del g
+    return out
 
-def bench_read_probe(q8, dev, gib: float = 4.0, reps: int = 10) -> dict:
+
+# ------------------------------------------------------------------ measured peaks
+
+def bench_read_probe(dev, gib: float = 4.0) -> dict:
+    """The HBM read probe over a 4 GiB buffer for each offered load depth; the
+    fastest median is the measured read peak."""
     import torch
+    from int8_weight_streaming_amd import probe
     nbytes = int(gib * (1 << 30))
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
-    sink = q8.probe_read(buf)
-    for _ in range(2):
-        q8.probe_read(buf, sink)
-    ms, _ = time_events(lambda i: q8.probe_read(buf, sink), reps)
+    sink = probe.sink(dev)
+    res = {}
+    for lpt in probe.READ_LOADS_PER_THREAD:
+        for _ in range(2):
+            probe.read(buf, lpt, sink)
+        st = stats(nbytes / (time_region(lambda i: probe.read(buf, lpt, sink), 4)[0] * 1e6) for _ in range(TRIALS))
+        res[f"lpt{lpt}_GBps"] = st
+        log(f"read probe, {lpt} loads per thread: {st['median']:.0f} GB/s")
     del buf
-    return {"bytes": nbytes, "ms": ms, "GBps": nbytes / ms / 1e6}
+    best = max(res, key=lambda key: res[key]["median"])
+    return {"bytes": nbytes, "GBps": res[best]["median"], "best": best, "variants": res}
 
 
-def bench_copy_probe(dev, gib: float = 1.0, reps: int = 10) -> dict:
+def bench_copy_probe(dev, gib: float = 1.0) -> dict:
     """Device-to-device copy of a known size: a second peak probe, and the
     reference that scales the HBM byte counters (it reads and writes `bytes`)."""
     import torch
@@ -150,12 +189,64 @@ def bench_copy_probe(dev, gib: float = 1.0, reps: int = 10) -> dict:
     b = torch.empty_like(a)
     for _ in range(2):
         b.copy_(a)
-    ms, _ = time_events(lambda i: b.copy_(a), reps)
+    st = stats(2 * nbytes / (time_region(lambda i: b.copy_(a), 5)[0] * 1e6) for _ in range(TRIALS))
     del a, b
-    return {"bytes_each_way": nbytes, "ms": ms, "GBps_read_plus_write": 2 * nbytes / ms / 1e6}
+    return {"bytes_each_way": nbytes, "GBps_read_plus_write": st["median"], "trials": st}
 
 
-def bench_gemv_1536(q8, wl, dev, copies: int = 256, iters: int = 2000) -> dict:
+def bench_mfma_probe(dev) -> dict:
+    """The int8 matrix-core rate probe at one and two workgroups of four waves
+    per compute unit; the faster median is the measured int8 peak."""
+    import torch
+    from int8_weight_streaming_amd import probe
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = probe.sink(dev)
+    res = {}
+    for wpc in (1, 2):
+        iters = 4000
+        ops = probe.mfma_i8(cus * wpc, 100, sink)             # warm-up
+        ops = probe.mfma_i8(cus * wpc, iters, sink)
+        torch.cuda.synchronize()
+        st = stats(ops / (time_region(lambda i: probe.mfma_i8(cus * wpc, iters, sink), 2)[0] * 1e9)
+                   for _ in range(TRIALS))
+        res[f"{4 * wpc}_waves_per_cu_TOPS"] = st
+        log(f"int8 MFMA probe, {4 * wpc} waves per CU: {st['median']:.0f} TOPS")
+    best = max(v["median"] for v in res.values())
+    return {"TOPS": best, "frac_of_published": best / INT8_PEAK_TOPS, "variants": res}
+
+
+def bench_sync_probe(dev) -> dict:
+    """What one dependency edge of a decode step costs on this GPU: the
+    per-launch cost of an empty kernel under graph replay, and one grid-wide
+    barrier over 64 / 128 / 256 single-wave workgroups (the synchronization a
+    single-launch step would need between two dependent products)."""
+    import torch
+    from int8_weight_streaming_amd import probe
+    flags = probe.barrier_flags(dev)
+    out = {"graph_node_us": graph_us(lambda: probe.barrier(flags, 1, 0), 200)}
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    bar = {}
+    for g in (64, 128, 256):
+        if g > cus:
+            continue
+        flags.zero_()
+        probe.barrier(flags, g, 10)
+        t = []
+        for rounds in (100, 1100):
+            ms, _ = time_region(lambda i: probe.barrier(flags, g, rounds), 3)
+            t.append(ms)
+        torch.cuda.synchronize()
+        if int(flags[-1].item()) != 0:
+            bar[str(g)] = None
+            continue
+        bar[str(g)] = (t[1] - t[0]) * 1e3 / 1000
+    out["grid_barrier_us"] = bar
+    return out
+
+
+# ------------------------------------------------------------------ workloads
+
+def bench_gemv_1536(q8, wl, dev, copies: int = 256) -> dict:
     """The 1536 x 1536 batch-1 GEMV: rotating 256 weight copies (640 MB) so the
     figure is HBM-bound, and a single copy (cache-resident), both graph-replayed."""
     import torch
@@ -168,29 +259,21 @@ def bench_gemv_1536(q8, wl, dev, copies: int = 256, iters: int = 2000) -> dict:
     y = torch.empty(n, dtype=torch.float32, device=dev)
     out = {}
     for label, nc in (("rotating", copies), ("single", 1)):
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for i in range(8):
-                q8.gemv(wqs[i % nc], wds[i % nc], x, out=y)
-        torch.cuda.current_stream().wait_stream(s)
-        g = torch.cuda.CUDAGraph()
-        per_graph = 500
-        with torch.cuda.graph(g):
-            for i in range(per_graph):
-                q8.gemv(wqs[i % nc], wds[i % nc], x, out=y)
-        g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, iters // per_graph)
-        ms, _ = time_events(lambda i: g.replay(), reps)
-        per_call_us = ms * 1e3 / per_graph
-        gbps = gemv_bytes(n, k) / per_call_us / 1e3
-        out[label] = {"us_per_gemv": per_call_us, "gemv_per_s": 1e6 / per_call_us,
-                      "GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
+        cnt = [0]
+
+        def call():
+            i = cnt[0] % nc
+            cnt[0] += 1
+            q8.gemv(wqs[i], wds[i], x, out=y)
+
+        st = graph_us(call, 512)
+        us = st["median"]
+        gbps = gemv_bytes(n, k) / us / 1e3
+        out[label] = {"us_per_gemv": st, "gemv_per_s": 1e6 / us, "GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
     return out
 
 
-def bench_quantize_weights(q8, w, reps: int = 20):
+def bench_quantize_weights(q8, w):
     """The weight quantizer on the resident fp32 lm_head matrix (read 4 B,
     write 1 B code + 1/16 B scale per weight), graph-replayed.  Returns the
     figures and (rows, codes, scales) of 4096 sampled rows of its output, which
@@ -199,23 +282,21 @@ def bench_quantize_weights(q8, w, reps: int = 20):
     n, k = w.shape
     wq = torch.empty((n, k), dtype=torch.int8, device=w.device)
     wd = torch.empty((n, k // 32), dtype=torch.uint16, device=w.device)
-    us = time_graph(lambda: q8.quantize_weights(w, out=(wq, wd)), reps) * 1e3
+    st = graph_us(lambda: q8.quantize_weights(w, out=(wq, wd)), 4)
     nbytes = n * k * 4 + n * k + n * (k // 32) * 2
     rows = np.random.Generator(np.random.PCG64(78)).choice(n, size=4096, replace=False)
     ridx = torch.as_tensor(rows, device=w.device)
     sample = (rows, wq.index_select(0, ridx).cpu().numpy(), wd.index_select(0, ridx).cpu().numpy())
-    return ({"us_per_call": us, "bytes_per_call": nbytes, "GBps": nbytes / us / 1e3,
-             "frac_hbm_peak": nbytes / us / 1e3 / HBM_PEAK_GBPS, "weights_per_s": n * k / us * 1e6},
-            sample)
+    us = st["median"]
+    return ({"us_per_call": st, "bytes_per_call": nbytes, "GBps": nbytes / us / 1e3,
+             "frac_hbm_peak": nbytes / us / 1e3 / HBM_PEAK_GBPS}, sample)
 
 
-def bench_lm_head_batches(q8, wl, dev, w, q8_copies, m_list=(1, 2, 4, 8), per_graph: int = 20,
-                          reps: int = 10) -> dict:
+def bench_lm_head_batches(q8, wl, dev, w, q8_copies, m_list=(1, 2, 4, 8)) -> dict:
     """The lm_head shape (262144 x 1536) at batch 1/2/4/8 with bf16 and with Q8
     activations, in int4 (226 MB per copy) and in Q8_0 (429 MB per copy, the
     headline's two copies), in the same run; two copies alternated so no call
-    finds its weights in cache; graph-replayed, HIP events on the launch
-    stream.  Returns {"int4": {...}, "q8_0": {...}}."""
+    finds its weights in cache; graph-replayed."""
     import torch
     cfg = wl.CONFIGS["lm_head_gemv_262144x1536_b1"]
     n, k = w.shape
@@ -230,27 +311,19 @@ def bench_lm_head_batches(q8, wl, dev, w, q8_copies, m_list=(1, 2, 4, 8), per_gr
                 x = to_dev(xb, dev)
                 xa = (x,) if act == "bf16" else q8.quantize_act(x)
                 y = torch.empty((m, n), dtype=torch.float32, device=dev)
-                s = torch.cuda.Stream()
-                s.wait_stream(torch.cuda.current_stream())
-                with torch.cuda.stream(s):
-                    for i in range(4):
-                        fn(*copies[i & 1], *xa, out=y)
-                torch.cuda.current_stream().wait_stream(s)
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    for i in range(per_graph):
-                        fn(*copies[i & 1], *xa, out=y)
-                g.replay()
-                torch.cuda.synchronize()
-                ms, _ = time_events(lambda i: g.replay(), reps)
-                us = ms * 1e3 / per_graph
+                cnt = [0]
+
+                def call():
+                    i = cnt[0] & 1
+                    cnt[0] += 1
+                    fn(*copies[i], *xa, out=y)
+
+                st = graph_us(call, 20)
+                us = st["median"]
                 nbytes = wbytes(m) - (m * k if act == "q8" else 0) + (m * k // 16 if act == "q8" else 0)
-                out[fmt][f"{act}_b{m}"] = {"us_per_call": us, "bytes_per_call": nbytes,
-                                           "GBps": nbytes / us / 1e3,
-                                           "frac_hbm_peak": nbytes / us / 1e3 / HBM_PEAK_GBPS,
-                                           "weights_per_s": n * k / us * 1e6}
+                out[fmt][f"{act}_b{m}"] = {"us_per_call": st, "bytes_per_call": nbytes, "GBps": nbytes / us / 1e3,
+                                           "frac_hbm_peak": nbytes / us / 1e3 / HBM_PEAK_GBPS}
                 log(f"{fmt} lm_head {act} m={m}: {us:.2f} us, {nbytes / us / 1e3:.0f} GB/s")
-                del g
     return out
 
 
@@ -271,12 +344,6 @@ def load_mimir(q8, wl, dev) -> tuple[dict, dict]:
     return weights, core_q4
 
 
-def q4_gemv_bytes(n: int, k: int, m: int = 1) -> int:
-    """Algorithmic bytes of one int4 product: 4-bit codes + binary16 scales,
-    m bf16 activation rows, m fp32 output rows."""
-    return n * k // 2 + n * (k // 32) * 2 + m * k * 2 + m * n * 4
-
-
 def mimir_step_bytes(wl, m: int, int4_core: bool = False) -> int:
     total = 0
     for item in wl.mimir_step_order():
@@ -289,7 +356,14 @@ def mimir_step_bytes(wl, m: int, int4_core: bool = False) -> int:
     return total
 
 
-def bench_mimir(q8, wl, dev, weights, m: int, replays: int = 20, core_q4=None) -> dict:
+def step_figures(ms_stats: dict, m: int, nbytes: int) -> dict:
+    ms = ms_stats["median"]
+    roof = m * HBM_PEAK_GBPS * 1e9 / nbytes
+    return {"m": m, "ms_per_step": ms_stats, "tok_per_s": m * 1e3 / ms, "bytes_per_step": nbytes,
+            "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": roof, "frac_hbm_roofline": (m * 1e3 / ms) / roof}
+
+
+def bench_mimir(q8, wl, dev, weights, m: int, core_q4=None) -> dict:
     """One decode token (m streams): 513 skinny products in recurrence order,
     captured once into a graph and replayed; eager replay of the same launches
     is timed too.  With `core_q4` the 512 block products use int4 weights and
@@ -317,117 +391,35 @@ def bench_mimir(q8, wl, dev, weights, m: int, replays: int = 20, core_q4=None) -
 
     step()
     torch.cuda.synchronize()
-    eager_ms, _ = time_events(lambda i: step(), 3)
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        step()
-    torch.cuda.current_stream().wait_stream(s)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    g.replay()
-    torch.cuda.synchronize()
-    ms, _ = time_events(lambda i: g.replay(), replays)
-    nbytes = mimir_step_bytes(wl, m, int4_core=core_q4 is not None)
-    return {"m": m, "ms_per_step": ms, "tok_per_s": m * 1e3 / ms, "eager_ms_per_step": eager_ms,
-            "eager_tok_per_s": m * 1e3 / eager_ms, "bytes_per_step": nbytes,
-            "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": m * HBM_PEAK_GBPS * 1e9 / nbytes,
-            "frac_hbm_roofline": (m * 1e3 / ms) / (m * HBM_PEAK_GBPS * 1e9 / nbytes)}
+    eager = stats(time_region(lambda i: step(), 3)[0] for _ in range(3))
+    st = graph_us(step, 1, reps=10)
+    res = step_figures({key: v / 1e3 if key != "n" else v for key, v in st.items()}, m,
+                       mimir_step_bytes(wl, m, int4_core=core_q4 is not None))
+    res["eager_ms_per_step"] = eager
+    res["eager_tok_per_s"] = m * 1e3 / eager["median"]
+    return res
 
 
-def time_graph(fn, per_graph: int, reps: int = 3, trials: int = 3) -> float:
-    """Mean ms per call of `fn` captured `per_graph` times into one HIP graph,
-    best of `trials` timed regions of `reps` replays (launch-independent)."""
+def bench_mimir_products(q8, wl, dev, weights) -> dict:
+    """Per-product table of one batch-1 step: each of the five product shapes
+    graph-replayed on its own, rotating through the 32 blocks' weights (the
+    lm_head through two copies), against its HBM time at 8 TB/s."""
     import torch
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        fn()
-    torch.cuda.current_stream().wait_stream(s)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(per_graph):
-            fn()
-    g.replay()
-    torch.cuda.synchronize()
-    best = min(time_region(lambda i: g.replay(), reps)[0] for _ in range(trials))
-    return best / per_graph
-
-
-PREFILL_SWEEP = (16, 64, 256, 1024, 4096)
-
-
-def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP) -> dict:
-    """Q8 x Q8 prefill: qkv and gate_up on [P, 1536] activations, down on
-    [P, 4096] (block-0 weights), each product graph-replayed.  P = 256 is the
-    configured workload (activations with the seeded special rows); the sweep
-    over P also fits time = fixed + P * slope for the three products, the
-    pages' prefill measure, and for the products with their activation side
-    (RMSNorm + quantizer fused for qkv and gate_up, the plain quantizer for
-    down)."""
-    import torch
-    cfg = wl.CONFIGS["prefill_p256"]
-    gemms = []
+    out = {}
     for proj, (name, n, k) in enumerate(wl.BLOCK_SHAPES):
-        if name != "o":
-            gemms.append((name, n, k, weights[(0, proj)]))
-    per_p = {}
-    for P in sweep:
-        if P == 256:
-            xa = wl.prefill_act_bf16(cfg["xa_seed"], P, wl.HIDDEN)
-            xb = wl.prefill_act_bf16(cfg["xb_seed"], P, wl.INTER)
-        else:
-            xa = wl.prefill_act_bf16(cfg["xa_seed"] + P, P, wl.HIDDEN)
-            xb = wl.prefill_act_bf16(cfg["xb_seed"] + P, P, wl.INTER)
-        xs = {}
-        for kk, xn in ((wl.HIDDEN, xa), (wl.INTER, xb)):
-            xd_ = to_dev(xn, dev)
-            q, d = q8.quantize_act(xd_)
-            xs[kk] = (xd_, q, d)
-        rows, tot_us, ops, nbytes = {}, 0.0, 0, 0
-        for name, n, k, (wq, wd) in gemms:
-            _, xq, xd = xs[k]
-            y = torch.empty((P, n), dtype=torch.float32, device=dev)
-            us = time_graph(lambda: q8.gemm_prefill(wq, wd, xq, xd, out=y), 10 if P >= 1024 else 20) * 1e3
-            o = 2 * P * n * k
-            rows[name] = {"us": us, "TOPS": o / us / 1e6}
-            tot_us += us
-            ops += o
-            nbytes += prefill_bytes(n, k, P)
-        q_us = {}
-        for kk, (x_, q, d) in xs.items():
-            q_us[kk] = time_graph(lambda: q8.quantize_act(x_, out=(q, d)), 20) * 1e3
-        # the activation side of qkv / gate_up: RMSNorm of the fp32 residual
-        # rows, bf16, Q8_0 -- one fused launch, or norm then quantize
-        h_ = to_dev(wl.bf16_bits_to_f32(xa), dev)
-        _, hq, hd = xs[wl.HIDDEN]
-        fused_us = time_graph(lambda: q8.quantize_act_fused(h_, q8.PRO_RMSNORM, out=(hq, hd)), 20) * 1e3
-        nrm = torch.empty_like(h_)
-        chain_us = time_graph(lambda: (q8.rmsnorm(h_, out=nrm),
-                                       q8.quantize_act_fused(nrm, q8.PRO_F32, out=(hq, hd))), 20) * 1e3
-        tops = ops / tot_us / 1e6
-        per_p[P] = {"us_three_gemms": tot_us, "int_ops": ops, "TOPS": tops,
-                    "frac_int8_peak": tops / INT8_PEAK_TOPS, "bytes": nbytes,
-                    "us_per_token": tot_us / P, "per_gemm": rows,
-                    "quantize_act_us": sum(q_us.values()),
-                    "rmsnorm_quantize_fused_us": fused_us, "rmsnorm_then_quantize_us": chain_us,
-                    # qkv and gate_up read normed residual rows (fused prologue),
-                    # down reads the bf16 SwiGLU rows (plain quantizer)
-                    "us_products_with_activation_side": tot_us + 2 * fused_us + q_us[wl.INTER]}
-        log(f"prefill P={P}: {tot_us:.1f} us, {tops:.0f} TOPS ({100 * tops / INT8_PEAK_TOPS:.1f}% of int8 peak); "
-            f"norm+quantize fused {fused_us:.1f} us vs {chain_us:.1f} us in two launches")
-    ps = np.array(sorted(per_p), dtype=np.float64)
-    ts = np.array([per_p[int(P)]["us_three_gemms"] for P in ps])
-    big = ps >= 256
-    out = dict(per_p[256])
-    out["p_sweep"] = {str(P): v for P, v in per_p.items()}
-    if big.sum() >= 2:
-        ta = np.array([per_p[int(P)]["us_products_with_activation_side"] for P in ps])
-        for key, tt in (("fit_p_ge_256", ts), ("fit_p_ge_256_with_activation_side", ta)):
-            slope, fixed = np.polyfit(ps[big], tt[big], 1)
-            out[key] = {"fixed_us": float(fixed), "slope_us_per_token": float(slope),
-                        "slope_ms_per_token": float(slope) * 1e-3}
+        x = to_dev(wl.normal_act_bf16(9950 + proj, 1, k), dev)
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+        cnt = [0]
+
+        def call():
+            blk = cnt[0] % wl.N_BLOCKS
+            cnt[0] += 1
+            q8.gemm_skinny(*weights[(blk, proj)], x, out=y)
+
+        st = graph_us(call, 64)
+        hbm_us = gemv_bytes(n, k) / HBM_PEAK_GBPS / 1e3
+        out[name] = {"us": st, "hbm_us_at_8TBps": hbm_us, "frac_hbm": hbm_us / st["median"],
+                     "kernel": q8.kernel_name(q8.OP_SKINNY, n, k, 1)}
     return out
 
 
@@ -471,15 +463,16 @@ def bench_attn(q8, wl, dev, slabs) -> dict:
             cnt[0] += 1
             q8.attn_decode(q, kq, kd, vq, vd, t, scale, work=work, out=out)
 
-        us = time_graph(call, 2 * len(slabs)) * 1e3
+        st = graph_us(call, 2 * len(slabs))
+        us = st["median"]
         nb = attn_bytes(t)
-        res[str(t)] = {"us_per_call": us, "GBps": nb / us / 1e3, "frac_hbm": nb / us / 1e3 / HBM_PEAK_GBPS,
+        res[str(t)] = {"us_per_call": st, "GBps": nb / us / 1e3, "frac_hbm": nb / us / 1e3 / HBM_PEAK_GBPS,
                        "bytes_per_call": nb, "ms_per_token_128_layers": 128 * us / 1e3}
         log(f"attn t={t}: {us:.2f} us, {nb / us / 1e3:.0f} GB/s")
     return res
 
 
-def bench_mimir_with_kv(q8, wl, dev, weights, slabs, t: int = 512, replays: int = 10) -> dict:
+def bench_mimir_with_kv(q8, wl, dev, weights, slabs, t: int = 512) -> dict:
     """One batch-1 decode token with the int8 KV read: the 513 products of the
     Mimir step plus one decode-attention call after every qkv product (128
     virtual layers, 12 heads x 128, context t), graph-replayed.  Bytes per token
@@ -504,14 +497,14 @@ def bench_mimir_with_kv(q8, wl, dev, weights, slabs, t: int = 512, replays: int 
                 q8.attn_decode(q, kq, kd, vq, vd, t, scale, work=work, out=out)
                 layer += 1
 
-    ms = time_graph(step, 1, reps=replays)
-    nbytes = mimir_step_bytes(wl, 1) + 128 * attn_bytes(t)
-    return {"context": t, "ms_per_step": ms, "tok_per_s": 1e3 / ms, "bytes_per_step": nbytes,
-            "GBps": nbytes / ms / 1e6, "hbm_roofline_tok_per_s": HBM_PEAK_GBPS * 1e9 / nbytes,
-            "frac_hbm_roofline": (1e3 / ms) / (HBM_PEAK_GBPS * 1e9 / nbytes)}
+    st = graph_us(step, 1, reps=5)
+    res = step_figures({key: v / 1e3 if key != "n" else v for key, v in st.items()}, 1,
+                       mimir_step_bytes(wl, 1) + 128 * attn_bytes(t))
+    res["context"] = t
+    return res
 
 
-def bench_fused_step(q8, wl, dev, weights, t: int, replays: int = 10) -> dict:
+def bench_fused_step(q8, wl, dev, weights, t: int) -> dict:
     """One batch-1 decode token of the whole block -- the glue fused into the
     products (RMSNorm, RoPE, SwiGLU, residual adds), attention that appends the
     token's key and value to its int8 cache (its combine folded into the o
@@ -526,58 +519,132 @@ def bench_fused_step(q8, wl, dev, weights, t: int, replays: int = 10) -> dict:
     st = DecodeStep(core, weights["lm_head"], order, module_ends, t,
                     wl.rope_pair_rows(2 * wl.HIDDEN, 3 * wl.HIDDEN), wl.swiglu_pair_rows(2 * wl.INTER))
     st.h.copy_(to_dev(wl.bf16_bits_to_f32(wl.normal_act_bf16(9901, 1, wl.HIDDEN)), dev))
-    ms = time_graph(lambda: st.run(t), 1, reps=replays)
+    tr = graph_us(lambda: st.run(t), 1, reps=5)
     # per layer: qkv, attention, o, gate/up, down, and the attention's combine
     # launch where it is not folded into the o product (contexts above 1024)
     launches = len(order) * (5 + (1 if t > 1024 else 0)) + len(module_ends) + 1
-    nbytes = mimir_step_bytes(wl, 1) + 128 * attn_bytes(t)
+    res = step_figures({key: v / 1e3 if key != "n" else v for key, v in tr.items()}, 1,
+                       mimir_step_bytes(wl, 1) + 128 * attn_bytes(t))
+    res.update({"context": t, "launches_per_token": launches})
     del st
     torch.cuda.empty_cache()
-    return {"context": t, "ms_per_step": ms, "tok_per_s": 1e3 / ms, "launches_per_token": launches,
-            "bytes_per_step": nbytes, "GBps": nbytes / ms / 1e6,
-            "hbm_roofline_tok_per_s": HBM_PEAK_GBPS * 1e9 / nbytes,
-            "frac_hbm_roofline": (1e3 / ms) / (HBM_PEAK_GBPS * 1e9 / nbytes)}
+    return res
 
 
-def bench_sync_probe(q8, dev) -> dict:
-    """What one dependency edge of a decode step costs on this GPU: the
-    per-launch cost of an empty kernel under graph replay, and one grid-wide
-    barrier over 64 / 128 / 256 single-wave workgroups (the synchronization a
-    single-launch step would need between two dependent products)."""
+PREFILL_SWEEP = (16, 64, 256, 1024, 4096)
+
+
+def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP, int8_peak_measured=None) -> dict:
+    """Q8 x Q8 prefill: qkv and gate_up on [P, 1536] activations, down on
+    [P, 4096] (block-0 weights), each product graph-replayed.  P = 256 is the
+    configured workload (activations with the seeded special rows); the sweep
+    over P also fits time = fixed + P * slope for the three products, the
+    pages' prefill measure, and for the products with their activation side
+    (RMSNorm + quantizer fused for qkv and gate_up, the plain quantizer for
+    down)."""
     import torch
-    flags = q8.probe_barrier_flags(dev)
-    out = {"graph_node_us": time_graph(lambda: q8.probe_barrier(flags, 1, 0), 200) * 1e3}
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    bar = {}
-    for g in (64, 128, 256):
-        if g > cus:
-            continue
-        flags.zero_()
-        q8.probe_barrier(flags, g, 10)
-        t = []
-        for rounds in (100, 1100):
-            ms, _ = time_region(lambda i: q8.probe_barrier(flags, g, rounds), 3)
-            t.append(ms)
-        torch.cuda.synchronize()
-        if int(flags[-1].item()) != 0:
-            bar[str(g)] = None
-            continue
-        bar[str(g)] = (t[1] - t[0]) * 1e3 / 1000
-    out["grid_barrier_us"] = bar
+    cfg = wl.CONFIGS["prefill_p256"]
+    gemms = []
+    for proj, (name, n, k) in enumerate(wl.BLOCK_SHAPES):
+        if name != "o":
+            gemms.append((name, n, k, weights[(0, proj)]))
+    per_p = {}
+    for P in sweep:
+        if P == 256:
+            xa = wl.prefill_act_bf16(cfg["xa_seed"], P, wl.HIDDEN)
+            xb = wl.prefill_act_bf16(cfg["xb_seed"], P, wl.INTER)
+        else:
+            xa = wl.prefill_act_bf16(cfg["xa_seed"] + P, P, wl.HIDDEN)
+            xb = wl.prefill_act_bf16(cfg["xb_seed"] + P, P, wl.INTER)
+        xs = {}
+        for kk, xn in ((wl.HIDDEN, xa), (wl.INTER, xb)):
+            xd_ = to_dev(xn, dev)
+            q, d = q8.quantize_act(xd_)
+            xs[kk] = (xd_, q, d)
+        rows, tot_us, ops, nbytes = {}, 0.0, 0, 0
+        for name, n, k, (wq, wd) in gemms:
+            _, xq, xd = xs[k]
+            y = torch.empty((P, n), dtype=torch.float32, device=dev)
+            st = graph_us(lambda: q8.gemm_prefill(wq, wd, xq, xd, out=y), 10 if P >= 1024 else 20)
+            o = 2 * P * n * k
+            rows[name] = {"us": st, "TOPS": o / st["median"] / 1e6, "kernel": q8.kernel_name(q8.OP_PREFILL, n, k, P)}
+            tot_us += st["median"]
+            ops += o
+            nbytes += prefill_bytes(n, k, P)
+        q_us = {}
+        for kk, (x_, q, d) in xs.items():
+            q_us[kk] = graph_us(lambda: q8.quantize_act(x_, out=(q, d)), 20)["median"]
+        # the activation side of qkv / gate_up: RMSNorm of the fp32 residual
+        # rows, bf16, Q8_0 -- one fused launch, or norm then quantize
+        h_ = to_dev(wl.bf16_bits_to_f32(xa), dev)
+        _, hq, hd = xs[wl.HIDDEN]
+        fused_us = graph_us(lambda: q8.quantize_act_fused(h_, q8.PRO_RMSNORM, out=(hq, hd)), 20)["median"]
+        nrm = torch.empty_like(h_)
+        chain_us = graph_us(lambda: (q8.rmsnorm(h_, out=nrm),
+                                     q8.quantize_act_fused(nrm, q8.PRO_F32, out=(hq, hd))), 20)["median"]
+        tops = ops / tot_us / 1e6
+        per_p[P] = {"us_three_gemms": tot_us, "int_ops": ops, "TOPS": tops,
+                    "frac_int8_peak": tops / INT8_PEAK_TOPS,
+                    "frac_measured_int8_peak": tops / int8_peak_measured if int8_peak_measured else None,
+                    "bytes": nbytes, "us_per_token": tot_us / P, "per_gemm": rows,
+                    "quantize_act_us": sum(q_us.values()),
+                    "rmsnorm_quantize_fused_us": fused_us, "rmsnorm_then_quantize_us": chain_us,
+                    "us_products_with_activation_side": tot_us + 2 * fused_us + q_us[wl.INTER]}
+        log(f"prefill P={P}: {tot_us:.1f} us, {tops:.0f} TOPS ({100 * tops / INT8_PEAK_TOPS:.1f}% of int8 peak); "
+            + ", ".join(f"{nm} {r['us']['median']:.1f} us ({r['kernel']})" for nm, r in rows.items()))
+    ps = np.array(sorted(per_p), dtype=np.float64)
+    ts = np.array([per_p[int(P)]["us_three_gemms"] for P in ps])
+    big = ps >= 256
+    out = dict(per_p[256]) if 256 in per_p else {}
+    out["p_sweep"] = {str(P): v for P, v in per_p.items()}
+    if big.sum() >= 2:
+        ta = np.array([per_p[int(P)]["us_products_with_activation_side"] for P in ps])
+        for key, tt in (("fit_p_ge_256", ts), ("fit_p_ge_256_with_activation_side", ta)):
+            slope, fixed = np.polyfit(ps[big], tt[big], 1)
+            out[key] = {"fixed_us": float(fixed), "slope_us_per_token": float(slope),
+                        "slope_ms_per_token": float(slope) * 1e-3}
     return out
 
 
-def cpu_baseline(w_np, x, y_rows, y_sample, wq_sample=None, seconds: float = 10.0):
-    """The CPU leg, the only use of the oracle here: it quantizes the lm_head
+# ------------------------------------------------------------------ CPU baseline (the oracle)
+
+def _time_sampled(fn, full_rows: int, target_s: float = 0.3):
+    """Median seconds of fn(rows) over the full row count, from TRIALS runs
+    over a row sample sized so one run takes about target_s (all rows when that
+    fits), scaled to all rows.  Returns (seconds, fraction of rows used)."""
+    probe_rows = max(1, full_rows // 64)
+    t0 = time.perf_counter()
+    fn(probe_rows)
+    est_full = (time.perf_counter() - t0) * full_rows / probe_rows
+    frac = 1.0
+    while frac > 1 / 1024 and est_full * frac > target_s:
+        frac /= 2
+    rows = max(1, int(full_rows * frac))
+    ts = []
+    for _ in range(TRIALS):
+        t0 = time.perf_counter()
+        fn(rows)
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)) * full_rows / rows, rows / full_rows
+
+
+def cpu_baseline(wl, w_np, x_np, y_rows, y_sample, wq_sample=None):
+    """The CPU leg, the only use of the oracle here.  It quantizes the lm_head
     weights, checks GPU results sampled from the timed runs (the GEMV's output
     rows within the fp32 tolerance; the weight quantizer's codes and scales bit
-    for bit), and its fp64 W8A16 GEMV is timed on the host cores.  Returns
-    (baseline, parity)."""
+    for bit), then times the oracle on the host cores -- once with one thread
+    and once with all -- on each workload, over a row sample of each product
+    sized to about 0.3 s per run (median of five, scaled to all rows):
+    the lm_head GEMV (fp64 W8A16 path and exact-int Q8 x Q8 path), one Mimir
+    step at batch 1 and at batch 8 (the four products of one block times 128
+    plus the lm_head), and the three P = 256 prefill products (exact int32
+    block sums alone, and with the fp64 fold).  Returns (baseline, parity)."""
     import oracle
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    oracle.set_threads(threads)
+    all_threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    oracle.set_threads(all_threads)
+    t_start = time.perf_counter()
     oq, od = oracle.quantize_f32(w_np)
-    y_ref = oracle.w8a16(oq, od, x, rows=y_rows)[0]
+    y_ref = oracle.w8a16(oq, od, x_np, rows=y_rows)[0]
     parity = {"rows_checked": int(y_rows.size),
               "max_abs": float(np.max(np.abs(y_sample - y_ref))),
               "rel_l2": float(np.linalg.norm(y_sample - y_ref) / np.linalg.norm(y_ref))}
@@ -588,19 +655,147 @@ def cpu_baseline(w_np, x, y_rows, y_sample, wq_sample=None, seconds: float = 10.
         parity["weight_quantizer_rows_checked"] = int(rows.size)
         parity["weight_quantizer_bit_exact"] = exact
         parity["ok"] = parity["ok"] and exact
-    n, k = oq.shape
-    nbytes = gemv_bytes(n, k)
-    times = []
-    t_end = time.perf_counter() + seconds
-    while not times or (time.perf_counter() < t_end and len(times) < 20):
-        t0 = time.perf_counter()
-        oracle.w8a16(oq, od, x)
-        times.append(time.perf_counter() - t0)
-    best = min(times)
-    return ({"value": nbytes / best / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-             "sample": f"fp64 oracle W8A16 GEMV over all {n} x {k} rows of the lm_head workload, "
-                       f"{len(times)} runs, best {best * 1e3:.1f} ms",
-             "host_cpus_visible": os.cpu_count()}, parity)
+
+    n_lm, k_lm = oq.shape
+    xq_lm, xd_lm = oracle.quantize_bf16(x_np)
+    block = {}
+    for proj, (name, n, k) in enumerate(wl.BLOCK_SHAPES):
+        block[name] = oracle.quantize_f32(wl.normal_weights(wl.mimir_weight_seed(0, proj), n, k))
+    x1 = {k: wl.normal_act_bf16(9900 + k, 1, k) for k in (wl.HIDDEN, wl.INTER)}
+    x8 = {k: wl.normal_act_bf16(9910 + k, 8, k) for k in (wl.HIDDEN, wl.INTER)}
+    x8_lm = wl.normal_act_bf16(9920, 8, k_lm)
+    cfg5 = wl.CONFIGS["prefill_p256"]
+    xp = {wl.HIDDEN: oracle.quantize_bf16(wl.prefill_act_bf16(cfg5["xa_seed"], 256, wl.HIDDEN)),
+          wl.INTER: oracle.quantize_bf16(wl.prefill_act_bf16(cfg5["xb_seed"], 256, wl.INTER))}
+    ar = np.arange(n_lm, dtype=np.int64)
+
+    def layer_rows(xs):
+        # the block's four products over the first `frac` of each one's rows
+        def run(rows):
+            frac = rows / 8192
+            for name, (q, d) in block.items():
+                nr = max(1, int(q.shape[0] * frac))
+                oracle.w8a16(q, d, xs[q.shape[1]], rows=ar[:nr])
+        return run
+
+    prefill = [(q, d, xp[q.shape[1]]) for name, (q, d) in block.items() if name != "o"]
+
+    def prefill_run(exact_only):
+        def run(rows):
+            frac = rows / 8192
+            for q, d, (pq, pd) in prefill:
+                nr = max(1, int(q.shape[0] * frac))
+                if exact_only:
+                    oracle.block_dots(q[:nr], pq)
+                else:
+                    oracle.q8q8(q, d, pq, pd, rows=ar[:nr])
+        return run
+
+    jobs = {
+        "lm_head_gemv_fp64_w8a16": (lambda r: oracle.w8a16(oq, od, x_np, rows=ar[:r]), n_lm),
+        "lm_head_gemv_exact_int_q8q8": (lambda r: oracle.q8q8(oq, od, xq_lm, xd_lm, rows=ar[:r]), n_lm),
+        "mimir_layer_b1": (layer_rows(x1), 8192),
+        "lm_head_b8": (lambda r: oracle.w8a16(oq, od, x8_lm, rows=ar[:r]), n_lm),
+        "mimir_layer_b8": (layer_rows(x8), 8192),
+        "prefill_p256_exact_int_block_sums": (prefill_run(True), 8192),
+        "prefill_p256_int_sums_fp64_fold": (prefill_run(False), 8192),
+    }
+    per_threads = {}
+    for threads in (1, all_threads):
+        oracle.set_threads(threads)
+        secs, fracs = {}, {}
+        for key, (fn, rows) in jobs.items():
+            secs[key], fracs[key] = _time_sampled(fn, rows)
+        lm1 = secs["lm_head_gemv_fp64_w8a16"]
+        step1 = 128 * secs["mimir_layer_b1"] + lm1
+        step8 = 128 * secs["mimir_layer_b8"] + secs["lm_head_b8"]
+        pf_ops = sum(2 * 256 * q.shape[0] * q.shape[1] for q, _, _ in prefill)
+        per_threads[str(threads)] = {
+            "lm_head_gemv_GBps": gemv_bytes(n_lm, k_lm) / lm1 / 1e9,
+            "lm_head_gemv_ms": lm1 * 1e3,
+            "lm_head_gemv_q8q8_ms": secs["lm_head_gemv_exact_int_q8q8"] * 1e3,
+            "mimir_step_b1_ms": step1 * 1e3, "mimir_step_b1_tok_per_s": 1.0 / step1,
+            "mimir_step_b8_ms": step8 * 1e3, "mimir_step_b8_tok_per_s": 8.0 / step8,
+            "prefill_p256_exact_int_ms": secs["prefill_p256_exact_int_block_sums"] * 1e3,
+            "prefill_p256_exact_int_TOPS": pf_ops / secs["prefill_p256_exact_int_block_sums"] / 1e12,
+            "prefill_p256_int_plus_fp64_fold_ms": secs["prefill_p256_int_sums_fp64_fold"] * 1e3,
+            "row_fraction_timed": {k: r4(v) for k, v in fracs.items()},
+        }
+        log(f"oracle, {threads} thread(s): lm_head GEMV {lm1 * 1e3:.1f} ms, step b1 {step1 * 1e3:.0f} ms, "
+            f"b8 {step8 * 1e3:.0f} ms, prefill P=256 {secs['prefill_p256_int_sums_fp64_fold'] * 1e3:.0f} ms")
+    oracle.set_threads(all_threads)
+    allc = per_threads[str(all_threads)]
+    import platform
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    base = {"value": round(allc["lm_head_gemv_GBps"], 3), "unit": "GB/s", "cores": all_threads, "kind": "oracle",
+            "sample": (f"fp64 oracle W8A16 GEMV of the lm_head workload ({n_lm} x {k_lm}) on {all_threads} threads, "
+                       "median of 5 runs over a row sample of about 0.3 s, scaled to all rows; the same on one thread "
+                       "and for the Mimir step (b1, b8) and P=256 prefill in per_threads"),
+            "per_threads": per_threads, "cpu_model": cpu_model or platform.processor(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+            "leg_seconds": round(time.perf_counter() - t_start, 1)}
+    return base, parity
+
+
+# ------------------------------------------------------------------ summary
+
+def summarize(extras: dict, cpu) -> dict:
+    """The figures a reader needs first, flat and rounded."""
+    s = {}
+    g = extras.get("gemv_1536x1536_b1")
+    if g:
+        s["gemv_1536_rotating_us"] = r4(g["rotating"]["us_per_gemv"]["median"])
+        s["gemv_1536_rotating_gemv_per_s"] = r4(g["rotating"]["gemv_per_s"])
+        s["gemv_1536_rotating_frac_hbm"] = r4(g["rotating"]["frac_hbm_peak"])
+        s["gemv_1536_single_us"] = r4(g["single"]["us_per_gemv"]["median"])
+    for m in (1, 2, 4, 8):
+        st = extras.get(f"mimir_step_b{m}")
+        if st:
+            s[f"mimir_b{m}_tok_per_s"] = r4(st["tok_per_s"])
+            s[f"mimir_b{m}_frac_roofline"] = r4(st["frac_hbm_roofline"])
+    for t in (512, 4096):
+        st = extras.get(f"fused_step_b1_ctx{t}")
+        if st:
+            s[f"fused_step_ctx{t}_tok_per_s"] = r4(st["tok_per_s"])
+    pf = extras.get("prefill_p256")
+    if pf and "us_three_gemms" in pf:
+        s["prefill_p256_us"] = r4(pf["us_three_gemms"])
+        s["prefill_p256_TOPS"] = r4(pf["TOPS"])
+        s["prefill_p256_frac_int8_peak"] = r4(pf["frac_int8_peak"])
+        s["prefill_p256_frac_measured_int8_peak"] = r4(pf["frac_measured_int8_peak"])
+        p4 = pf.get("p_sweep", {}).get("4096")
+        if p4:
+            s["prefill_p4096_frac_int8_peak"] = r4(p4["frac_int8_peak"])
+        if "fit_p_ge_256" in pf:
+            s["prefill_fit_fixed_us"] = r4(pf["fit_p_ge_256"]["fixed_us"])
+            s["prefill_fit_slope_us_per_token"] = r4(pf["fit_p_ge_256"]["slope_us_per_token"])
+    at = extras.get("attn_decode_int8kv")
+    if at:
+        for t in ("512", "4096"):
+            s[f"attn_t{t}_us"] = r4(at[t]["us_per_call"]["median"])
+            s[f"attn_t{t}_frac_hbm"] = r4(at[t]["frac_hbm"])
+    lb = extras.get("lm_head_batches")
+    if lb:
+        for m in (1, 2, 4, 8):
+            s[f"lm_head_bf16_b{m}_us"] = r4(lb["q8_0"][f"bf16_b{m}"]["us_per_call"]["median"])
+    if "read_probe" in extras:
+        s["read_peak_GBps"] = r4(extras["read_probe"]["GBps"])
+    if "copy_probe" in extras:
+        s["copy_GBps_read_plus_write"] = r4(extras["copy_probe"]["GBps_read_plus_write"])
+    if "mfma_i8_probe" in extras:
+        s["int8_mfma_measured_TOPS"] = r4(extras["mfma_i8_probe"]["TOPS"])
+    if cpu:
+        one = cpu["per_threads"]["1"]
+        s["cpu_oracle_1t_lm_head_GBps"] = r4(one["lm_head_gemv_GBps"])
+        s["cpu_oracle_1t_mimir_b1_tok_per_s"] = r4(one["mimir_step_b1_tok_per_s"])
+    return s
 
 
 # ------------------------------------------------------------------ main
@@ -614,13 +809,21 @@ def main() -> int:
                     help="time only the headline GEMV (no other workloads, no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
-                    help="run only the P=256 prefill GEMMs (for hardware-counter passes)")
+                    help="run only the prefill products (for hardware-counter passes)")
+    ap.add_argument("--prefill-p", type=int, nargs="*", default=[256],
+                    help="P values of --prefill-only")
+    ap.add_argument("--details", default=None, help="also write the full per-figure details (JSON) to this path")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the weight-streaming products shard by output "
               "rows with no collective, so a multi-GPU figure is N independent copies of this "
               "one; run with --gpus 1.", file=sys.stderr)
         return 2
+
+    want_cpu = not args.metric_only and not args.no_cpu_baseline and not args.prefill_only
+    if want_cpu:
+        import oracle
+        oracle.ensure_built()                 # before the GPU is touched: no compiler after that
 
     import torch
     import int8_weight_streaming_amd as q8
@@ -640,7 +843,8 @@ def main() -> int:
             if name != "o":
                 weights[(0, proj)] = quantize_on_device(
                     q8, wl.normal_weights(wl.mimir_weight_seed(0, proj), n_, k_), dev)
-        print(json.dumps({"prefill_p256": bench_prefill(q8, wl, dev, weights, sweep=(256,))}), flush=True)
+        res = bench_prefill(q8, wl, dev, weights, sweep=tuple(args.prefill_p))
+        print(json.dumps({"prefill": res}), flush=True)
         return 0
 
     # ---- headline: lm_head-shaped GEMV, batch 1
@@ -662,45 +866,43 @@ def main() -> int:
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
-    kern_ms, wall = time_region(call, args.steps)
+    kern_ms, wall = time_region(call, args.steps)          # the contract's timed region
     ms_per_step = wall * 1e3 / args.steps
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
-    log(f"lm_head gemv: {kern_ms * 1e3:.2f} us/kernel, {achieved:.1f} GB/s kernel, {value:.1f} GB/s wall")
+    trials = stats(time_region(call, max(args.steps, 20))[0] * 1e3 for _ in range(TRIALS))
+    log(f"lm_head gemv: {kern_ms * 1e3:.2f} us/kernel, {achieved:.1f} GB/s kernel, {value:.1f} GB/s wall; "
+        f"trials median {trials['median']:.2f} us")
 
     # rows of the timed output, checked against the oracle by the CPU leg
     y_rows = np.random.Generator(np.random.PCG64(77)).choice(n, size=4096, replace=False)
     y_sample = y.cpu().numpy()[y_rows].astype(np.float64)
-    q4_lm = wquant = wq_sample = None
+    extras = {}
+    wq_sample = None
     if not args.metric_only:
         log("lm_head products at batch 1-8, int4 and Q8_0")
         w_dev = to_dev(w_np, dev)
-        q4_lm = bench_lm_head_batches(q8, wl, dev, w_dev, copies)
-        wquant, wq_sample = bench_quantize_weights(q8, w_dev)
-        log(f"weight quantizer: {wquant['us_per_call']:.1f} us for {n}x{k} fp32, {wquant['GBps']:.0f} GB/s")
+        extras["lm_head_batches"] = bench_lm_head_batches(q8, wl, dev, w_dev, copies)
+        extras["weight_quantize_262144x1536"], wq_sample = bench_quantize_weights(q8, w_dev)
         del w_dev
         torch.cuda.empty_cache()
 
-    extras = {}
-    probe = bench_read_probe(q8, dev)
-    log(f"read probe: {probe['GBps']:.1f} GB/s")
-    extras["read_probe"] = probe
-    measured_peak = probe["GBps"]
+    extras["read_probe"] = bench_read_probe(dev)
+    measured_peak = extras["read_probe"]["GBps"]
     extras["copy_probe"] = bench_copy_probe(dev)
     log(f"copy probe: {extras['copy_probe']['GBps_read_plus_write']:.1f} GB/s (read + write)")
+    extras["mfma_i8_probe"] = bench_mfma_probe(dev)
 
-    if q4_lm is not None:
-        extras["lm_head_batches"] = q4_lm
-    if wquant is not None:
-        extras["weight_quantize_262144x1536"] = wquant
     if not args.metric_only:
         log("gemv 1536x1536")
         extras["gemv_1536x1536_b1"] = bench_gemv_1536(q8, wl, dev)
         log("loading Mimir weight set (32 blocks in Q8_0 and int4, lm_head in Q8_0)")
         weights, core_q4 = load_mimir(q8, wl, dev)
+        extras["mimir_products_b1"] = bench_mimir_products(q8, wl, dev, weights)
         for m in (1, 2, 4, 8):
             log(f"mimir step m={m}")
             extras[f"mimir_step_b{m}"] = bench_mimir(q8, wl, dev, weights, m)
+            log(f"  {extras[f'mimir_step_b{m}']['tok_per_s']:.0f} tok/s")
         for m in (1, 2, 4, 8):
             log(f"mimir step, int4 core + int8 vocab, m={m}")
             extras[f"mimir_step_int4core_b{m}"] = bench_mimir(q8, wl, dev, weights, m, core_q4=core_q4)
@@ -716,15 +918,16 @@ def main() -> int:
             log(f"fused decode step (glue in the products, KV append) at context {t}")
             extras[f"fused_step_b1_ctx{t}"] = bench_fused_step(q8, wl, dev, weights, t)
         log("prefill P sweep")
-        extras["prefill_p256"] = bench_prefill(q8, wl, dev, weights)
+        extras["prefill_p256"] = bench_prefill(q8, wl, dev, weights,
+                                               int8_peak_measured=extras["mfma_i8_probe"]["TOPS"])
         del weights
         log("decode synchronization probe")
-        extras["sync_probe"] = bench_sync_probe(q8, dev)
+        extras["sync_probe"] = bench_sync_probe(dev)
 
     cpu = parity = None
-    if not args.metric_only and not args.no_cpu_baseline:
-        log("cpu baseline (oracle): sampled parity of the timed outputs, then the oracle GEMV timed")
-        cpu, parity = cpu_baseline(w_np, x_np, y_rows, y_sample, wq_sample)
+    if want_cpu:
+        log("cpu baseline (oracle): sampled parity of the timed outputs, then the oracle timed")
+        cpu, parity = cpu_baseline(wl, w_np, x_np, y_rows, y_sample, wq_sample)
     del w_np
 
     torch.cuda.synchronize()
@@ -763,17 +966,26 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
+                     "kernel": q8.kernel_name(q8.OP_SKINNY, n, k, 1),
                      "kernel_us": round(kern_ms * 1e3, 3),
+                     "kernel_us_trials": {key: r4(v) for key, v in trials.items()},
+                     "measured_read_peak_GBps": round(measured_peak, 1),
                      "frac_of_measured_read_peak": round(achieved / measured_peak, 4)},
-        "cpu_baseline": cpu,
+        "summary": summarize(extras, cpu),
+        "cpu_baseline": None if cpu is None else {key: cpu[key] for key in
+                                                  ("value", "unit", "cores", "kind", "sample", "cpu_model")},
         "parity_sample": parity,
-        "extras": extras,
         "gpu_state": {"before": state_before, "after": gpu_state()},
         "context": {"pages_gemv_bf16_rtx3060_GBps": 338.7, "pages_int8_decode_rtx3060_tok_s": 46.7,
                     "pages_q8_decode_zen5_1t_ms_per_tok": 7.7, "pages_q8_prefill_slope_zen5_ms_per_tok": 0.346},
     }
     if "mimir_step_b1" in extras:
         result["mimir_tok_s"] = round(extras["mimir_step_b1"]["tok_per_s"], 1)
+    details = {"extras": extras, "cpu_baseline": cpu}
+    if args.details:
+        with open(args.details, "w") as f:
+            json.dump(details, f)
+    print("[bench] details " + json.dumps(details), file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
     return 0 if parity is None or parity["ok"] else 1
 

@@ -1,11 +1,12 @@
 /*
- * q8probe.h -- measurement utility shipped beside q8stream: an HBM read probe.
+ * q8probe.h -- measurement probes of the benchmark, built as their own library
+ * (libq8probe.so) beside q8stream.  Not part of the computation.
  *
- * Not part of the computation.  The benchmark uses it to measure the device's
- * attainable read bandwidth, the ceiling that the weight-streaming products are
- * compared with [Frigg README, "The machine": the bench vram table quotes a
- * plain read probe and a copy probe beside the GEMV, and ceilings use the
- * measured figure, not the nominal one].
+ * The benchmark quotes measured ceilings next to the published ones [Frigg
+ * README, "The machine": a plain read probe and a copy probe are timed beside
+ * the GEMV, and the ceilings use the measured figure, not the nominal one].
+ * Error codes and conventions are those of q8stream.h (host-side validation
+ * before any HIP call; Q8_ERR_DEVICE without a usable device).
  */
 #ifndef Q8PROBE_H
 #define Q8PROBE_H
@@ -19,15 +20,16 @@
 extern "C" {
 #endif
 
-/* Read `bytes` bytes (a positive multiple of 16) from the 16-byte aligned
- * device buffer `src` with 16-byte loads and write one 32-bit checksum per
- * workgroup into `sink` (at least q8_probe_sink_words() words, caller-owned),
- * so that the loads cannot be removed.  Same error conventions as q8stream. */
-q8_status q8_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
-
-/* Number of 32-bit words q8_probe_read writes into `sink` on the current device
- * (0 if there is no usable device). */
-int64_t q8_probe_sink_words(void);
+/* Read `bytes` bytes (a positive multiple of 16, at most 2^40) of the 16-byte
+ * aligned device buffer `src` once, with the decode product's access pattern:
+ * one workgroup of 256 threads per contiguous span of 256 * loads_per_thread *
+ * 16 bytes, every thread issuing its loads_per_thread (4, 8, 12 or 16)
+ * non-temporal 16-byte loads before using any.  The loaded words are folded
+ * into a checksum that is written to sink[0] (a caller-owned 4-byte aligned
+ * int32 word) only in a case that never arises for the benchmark's buffers, so
+ * the loads cannot be removed and nothing else is written. */
+q8_status q8_probe_read(const void* src, int64_t bytes, int loads_per_thread, uint32_t* sink,
+                        hipStream_t stream);
 
 /* Grid-barrier probe: `workgroups` single-wave workgroups (1 .. number of
  * compute units) pass `rounds` grid-wide barriers one after another, the way a
@@ -51,6 +53,14 @@ q8_status q8_probe_barrier(uint32_t* flags, int workgroups, int rounds, hipStrea
 
 /* Words q8_probe_barrier needs in `flags`. */
 int64_t q8_probe_barrier_words(void);
+
+/* int8 matrix-core probe: `workgroups` workgroups of four waves, each wave
+ * running `iters` rounds of eight independent v_mfma_i32_32x32x32_i8 chains
+ * (65,536 integer operations per instruction), so workgroups * 4 * iters * 8 *
+ * 65,536 operations; the timed rate is the chip's sustained int8 matrix rate.
+ * sink: one caller-owned int32 word, written only in a case the probe's
+ * operands never produce.  1 <= workgroups <= 2^20, 1 <= iters <= 2^24. */
+q8_status q8_probe_mfma_i8(int workgroups, int iters, int32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

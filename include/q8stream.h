@@ -131,7 +131,7 @@ q8_status q8_gemm_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_
 
 /* Q8 x Q8 prefill product for p activation rows (0 <= p <= 4,194,240).  For K
  * a multiple of 512 (and K a multiple of 256 with at least as many 64 x 64
- * output tiles as compute units) the kernels use a fixed 38-80 KiB of LDS per
+ * output tiles as compute units) the kernels use a fixed 36-80 KiB of LDS per
  * workgroup, for K up to 2^24.  For any other K a workgroup keeps the binary16
  * scales of its rows for the whole of K in LDS: 36 KiB + 128 bytes per
  * 32-element block must fit the device's per-workgroup LDS (K <= 7168 with 64
@@ -172,8 +172,8 @@ typedef enum { Q8_OP_SKINNY = 0, Q8_OP_PREFILL = 1, Q8_OP_Q4_SKINNY = 2 } q8_op;
 q8_status q8_kernel_name(int op, int64_t n, int64_t k, int64_t rows, int act, char* buf, int64_t buf_len);
 
 /* Decode attention over a Q8_0 key/value cache, one query row per head and no
- * mask [Frigg README: "Masks" (decode passes no mask: one query against the
- * whole cache), "Cache" (one static slab [heads][4096][128] per virtual layer
+ * mask [Frigg README: "Masks" (the single decode query attends to every cached
+ * row unmasked), "Cache" (one static slab [heads][4096][128] per virtual layer
  * for K and for V), "The model, as verified" (12 heads of head_dim 128,
  * multi-head attention: one key/value head per query head)]:
  *

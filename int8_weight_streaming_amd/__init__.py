@@ -51,8 +51,6 @@ EXPORTED = (
 )
 OP_SKINNY, OP_PREFILL, OP_Q4_SKINNY = 0, 1, 2
 ATTN_SCRATCH_WORDS = 262144
-PROBE_EXPORTED = ("q8_probe_read", "q8_probe_sink_words", "q8_probe_barrier",
-                  "q8_probe_barrier_words")
 
 
 class Q8Error(RuntimeError):
@@ -92,12 +90,6 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q8_kernel_name.restype = I
     L.q8_attn_work_words.argtypes = [I64, I64]
     L.q8_attn_work_words.restype = I64
-    L.q8_probe_read.argtypes = [P, I64, P, P]
-    L.q8_probe_read.restype = I
-    L.q8_probe_sink_words.restype = I64
-    L.q8_probe_barrier.argtypes = [P, I, I, P]
-    L.q8_probe_barrier.restype = I
-    L.q8_probe_barrier_words.restype = I64
     L.q4_quantize_weights.argtypes = [P, I64, I64, P, P, P]
     L.q4_gemm_skinny.argtypes = [P, P, I64, I64, I64, I, P, P, P, P]
     L.q8_gemm_fused.argtypes = [P, P, I64, I64, I64, I, P, I, P, I64, I64, P]
@@ -541,34 +533,3 @@ def kernel_name(op: int, n: int, k: int, rows: int, act: int = Q8_ACT_BF16) -> s
     _check("q8_kernel_name", load_library().q8_kernel_name(
         int(op), int(n), int(k), int(rows), int(act), C.cast(buf, C.c_void_p), len(buf)))
     return buf.value.decode()
-
-
-# ------------------------------------------------------------------ measurement utility
-
-def probe_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
-    """Stream every byte of `buf` (read-only) with the library's HBM read probe."""
-    if not buf.is_cuda or not buf.is_contiguous():
-        raise ValueError("buf must be a contiguous device tensor")
-    L = load_library()
-    words = max(1, L.q8_probe_sink_words())
-    if sink is None:
-        sink = torch.empty((words,), dtype=torch.int32, device=buf.device)
-    elif sink.dtype != torch.int32 or not sink.is_cuda or not sink.is_contiguous() or sink.numel() < words:
-        raise ValueError(f"sink must be a contiguous int32 device tensor of >= {words} words")
-    nbytes = buf.numel() * buf.element_size()
-    _check("q8_probe_read", L.q8_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream()))
-    return sink
-
-
-def probe_barrier_flags(device) -> torch.Tensor:
-    """A zero-filled flag buffer for probe_barrier."""
-    return torch.zeros((load_library().q8_probe_barrier_words(),), dtype=torch.int32, device=device)
-
-
-def probe_barrier(flags: torch.Tensor, workgroups: int, rounds: int) -> None:
-    """Enqueue `rounds` grid-wide barriers over `workgroups` single-wave
-    workgroups (rounds = 0: an empty kernel).  After synchronizing, a non-zero
-    last word of `flags` means a barrier timed out and the measurement is void."""
-    if flags.dtype != torch.int32 or not flags.is_cuda or flags.numel() < load_library().q8_probe_barrier_words():
-        raise ValueError("flags must come from probe_barrier_flags()")
-    _check("q8_probe_barrier", load_library().q8_probe_barrier(_ptr(flags), workgroups, rounds, _stream()))

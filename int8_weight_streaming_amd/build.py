@@ -1,7 +1,8 @@
 """Build the q8stream shared library (gfx950) in-tree with hipcc.
 
 Each source is compiled to an object in ``_build/`` (in parallel), then linked
-into ``int8_weight_streaming_amd/libq8stream.so``.
+into ``int8_weight_streaming_amd/libq8stream.so``; the benchmark's measurement
+probes are linked into their own ``libq8probe.so``.
 """
 from __future__ import annotations
 
@@ -17,8 +18,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq8stream.so")
 
-SOURCES = ["q8_api.cpp", "q8_quantize.hip", "q8_skinny.hip", "q8_prefill.hip", "q8_attn.hip", "q4_skinny.hip", "q8_fused.hip",
-           "q8_probe.hip"]
+SOURCES = ["q8_api.cpp", "q8_quantize.hip", "q8_skinny.hip", "q8_prefill.hip", "q8_attn.hip", "q4_skinny.hip",
+           "q8_fused.hip"]
+PROBE_SOURCES = ["q8_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libq8probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -47,18 +50,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -5,8 +5,8 @@
 //
 // one bf16 query row per head against t rows of a static cache slab
 // [heads][t_cap][128] whose K and V are Q8_0 (int8 codes, one binary16 scale
-// per 32 consecutive elements of a row) [Frigg README: "Masks" (decode passes
-// no mask, one query against the whole cache), "Cache" (one static slab of
+// per 32 consecutive elements of a row) [Frigg README: "Masks" (the single
+// decode query attends to every cached row unmasked), "Cache" (one static slab of
 // [heads][4096][128] per virtual layer for K and for V), "The model, as
 // verified" (12 heads of 128, multi-head attention), the bytes-per-token table
 // (an int8 KV read per decoded token)].

@@ -220,8 +220,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kStreamSlice = 2 * 32 * kPitch + 64 * 16;   // operand rows + per-lane scales
-constexpr int kStreamLds = 4 * kStreamSlice;              // 40,960 B: three workgroups per CU
+constexpr int kStreamSlice = 2 * 32 * kPitch;             // one wave's operand rows (scales stay in registers)
+constexpr int kStreamLds = 4 * kStreamSlice;              // 36,864 B per workgroup
 constexpr int kStreamWgPerCu = 3;
 constexpr int64_t kStreamMaxK = int64_t(1) << 24;         // 32-bit buffer offsets
 

@@ -1,10 +1,19 @@
-// q8_probe.hip -- HBM read-bandwidth probe (measurement utility).
+// q8_probe.hip -- measurement probes of the benchmark (libq8probe.so; not part
+// of the q8stream library).
 //
-// Each workgroup streams one contiguous span of the buffer with 16-byte
-// non-temporal loads, four in flight per lane, and folds them into an xor
-// checksum; one word per workgroup is written so the loads stay live.
-// Contiguous spans per workgroup keep each DRAM page's reads together, which
-// measured faster on MI355X than a grid-stride walk over the whole buffer.
+//  * HBM read probe.  Streams a buffer with the access pattern of the decode
+//    product at its best: every workgroup reads one contiguous span of
+//    256 x LPT x 16 bytes, each thread issues all of its LPT 16-byte
+//    non-temporal loads before it uses any (the decode product issues a whole
+//    K tile of a row group the same way), and the grid has one workgroup per
+//    span, so the hardware keeps as many spans in flight as occupancy allows.
+//    LPT (loads per thread) is a parameter; the benchmark sweeps it and takes
+//    the fastest as the measured read peak.
+//  * Grid-barrier probe: what one dependency edge would cost inside a single
+//    persistent launch, against a graph-replayed launch boundary.
+//  * int8 matrix-core probe: independent chains of v_mfma_i32_32x32x32_i8 per
+//    wave, so the sustained int8 rate of the chip (at whatever clock it holds
+//    under that load) can be quoted beside the published peak.
 #include "q8probe.h"
 #include "q8_device.hpp"
 
@@ -12,33 +21,27 @@
 
 namespace {
 
-constexpr int kProbeBlocksPerCu = 16;
+// ---- HBM read probe
 
-__global__ __launch_bounds__(256) void probe_read_kernel(const q8::u32x4* __restrict__ src,
-                                                         int64_t n16, uint32_t* __restrict__ sink) {
-    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
-    const int64_t b0 = (int64_t)blockIdx.x * per;
-    const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
-    q8::u32x4 acc = {0u, 0u, 0u, 0u};
-    int64_t i = b0 + threadIdx.x;
-    for (; i + 3 * 256 < b1; i += 4 * 256) {
-        const q8::u32x4 a = __builtin_nontemporal_load(src + i);
-        const q8::u32x4 b = __builtin_nontemporal_load(src + i + 256);
-        const q8::u32x4 c = __builtin_nontemporal_load(src + i + 512);
-        const q8::u32x4 d = __builtin_nontemporal_load(src + i + 768);
-        acc ^= a ^ b ^ c ^ d;
+template <int LPT>
+__global__ __launch_bounds__(256) void probe_read_kernel(const q8::u32x4* __restrict__ src, int64_t n16,
+                                                         uint32_t* __restrict__ sink) {
+    const int64_t base = (int64_t)blockIdx.x * (256 * LPT) + threadIdx.x;
+    q8::u32x4 v[LPT];
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+        const int64_t i = base + 256 * j;
+        v[j] = __builtin_nontemporal_load(src + (i < n16 ? i : n16 - 1));
     }
-    for (; i < b1; i += 256) acc ^= __builtin_nontemporal_load(src + i);
-    uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
-    __shared__ uint32_t red[256];
-    red[threadIdx.x] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t s = 0;
-        for (int t = 0; t < 256; ++t) s ^= red[t];
-        sink[blockIdx.x] = s;
-    }
+    q8::u32x4 acc = v[0];
+#pragma unroll
+    for (int j = 1; j < LPT; ++j) acc ^= v[j];
+    const uint32_t s = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    // one word per workgroup keeps the loads live; lane 0 of wave 0 writes it
+    // only if the xor of everything is a value no buffer here produces
+    if (s == 0x9E3779B9u && threadIdx.x == 0) sink[0] = s;
 }
+
 // ---- grid-barrier probe
 
 constexpr int kBarReplicas = 8;                // one flag array per XCD
@@ -76,6 +79,28 @@ __global__ __launch_bounds__(64) void probe_barrier_kernel(unsigned* __restrict_
     }
 }
 
+// ---- int8 matrix-core probe
+
+// Eight independent accumulation chains per wave, `iters` rounds of eight
+// v_mfma_i32_32x32x32_i8 each (65,536 integer operations per instruction).
+// The result is written only under a condition the operands never meet, so the
+// chains stay live without a store per wave.
+__global__ __launch_bounds__(256) void probe_mfma_i8_kernel(int iters, int* __restrict__ sink) {
+    const int l = threadIdx.x;
+    const q8::i32x4 a = {l, l + 1, l + 2, l + 3};
+    q8::i32x16 c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = (q8::i32x16){};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a, c[j], 0, 0, 0);
+    }
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s ^= c[j][0] ^ c[j][15];
+    if (s == 0x7FEDCBA9 && l == 0) sink[0] = s;
+}
+
 int cu_count_current() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -84,20 +109,35 @@ int cu_count_current() {
     return cus;
 }
 
+template <int LPT>
+hipError_t launch_read(const void* src, int64_t n16, uint32_t* sink, hipStream_t stream) {
+    const int64_t grid = (n16 + 256 * LPT - 1) / (256 * LPT);
+    probe_read_kernel<LPT><<<(unsigned)grid, 256, 0, stream>>>(reinterpret_cast<const q8::u32x4*>(src), n16,
+                                                                sink);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-extern "C" int64_t q8_probe_sink_words(void) { return (int64_t)cu_count_current() * kProbeBlocksPerCu; }
-
-extern "C" q8_status q8_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
-    if (bytes <= 0 || bytes % 16 != 0) return Q8_ERR_SHAPE;
+extern "C" q8_status q8_probe_read(const void* src, int64_t bytes, int loads_per_thread, uint32_t* sink,
+                                   hipStream_t stream) {
+    if (bytes <= 0 || bytes % 16 != 0 || bytes > ((int64_t)1 << 40)) return Q8_ERR_SHAPE;
+    if (loads_per_thread != 4 && loads_per_thread != 8 && loads_per_thread != 12 && loads_per_thread != 16)
+        return Q8_ERR_SHAPE;
     if (!src || !sink) return Q8_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return Q8_ERR_ALIGN;
-    const int cus = cu_count_current();
-    if (cus <= 0) return Q8_ERR_DEVICE;
+    if (cu_count_current() <= 0) return Q8_ERR_DEVICE;
+    if ((bytes / 16 + 1023) / 1024 >= ((int64_t)1 << 31)) return Q8_ERR_SHAPE;
     (void)hipGetLastError();
-    probe_read_kernel<<<cus * kProbeBlocksPerCu, 256, 0, stream>>>(
-        reinterpret_cast<const q8::u32x4*>(src), bytes / 16, sink);
-    return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ERR_HIP;
+    const int64_t n16 = bytes / 16;
+    hipError_t e;
+    switch (loads_per_thread) {
+        case 4: e = launch_read<4>(src, n16, sink, stream); break;
+        case 8: e = launch_read<8>(src, n16, sink, stream); break;
+        case 12: e = launch_read<12>(src, n16, sink, stream); break;
+        default: e = launch_read<16>(src, n16, sink, stream); break;
+    }
+    return e == hipSuccess ? Q8_OK : Q8_ERR_HIP;
 }
 
 extern "C" int64_t q8_probe_barrier_words(void) { return (int64_t)kBarErr + 1; }
@@ -110,5 +150,15 @@ extern "C" q8_status q8_probe_barrier(uint32_t* flags, int workgroups, int round
     if (workgroups < 1 || workgroups > cus || workgroups > kBarStride || rounds < 0) return Q8_ERR_SHAPE;
     (void)hipGetLastError();
     probe_barrier_kernel<<<workgroups, 64, 0, stream>>>(flags, rounds);
+    return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ERR_HIP;
+}
+
+extern "C" q8_status q8_probe_mfma_i8(int workgroups, int iters, int32_t* sink, hipStream_t stream) {
+    if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24)) return Q8_ERR_SHAPE;
+    if (!sink) return Q8_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(sink) & 3u) return Q8_ERR_ALIGN;
+    if (cu_count_current() <= 0) return Q8_ERR_DEVICE;
+    (void)hipGetLastError();
+    probe_mfma_i8_kernel<<<workgroups, 256, 0, stream>>>(iters, sink);
     return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ERR_HIP;
 }

@@ -23,22 +23,39 @@ _CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
            "-Wall", "-shared", "-fPIC"]
 
 
+def _stale() -> bool:
+    return not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+
+
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (plain C, OpenMP); returns the library path."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    """Compile the oracle with gcc (plain C, OpenMP) into ``liboracle.so``.
+
+    Runs a compiler in a child process: call it only from a process that has
+    not initialised a GPU (the build step, the test session's start, the
+    benchmark's start)."""
+    if force or _stale():
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
 
+def ensure_built() -> str:
+    """Build the oracle only if the library is missing or older than its source."""
+    return build(force=False)
+
+
 _lib = None
 
 
 def lib():
+    """The loaded oracle library.  Never compiles: raises if ``liboracle.so`` is
+    missing or older than ``q8_oracle.c`` (run ``build()`` first)."""
     global _lib
     if _lib is None:
-        build()
+        if _stale():
+            raise ImportError(f"{_LIB} is missing or older than {_SRC}: run oracle.build() (or "
+                              "__graft_entry__.build()) before using the oracle")
         L = C.CDLL(_LIB)
         P = C.c_void_p
         I64 = C.c_int64

@@ -54,8 +54,8 @@
  *
  *  - Decode attention over a Q8_0 key/value cache [Frigg README, "The model, as
  *    verified": hidden 1536 = 12 heads x head_dim 128, multi-head attention
- *    with 12 key/value heads; "Masks": decode passes no mask, one query
- *    against the whole cache; "Cache": one static slab [heads][4096][128] per
+ *    with 12 key/value heads; "Masks": the single decode query attends to
+ *    every cached row unmasked; "Cache": one static slab [heads][4096][128] per
  *    virtual layer for K and for V; the bytes-per-token table counts an int8
  *    KV read per token].  The pages name int8 KV without its block layout; it
  *    is read here as the same Q8_0 format (blocks of 32 along head_dim, one

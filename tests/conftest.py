@@ -11,6 +11,11 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: long CPU test")
+    # The oracle library is compiled (if missing or stale) here, at session
+    # start, before any test touches a GPU: no process that has initialised a
+    # GPU starts the compiler.
+    import oracle
+    oracle.ensure_built()
 
 
 def gpu_available() -> bool:

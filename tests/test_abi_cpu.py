@@ -35,10 +35,14 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(q8.EXPORTED)
     for name in names:
         assert hasattr(lib, name), name
+    # the measurement probes live in their own library, not in the product's
+    from int8_weight_streaming_amd import probe as q8probe
+    plib = q8probe.load()
     probe = declared_functions(os.path.join(ROOT, "include", "q8probe.h"))
-    assert set(probe) == set(q8.PROBE_EXPORTED)
+    assert set(probe) == set(q8probe.EXPORTED)
     for name in probe:
-        assert hasattr(lib, name), name
+        assert hasattr(plib, name), name
+        assert not hasattr(lib, name), name
 
 
 def test_version_and_status_strings(lib):
@@ -241,14 +245,21 @@ def test_valid_arguments_without_gpu_report_device(lib):
     assert lib.q4_gemm_skinny(A, B, 8, 64, 2, 0, A, None, A, None) == DEVICE
 
 
-def test_probe_validation(lib):
+def test_probe_validation():
     """The measurement probes check their arguments before any device call."""
-    assert lib.q8_probe_read(A, 0, A, None) == SHAPE
-    assert lib.q8_probe_read(A, 24, A, None) == SHAPE
-    assert lib.q8_probe_read(None, 64, A, None) == NULL
-    assert lib.q8_probe_barrier(None, 4, 1, None) == NULL
-    assert lib.q8_probe_barrier(0x300002, 4, 1, None) == ALIGN   # flags need 4-byte alignment
-    assert lib.q8_probe_barrier_words() > 8 * 1024
+    from int8_weight_streaming_amd import probe as q8probe
+    plib = q8probe.load()
+    assert plib.q8_probe_read(A, 0, 8, A, None) == SHAPE
+    assert plib.q8_probe_read(A, 24, 8, A, None) == SHAPE
+    assert plib.q8_probe_read(A, 64, 5, A, None) == SHAPE      # loads per thread not offered
+    assert plib.q8_probe_read(None, 64, 8, A, None) == NULL
+    assert plib.q8_probe_read(MIS, 64, 8, A, None) == ALIGN
+    assert plib.q8_probe_barrier(None, 4, 1, None) == NULL
+    assert plib.q8_probe_barrier(0x300002, 4, 1, None) == ALIGN   # flags need 4-byte alignment
+    assert plib.q8_probe_barrier_words() > 8 * 1024
+    assert plib.q8_probe_mfma_i8(0, 10, A, None) == SHAPE
+    assert plib.q8_probe_mfma_i8(4, 0, A, None) == SHAPE
+    assert plib.q8_probe_mfma_i8(4, 10, None, None) == NULL
 
 
 def test_attn_validation(lib):

@@ -521,22 +521,3 @@ def test_rejects_bad_batch_loudly():
     wd = torch.zeros((4, 2), dtype=torch.uint16, device=DEV)
     with pytest.raises(q8.Q8Error):
         q8.gemm_skinny(wq, wd, torch.zeros((9, 64), dtype=torch.uint16, device=DEV))
-
-
-def test_barrier_probe_completes():
-    """The grid-barrier measurement probe: every round completes on every
-    workgroup (no timeout flagged), and consecutive calls continue from the
-    epochs the previous call left."""
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    flags = q8.probe_barrier_flags(DEV)
-    for g in sorted({1, 64, min(256, cus), cus}):
-        flags.zero_()
-        q8.probe_barrier(flags, g, 50)
-        q8.probe_barrier(flags, g, 25)
-        q8.probe_barrier(flags, g, 0)
-        torch.cuda.synchronize()
-        f = flags.cpu().numpy()
-        assert f[-1] == 0, f"barrier timed out with {g} workgroups"
-        for r in range(8):
-            assert np.all(f[r * 1024: r * 1024 + g] == 75), (g, r)
-
