@@ -62,10 +62,10 @@ static hipError_t launch_cfg(const int8_t* wq, const uint16_t* wd, int64_t n, in
 //    (activations in registers) and one wave per row above that.
 SkinnyLayout skinny_layout(int64_t n, int64_t k, int m, int cu_count) {
     const int64_t tall_wgs = (n + 31) / 32;
-    if (tall_wgs >= (int64_t)cu_count * (m <= 2 ? 1 : 4)) return {16, 2, 6};
-    if (k / 32 <= 48) return {32, 1, 3};
-    if (m <= 2) return {32, 1, 8};
-    return {64, 1, 2};
+    if (tall_wgs >= (int64_t)cu_count * (m <= 2 ? 1 : 4)) return {16, 2, 6, false};
+    if (k / 32 <= 48) return {32, 1, 3, false};
+    if (m <= 2) return {32, 1, 8, false};
+    return {64, 1, 2, false};
 }
 
 template <int M, int ACT>
@@ -103,6 +103,8 @@ static hipError_t launch_act(const int8_t* wq, const uint16_t* wd, int64_t n, in
 hipError_t launch_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int m,
                          int act, const void* x, const uint16_t* xd, float* y,
                          const DeviceInfo& dev, hipStream_t stream) {
+    if (act == 0 && skinny_mfma_applies(n, k, m, dev.cu_count))
+        return launch_skinny_mfma(wq, wd, n, k, m, x, y, dev, stream);
     const int nb = (int)(k / 32);
     if (act == 0) return launch_act<0>(wq, wd, n, nb, m, x, xd, y, dev, stream);
     return launch_act<1>(wq, wd, n, nb, m, x, xd, y, dev, stream);

@@ -1,0 +1,209 @@
+// q8_skinny_mfma.hip -- batch 3..8 W8A16 products on the bf16 matrix cores.
+//
+//   y[m][j] = sum_b wd[j][b] * sum_{i<32} wq[j][32b+i] * x[m][32b+i]
+//
+// At batch 3..8 the vector-ALU form of the decode product spends about four
+// dot instructions per weight on the activation rows, more than the weight
+// bytes cost at HBM speed [Frigg README, Finding 8: a batched kernel's cost
+// should stay nearly flat in the batch size].  Here the multiply-adds go to the
+// matrix cores: per 32-element block and 16 weight rows one
+// v_mfma_f32_16x16x32_bf16 takes the activation rows as A (16 x 32; rows m and
+// up read as zero) and the exactly converted weight codes as B (32 x 16), so
+// its fp32 result D[m][j] is the block's dot product; the vector ALUs only
+// convert the codes (int8 -> bf16 is exact) and fold each block with its scale
+// (lane (j, g) holds D[4g .. 4g + 3][j], one weight row, so one scale per lane
+// and block).
+//
+// Loads stay coalesced: a wave's 16 RGW weight rows arrive four blocks (128
+// bytes per row) at a time with full-line 16-byte loads, eight lanes per row,
+// are written to the wave's LDS slice (row pitch 136 bytes) and read back as
+// B fragments (8 bytes per lane: row j, bytes 8g .. 8g + 7 of the block; the
+// activation fragment uses the same k positions).  Loading fragments straight
+// from memory touches 16 rows x 32 bytes per instruction and streamed the
+// lm_head at under 2 TB/s.  The next four blocks are in flight while the
+// current ones are multiplied.  KS waves of a workgroup split K (contiguous
+// block ranges) and add their partial results through LDS in a fixed order,
+// so results are bitwise reproducible; no atomics.
+#include "q8_device.hpp"
+#include "q8_internal.hpp"
+
+namespace q8 {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMPitch = 136;                      // LDS bytes per staged row of 4 blocks (128 + 8)
+
+// Workgroup of 4 waves: 4 / KS sets of 16 RGW rows, each set's K split over KS waves.
+template <int M, int RGW, int KS, int NT>
+__global__ __launch_bounds__(256) void skinny_mfma_kernel(const int8_t* __restrict__ wq,
+                                                          const uint16_t* __restrict__ wd, int64_t n, int nb,
+                                                          const uint16_t* __restrict__ x, float* __restrict__ y) {
+    static_assert(M >= 1 && M <= 16, "activation rows fill at most the 16 rows of the A operand");
+    constexpr int RS = 4 / KS;                       // row sets per workgroup
+    constexpr int ROWS = 16 * RGW;                   // rows per wave
+    constexpr int NLW = ROWS / 8;                    // 16-byte weight loads per lane per step
+    __shared__ __attribute__((aligned(16))) unsigned char lds[4][ROWS * kMPitch];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int ks = wave % KS, rs = wave / KS;
+    const int64_t n0 = ((int64_t)blockIdx.x * RS + rs) * ROWS;
+    const int k = nb * 32;
+    const int nbw = nb / KS, b0 = ks * nbw;          // this wave's blocks
+    // descriptors: weight rows past n and activation rows past M read as zero
+    const int nv = n - n0 <= 0 ? 0 : (n - n0 < ROWS ? (int)(n - n0) : ROWS);
+    const auto rW = range_rsrc32(wq + (nv ? n0 * k : 0), nv * k);
+    const auto rS = range_rsrc32(wd + (nv ? n0 * nb : 0), nv * nb * 2);
+    const auto rX = range_rsrc32(x, M * k * 2);
+    const int j = lane & 15, g = lane >> 4;          // fragment lane: row / column j, k group g
+    const int cr = lane >> 3, cc = lane & 7;         // copy lane: rows cr + 8 t, 16-byte chunk cc
+    unsigned char* const sl = lds[wave];
+
+    struct Step {
+        i32x4 w[NLW];
+        i32x4 xv[4];
+        i32x2 s[RGW];
+    };
+    auto issue = [&](int c, Step& st) {
+        const int bb = b0 + 4 * c;
+#pragma unroll
+        for (int t = 0; t < NLW; ++t)
+            st.w[t] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rW, (cr + 8 * t) * k + cc * 16, bb * 32, NT ? kLoadNT : 0));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            st.xv[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, j * k * 2 + 16 * g,
+                                                                                        (bb + u) * 64, 0));
+#pragma unroll
+        for (int r = 0; r < RGW; ++r)
+            st.s[r] = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rS, (16 * r + j) * nb * 2,
+                                                                                      bb * 2, 0));
+    };
+    f32x4 acc[RGW];
+#pragma unroll
+    for (int r = 0; r < RGW; ++r) acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const Step& st) {
+        // LDS operations of one wave run in order: the previous step's fragment
+        // reads are done before this write
+#pragma unroll
+        for (int t = 0; t < NLW; ++t) *reinterpret_cast<i32x4*>(sl + (cr + 8 * t) * kMPitch + cc * 16) = st.w[t];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int r = 0; r < RGW; ++r) {
+                const i32x2 wv = *reinterpret_cast<const i32x2*>(sl + (16 * r + j) * kMPitch + 32 * u + 8 * g);
+                uint32_t b[4];
+                i8x4_to_bf16x4((uint32_t)wv[0], b[0], b[1]);
+                i8x4_to_bf16x4((uint32_t)wv[1], b[2], b[3]);
+                const i32x4 bw = {(int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+                const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st.xv[u]),
+                                                                        __builtin_bit_cast(bf16x8, bw), z, 0, 0, 0);
+                const uint32_t sv = (uint32_t)st.s[r][u >> 1];
+                const float ws = half_bits_to_float((uint16_t)((u & 1) ? (sv >> 16) : (sv & 0xFFFFu)));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[r][q] = fmaf(d[q], ws, acc[r][q]);
+            }
+        }
+    };
+    // two steps of registers: step c + 1 is loading while step c is multiplied
+    const int NS = nbw / 4;
+    Step s0, s1;
+    issue(0, s0);
+    for (int c = 0; c < NS; c += 2) {
+        if (c + 1 < NS) issue(c + 1, s1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 1 >= NS) break;
+        if (c + 2 < NS) issue(c + 2, s0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (KS > 1) {
+        // the K slices of a row set, added in wave order through LDS (the
+        // slices' staging bytes are consumed)
+        __syncthreads();
+        float* part = reinterpret_cast<float*>(&lds[0][0]);
+#pragma unroll
+        for (int r = 0; r < RGW; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) part[((wave * RGW + r) * 4 + q) * 64 + lane] = acc[r][q];
+        __syncthreads();
+        if (ks != 0) return;
+#pragma unroll
+        for (int s = 1; s < KS; ++s)
+#pragma unroll
+            for (int r = 0; r < RGW; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[r][q] += part[(((wave + s) * RGW + r) * 4 + q) * 64 + lane];
+    }
+#pragma unroll
+    for (int r = 0; r < RGW; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = 4 * g + q;
+            const int64_t row = n0 + 16 * r + j;
+            if (m < M && row < n) y[(int64_t)m * n + row] = acc[r][q];
+        }
+}
+
+static_assert(sizeof(float) * 4 * 1 * 4 * 64 <= 4 * 16 * 1 * kMPitch, "partials fit the slices (RGW = 1)");
+static_assert(sizeof(float) * 4 * 2 * 4 * 64 <= 4 * 16 * 2 * kMPitch, "partials fit the slices (RGW = 2)");
+
+template <int M, int RGW, int KS, int NT>
+hipError_t launch_cfg(const int8_t* wq, const uint16_t* wd, int64_t n, int nb, const void* x, float* y,
+                      hipStream_t stream) {
+    const int64_t rows = 16 * RGW * (4 / KS);
+    const int64_t grid = (n + rows - 1) / rows;
+    skinny_mfma_kernel<M, RGW, KS, NT><<<(unsigned)grid, 256, 0, stream>>>(wq, wd, n, nb,
+                                                                           static_cast<const uint16_t*>(x), y);
+    return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int nb, const void* x, float* y,
+                    const SkinnyLayout& L, hipStream_t stream) {
+    if (L.r == 2) return launch_cfg<M, 2, 4, 1>(wq, wd, n, nb, x, y, stream);
+    return launch_cfg<M, 1, 4, 0>(wq, wd, n, nb, x, y, stream);
+}
+
+}  // namespace
+
+// The matrix-core form is used for bf16 activations from batch 3 on where it
+// measured faster than the vector-ALU form (graph replay, weights rotated past
+// the caches): every Mimir shape and the lm_head at batch 5..8; at batch 3..4
+// only matrices of at least 64 rows per compute unit (the lm_head), where the vector form's per-weight arithmetic shows.  It needs K a multiple of 512 (whole four-block
+// steps in each of the four K slices).  Tall matrices (4 or more 32-row
+// workgroups per compute unit) use two 16-row groups per wave and
+// non-temporal weight loads; shorter ones one group.
+bool skinny_mfma_applies(int64_t n, int64_t k, int m, int cu_count) {
+    if (m < 3 || m > 8 || k % 512 != 0) return false;
+    if (m >= 5) return true;
+    return (n + 31) / 32 >= 2 * (int64_t)cu_count;
+}
+SkinnyLayout skinny_mfma_layout(int64_t n, int cu_count) {
+    const bool tall = (n + 31) / 32 >= 4 * (int64_t)cu_count;
+    return SkinnyLayout{16, tall ? 2 : 1, 4, true};
+}
+
+hipError_t launch_skinny_mfma(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int m, const void* x,
+                              float* y, const DeviceInfo& dev, hipStream_t stream) {
+    (void)hipGetLastError();
+    const int nb = (int)(k / 32);
+    const SkinnyLayout L = skinny_mfma_layout(n, dev.cu_count);
+    switch (m) {
+        case 3: return launch_m<3>(wq, wd, n, nb, x, y, L, stream);
+        case 4: return launch_m<4>(wq, wd, n, nb, x, y, L, stream);
+        case 5: return launch_m<5>(wq, wd, n, nb, x, y, L, stream);
+        case 6: return launch_m<6>(wq, wd, n, nb, x, y, L, stream);
+        case 7: return launch_m<7>(wq, wd, n, nb, x, y, L, stream);
+        case 8: return launch_m<8>(wq, wd, n, nb, x, y, L, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace q8

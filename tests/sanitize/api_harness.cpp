@@ -96,7 +96,13 @@ hipError_t launch_prefill(const int8_t*, const uint16_t*, int64_t n, int64_t k, 
     return rec(n, k, p);
 }
 int prefill_kind(int64_t, int64_t k, int64_t, int) { return k % 512 == 0 ? kPrefillStream : kPrefillTile32; }
-SkinnyLayout skinny_layout(int64_t, int64_t, int, int) { return {16, 2, 6}; }
+SkinnyLayout skinny_layout(int64_t, int64_t, int, int) { return {16, 2, 6, false}; }
+bool skinny_mfma_applies(int64_t, int64_t k, int m, int) { return m >= 5 && k % 512 == 0; }
+SkinnyLayout skinny_mfma_layout(int64_t, int) { return {16, 1, 4, true}; }
+hipError_t launch_skinny_mfma(const int8_t*, const uint16_t*, int64_t n, int64_t k, int m, const void*, float*,
+                              const DeviceInfo&, hipStream_t) {
+    return rec(n, k, m);
+}
 Q4Layout q4_layout(int64_t, int64_t, int, int, int) { return {16, 2, 3, 0}; }
 // attention sizes: 64-row chunks up to 512 rows, 128 up to 2048, 256 above
 static int64_t chunk_rows(int64_t t) { return t <= 512 ? 64 : t <= 2048 ? 128 : 256; }
@@ -225,6 +231,10 @@ int main() {
     char name[96];
     call([&] { return q8_kernel_name(Q8_OP_SKINNY, 262144, 1536, 1, 0, name, sizeof name); }, Q8_OK, false);
     EXPECT(std::strcmp(name, "skinny_kernel<1,0,16,2,6>") == 0);
+    call([&] { return q8_kernel_name(Q8_OP_SKINNY, 262144, 1536, 8, 0, name, sizeof name); }, Q8_OK, false);
+    EXPECT(std::strcmp(name, "skinny_mfma_kernel<8,1,4,0>") == 0);
+    call([&] { return q8_kernel_name(Q8_OP_SKINNY, 262144, 1536, 8, 1, name, sizeof name); }, Q8_OK, false);
+    EXPECT(std::strcmp(name, "skinny_kernel<8,1,16,2,6>") == 0);
     call([&] { return q8_kernel_name(Q8_OP_PREFILL, 4608, 1536, 256, 9, name, sizeof name); }, Q8_OK, false);
     EXPECT(std::strcmp(name, "prefill_stream_kernel") == 0);
     call([&] { return q8_kernel_name(Q8_OP_SKINNY, 262144, 1536, 1, 0, name, 5); }, Q8_ERR_SHAPE, false);

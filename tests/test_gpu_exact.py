@@ -96,26 +96,47 @@ def assert_bitwise(got, ref64, what):
 
 # ------------------------------------------------------------------ decode products (Q8_0 weights)
 
-# (name, n as a function of the compute-unit count, k, batches, layout (G, R, CPL))
+# (name, n as a function of the compute-unit count, k, batches, vector-ALU layout (G, R, CPL))
 SKINNY_FORMS = [
     ("tall b1-2", lambda c: 32 * c + 5, 1536, (1, 2), (16, 2, 6)),
-    ("tall b3-8", lambda c: 128 * c + 7, 1536, (3, 8), (16, 2, 6)),
+    ("tall b3-8", lambda c: 128 * c + 7, 1536, (3, 4, 8), (16, 2, 6)),
     ("tall b1-2, K in several tiles", lambda c: 32 * c + 9, 4128, (1, 2), (16, 2, 6)),
-    ("short", lambda c: 200, 1536, (1, 2, 3, 8), (32, 1, 3)),
+    ("tall b3-8, K in several tiles", lambda c: 128 * c + 3, 4128, (3, 8), (16, 2, 6)),
+    ("short", lambda c: 200, 1536, (1, 2, 3, 5, 8), (32, 1, 3)),
     ("short, ragged K tile", lambda c: 77, 992, (1, 2, 5, 8), (32, 1, 3)),
     ("long K b1-2", lambda c: 200, 4128, (1, 2), (32, 1, 8)),
     ("long K b3-8", lambda c: 130, 4128, (3, 8), (64, 1, 2)),
+    ("long K, K a multiple of 512", lambda c: 130, 4096, (3, 6, 8), (64, 1, 2)),
+    ("middle, ragged rows", lambda c: 64 * c + 13, 1536, (4, 7), (16, 2, 6)),
 ]
 SKINNY_CASES = [(name, nf, k, m, lay) for name, nf, k, ms, lay in SKINNY_FORMS for m in ms]
+
+
+def expected_skinny(n, k, m, act, lay, c):
+    """The kernel the dispatch rule picks: the matrix-core form for bf16
+    activations at batch 5..8 (any shape) or 3..4 (at least 64 rows per compute
+    unit), K a multiple of 512 -- two 16-row fragments per wave from 128 rows
+    per compute unit on; else the vector-ALU layout."""
+    a = q8.Q8_ACT_Q8 if act == "q8" else q8.Q8_ACT_BF16
+    mfma = act == "bf16" and k % 512 == 0 and (m >= 5 or (m >= 3 and (n + 31) // 32 >= 2 * c))
+    if mfma:
+        rgw = 2 if (n + 31) // 32 >= 4 * c else 1
+        return f"skinny_mfma_kernel<{m},{rgw},4,{1 if rgw == 2 else 0}>"
+    if act == "bf16" and m >= 3 and (n + 31) // 32 < 4 * c and lay == (16, 2, 6):
+        lay = (32, 1, 3) if k // 32 <= 48 else (64, 1, 2)      # a middle matrix at batch 3-8
+    return f"skinny_kernel<{m},{a},{lay[0]},{lay[1]},{lay[2]}>"
 
 
 @pytest.mark.parametrize("name,nf,k,m,lay", SKINNY_CASES,
                          ids=[f"{c[0]}-m{c[3]}" for c in SKINNY_CASES])
 @pytest.mark.parametrize("act", ["q8", "bf16"])
 def test_skinny_block_sums_bitwise(name, nf, k, m, lay, act):
-    n = nf(cus())
+    c = cus()
+    n = nf(c)
     a = q8.Q8_ACT_Q8 if act == "q8" else q8.Q8_ACT_BF16
-    want = f"skinny_kernel<{m},{a},{lay[0]},{lay[1]},{lay[2]}>"
+    if act == "q8" and m >= 3 and (n + 31) // 32 < 4 * c and lay == (16, 2, 6):
+        lay = (32, 1, 3) if k // 32 <= 48 else (64, 1, 2)
+    want = expected_skinny(n, k, m, act, lay, c)
     got_name = q8.kernel_name(q8.OP_SKINNY, n, k, m, a)
     log(f"skinny {name} act={act} n={n} k={k} m={m}: {got_name}")
     assert got_name == want
