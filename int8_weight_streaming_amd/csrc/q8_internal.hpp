@@ -22,7 +22,8 @@ hipError_t launch_quantize_bf16(const uint16_t* x, int64_t nblocks, int8_t* q, u
 // Lane-group layout of the decode product kernel for (n, k, m) on a device
 // with cu_count compute units: G lanes per group, R rows per group, CPL
 // 16-byte chunks per lane per K tile.  For the matrix-core form (mfma): 16
-// rows per fragment, R fragments of rows per wave, K split over CPL waves.
+// rows per fragment, R fragments of rows per wave, K split over CPL waves
+// (workgroups of max(4, CPL) waves).
 struct SkinnyLayout {
     int g, r, cpl;
     bool mfma;
@@ -31,7 +32,7 @@ SkinnyLayout skinny_layout(int64_t n, int64_t k, int m, int cu_count);
 // The batch 3..8 W8A16 product on the matrix cores (bf16 activations only):
 // whether it is used for (n, k, m), its layout, and its launch.
 bool skinny_mfma_applies(int64_t n, int64_t k, int m, int cu_count);
-SkinnyLayout skinny_mfma_layout(int64_t n, int cu_count);
+SkinnyLayout skinny_mfma_layout(int64_t n, int64_t k, int cu_count);
 hipError_t launch_skinny_mfma(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int m, const void* x,
                               float* y, const DeviceInfo& dev, hipStream_t stream);
 

@@ -98,7 +98,7 @@ hipError_t launch_prefill(const int8_t*, const uint16_t*, int64_t n, int64_t k, 
 int prefill_kind(int64_t, int64_t k, int64_t, int) { return k % 512 == 0 ? kPrefillStream : kPrefillTile32; }
 SkinnyLayout skinny_layout(int64_t, int64_t, int, int) { return {16, 2, 6, false}; }
 bool skinny_mfma_applies(int64_t, int64_t k, int m, int) { return m >= 5 && k % 512 == 0; }
-SkinnyLayout skinny_mfma_layout(int64_t, int) { return {16, 1, 4, true}; }
+SkinnyLayout skinny_mfma_layout(int64_t, int64_t, int) { return {16, 1, 4, true}; }
 hipError_t launch_skinny_mfma(const int8_t*, const uint16_t*, int64_t n, int64_t k, int m, const void*, float*,
                               const DeviceInfo&, hipStream_t) {
     return rec(n, k, m);

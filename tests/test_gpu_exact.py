@@ -107,6 +107,8 @@ SKINNY_FORMS = [
     ("long K b1-2", lambda c: 200, 4128, (1, 2), (32, 1, 8)),
     ("long K b3-8", lambda c: 130, 4128, (3, 8), (64, 1, 2)),
     ("long K, K a multiple of 512", lambda c: 130, 4096, (3, 6, 8), (64, 1, 2)),
+    ("long K, K a multiple of 512 but not 1024", lambda c: 70, 2560, (5, 8), (64, 1, 2)),
+    ("down shape", lambda c: 1536, 4096, (5, 8), (64, 1, 2)),
     ("middle, ragged rows", lambda c: 64 * c + 13, 1536, (4, 7), (16, 2, 6)),
 ]
 SKINNY_CASES = [(name, nf, k, m, lay) for name, nf, k, ms, lay in SKINNY_FORMS for m in ms]
@@ -116,12 +118,16 @@ def expected_skinny(n, k, m, act, lay, c):
     """The kernel the dispatch rule picks: the matrix-core form for bf16
     activations at batch 5..8 (any shape) or 3..4 (at least 64 rows per compute
     unit), K a multiple of 512 -- two 16-row fragments per wave from 128 rows
-    per compute unit on; else the vector-ALU layout."""
+    per compute unit on, an eight-way K split for K a multiple of 1024 below 32
+    rows per compute unit; else the vector-ALU layout."""
     a = q8.Q8_ACT_Q8 if act == "q8" else q8.Q8_ACT_BF16
     mfma = act == "bf16" and k % 512 == 0 and (m >= 5 or (m >= 3 and (n + 31) // 32 >= 2 * c))
     if mfma:
-        rgw = 2 if (n + 31) // 32 >= 4 * c else 1
-        return f"skinny_mfma_kernel<{m},{rgw},4,{1 if rgw == 2 else 0}>"
+        if (n + 31) // 32 >= 4 * c:
+            return f"skinny_mfma_kernel<{m},2,4,1>"
+        if k % 1024 == 0 and (n + 31) // 32 < c:
+            return f"skinny_mfma_kernel<{m},1,8,0>"
+        return f"skinny_mfma_kernel<{m},1,4,0>"
     if act == "bf16" and m >= 3 and (n + 31) // 32 < 4 * c and lay == (16, 2, 6):
         lay = (32, 1, 3) if k // 32 <= 48 else (64, 1, 2)      # a middle matrix at batch 3-8
     return f"skinny_kernel<{m},{a},{lay[0]},{lay[1]},{lay[2]}>"
