@@ -170,6 +170,7 @@ template <int M>
 hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int nb, const void* x, float* y,
                     const SkinnyLayout& L, hipStream_t stream) {
     if (L.r == 2) return launch_cfg<M, 2, 4, 1, 4>(wq, wd, n, nb, x, y, stream);
+    if (L.cpl == 12) return launch_cfg<M, 1, 12, 0, 12>(wq, wd, n, nb, x, y, stream);
     if (L.cpl == 8) return launch_cfg<M, 1, 8, 0, 8>(wq, wd, n, nb, x, y, stream);
     return launch_cfg<M, 1, 4, 0, 4>(wq, wd, n, nb, x, y, stream);
 }
@@ -179,12 +180,18 @@ hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int nb, con
 // The matrix-core form is used for bf16 activations from batch 3 on where it
 // measured faster than the vector-ALU form (graph replay, weights rotated past
 // the caches): every Mimir shape and the lm_head at batch 5..8; at batch 3..4
-// only matrices of at least 64 rows per compute unit (the lm_head), where the vector form's per-weight arithmetic shows.  It needs K a multiple of 512 (whole four-block
+// only matrices of at least 64 rows per compute unit (the lm_head), where the
+// vector form's per-weight arithmetic shows (qkv and gate_up at batch 3..4
+// measured faster alone on the matrix cores but slower inside the decode step:
+// 2.25 against 2.17 ms at batch 3).  It needs K a multiple of 512 (whole four-block
 // steps in each of the four K slices).  Tall matrices (4 or more 32-row
 // workgroups per compute unit) use two 16-row groups per wave and
-// non-temporal weight loads; shorter ones one group, and for K a multiple of
-// 1024 below 32 rows per compute unit (the down projection) eight waves split
-// K eight ways (down at batch 8: 6.5 against 7.4 us with four).
+// non-temporal weight loads; shorter ones one group with K split over the
+// waves of a workgroup: twelve ways when the 32-element blocks are a multiple
+// of 48 (K = 1536: one four-block step per wave; qkv / o / gate_up at batch 8
+// 4.85 / 3.85 / 5.45 against 4.99 / 4.09 / 5.58 us with four), else eight
+// ways for K a multiple of 1024 below 32 rows per compute unit (the down
+// projection at batch 8: 6.5 against 7.4 us with four), else four.
 bool skinny_mfma_applies(int64_t n, int64_t k, int m, int cu_count) {
     if (m < 3 || m > 8 || k % 512 != 0) return false;
     if (m >= 5) return true;
@@ -192,6 +199,7 @@ bool skinny_mfma_applies(int64_t n, int64_t k, int m, int cu_count) {
 }
 SkinnyLayout skinny_mfma_layout(int64_t n, int64_t k, int cu_count) {
     if ((n + 31) / 32 >= 4 * (int64_t)cu_count) return SkinnyLayout{16, 2, 4, true};
+    if (k % 1536 == 0) return SkinnyLayout{16, 1, 12, true};
     if (k % 1024 == 0 && (n + 31) / 32 < (int64_t)cu_count) return SkinnyLayout{16, 1, 8, true};
     return SkinnyLayout{16, 1, 4, true};
 }

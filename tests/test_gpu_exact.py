@@ -110,6 +110,8 @@ SKINNY_FORMS = [
     ("long K, K a multiple of 512 but not 1024", lambda c: 70, 2560, (5, 8), (64, 1, 2)),
     ("down shape", lambda c: 1536, 4096, (5, 8), (64, 1, 2)),
     ("middle, ragged rows", lambda c: 64 * c + 13, 1536, (4, 7), (16, 2, 6)),
+    ("qkv shape", lambda c: 18 * c, 1536, (3, 8), (32, 1, 3)),
+    ("K two twelve-way steps", lambda c: 300, 3072, (5, 8), (64, 1, 2)),
 ]
 SKINNY_CASES = [(name, nf, k, m, lay) for name, nf, k, ms, lay in SKINNY_FORMS for m in ms]
 
@@ -118,14 +120,18 @@ def expected_skinny(n, k, m, act, lay, c):
     """The kernel the dispatch rule picks: the matrix-core form for bf16
     activations at batch 5..8 (any shape) or 3..4 (at least 64 rows per compute
     unit), K a multiple of 512 -- two 16-row fragments per wave from 128 rows
-    per compute unit on, an eight-way K split for K a multiple of 1024 below 32
-    rows per compute unit; else the vector-ALU layout."""
+    per compute unit on, else a twelve-way K split for K a multiple of 1536, an
+    eight-way one for K a multiple of 1024 below 32 rows per compute unit, a
+    four-way one otherwise; else the vector-ALU layout."""
     a = q8.Q8_ACT_Q8 if act == "q8" else q8.Q8_ACT_BF16
-    mfma = act == "bf16" and k % 512 == 0 and (m >= 5 or (m >= 3 and (n + 31) // 32 >= 2 * c))
+    groups = (n + 31) // 32
+    mfma = act == "bf16" and k % 512 == 0 and (m >= 5 or (m >= 3 and groups >= 2 * c))
     if mfma:
-        if (n + 31) // 32 >= 4 * c:
+        if groups >= 4 * c:
             return f"skinny_mfma_kernel<{m},2,4,1>"
-        if k % 1024 == 0 and (n + 31) // 32 < c:
+        if k % 1536 == 0:
+            return f"skinny_mfma_kernel<{m},1,12,0>"
+        if k % 1024 == 0 and groups < c:
             return f"skinny_mfma_kernel<{m},1,8,0>"
         return f"skinny_mfma_kernel<{m},1,4,0>"
     if act == "bf16" and m >= 3 and (n + 31) // 32 < 4 * c and lay == (16, 2, 6):
