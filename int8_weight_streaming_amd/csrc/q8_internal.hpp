@@ -29,7 +29,7 @@ struct SkinnyLayout {
     bool mfma;
 };
 SkinnyLayout skinny_layout(int64_t n, int64_t k, int m, int cu_count);
-// The batch 3..8 W8A16 product on the matrix cores (bf16 activations only):
+// The batch 2..8 W8A16 product on the matrix cores (bf16 activations only):
 // whether it is used for (n, k, m), its layout, and its launch.
 bool skinny_mfma_applies(int64_t n, int64_t k, int m, int cu_count);
 SkinnyLayout skinny_mfma_layout(int64_t n, int64_t k, int cu_count);

@@ -1,4 +1,4 @@
-// q8_skinny_mfma.hip -- batch 3..8 W8A16 products on the bf16 matrix cores.
+// q8_skinny_mfma.hip -- batch 2..8 W8A16 products on the bf16 matrix cores.
 //
 //   y[m][j] = sum_b wd[j][b] * sum_{i<32} wq[j][32b+i] * x[m][32b+i]
 //
@@ -203,11 +203,11 @@ hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int nb, con
 
 // The matrix-core form is used for bf16 activations from batch 3 on where it
 // measured faster than the vector-ALU form (graph replay, weights rotated past
-// the caches): every Mimir shape and the lm_head at batch 5..8; at batch 3..4
-// only matrices of at least 64 rows per compute unit (the lm_head), where the
-// vector form's per-weight arithmetic shows (qkv and gate_up at batch 3..4
-// measured faster alone on the matrix cores but slower inside the decode step:
-// 2.25 against 2.17 ms at batch 3).  It needs K a multiple of 512 (whole four-block
+// the caches): every Mimir shape and the lm_head at batch 5..8; at batch 2..4
+// only matrices of at least 64 rows per compute unit (the lm_head, batch 2:
+// 71.1 against 79.8 us), where the vector form's per-weight arithmetic shows
+// (qkv and gate_up at batch 2..4 measured faster alone on the matrix cores but
+// level or slower inside the decode step: 2.25 against 2.17 ms at batch 3).  It needs K a multiple of 512 (whole four-block
 // steps in each of the four K slices).  Tall matrices (4 or more 32-row
 // workgroups per compute unit) use two 16-row groups per wave and
 // non-temporal weight loads; shorter ones one group with K split over the
@@ -217,7 +217,7 @@ hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int nb, con
 // ways for K a multiple of 1024 below 32 rows per compute unit (the down
 // projection at batch 8: 6.5 against 7.4 us with four), else four.
 bool skinny_mfma_applies(int64_t n, int64_t k, int m, int cu_count) {
-    if (m < 3 || m > 8 || k % 512 != 0) return false;
+    if (m < 2 || m > 8 || k % 512 != 0) return false;
     if (m >= 5) return true;
     return (n + 31) / 32 >= 2 * (int64_t)cu_count;
 }
@@ -234,6 +234,7 @@ hipError_t launch_skinny_mfma(const int8_t* wq, const uint16_t* wd, int64_t n, i
     const int nb = (int)(k / 32);
     const SkinnyLayout L = skinny_mfma_layout(n, k, dev.cu_count);
     switch (m) {
+        case 2: return launch_m<2>(wq, wd, n, nb, x, y, L, stream);
         case 3: return launch_m<3>(wq, wd, n, nb, x, y, L, stream);
         case 4: return launch_m<4>(wq, wd, n, nb, x, y, L, stream);
         case 5: return launch_m<5>(wq, wd, n, nb, x, y, L, stream);

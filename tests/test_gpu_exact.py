@@ -99,7 +99,7 @@ def assert_bitwise(got, ref64, what):
 # (name, n as a function of the compute-unit count, k, batches, vector-ALU layout (G, R, CPL))
 SKINNY_FORMS = [
     ("tall b1-2", lambda c: 32 * c + 5, 1536, (1, 2), (16, 2, 6)),
-    ("tall b3-8", lambda c: 128 * c + 7, 1536, (3, 4, 8), (16, 2, 6)),
+    ("tall b2-8", lambda c: 128 * c + 7, 1536, (2, 3, 4, 8), (16, 2, 6)),
     ("tall b1-2, K in several tiles", lambda c: 32 * c + 9, 4128, (1, 2), (16, 2, 6)),
     ("tall b3-8, K in several tiles", lambda c: 128 * c + 3, 4128, (3, 8), (16, 2, 6)),
     ("short", lambda c: 200, 1536, (1, 2, 3, 5, 8), (32, 1, 3)),
@@ -118,14 +118,14 @@ SKINNY_CASES = [(name, nf, k, m, lay) for name, nf, k, ms, lay in SKINNY_FORMS f
 
 def expected_skinny(n, k, m, act, lay, c):
     """The kernel the dispatch rule picks: the matrix-core form for bf16
-    activations at batch 5..8 (any shape) or 3..4 (at least 64 rows per compute
+    activations at batch 5..8 (any shape) or 2..4 (at least 64 rows per compute
     unit), K a multiple of 512 -- two 16-row fragments per wave from 128 rows
     per compute unit on, else a twelve-way K split for K a multiple of 1536, an
     eight-way one for K a multiple of 1024 below 32 rows per compute unit, a
     four-way one otherwise; else the vector-ALU layout."""
     a = q8.Q8_ACT_Q8 if act == "q8" else q8.Q8_ACT_BF16
     groups = (n + 31) // 32
-    mfma = act == "bf16" and k % 512 == 0 and (m >= 5 or (m >= 3 and groups >= 2 * c))
+    mfma = act == "bf16" and k % 512 == 0 and (m >= 5 or (m >= 2 and groups >= 2 * c))
     if mfma:
         if groups >= 4 * c:
             return f"skinny_mfma_kernel<{m},2,4,1>"
