@@ -21,9 +21,9 @@ hipError_t launch_quantize_bf16(const uint16_t* x, int64_t nblocks, int8_t* q, u
 
 // Lane-group layout of the decode product kernel for (n, k, m) on a device
 // with cu_count compute units: G lanes per group, R rows per group, CPL
-// 16-byte chunks per lane per K tile.  For the matrix-core form (mfma): 16
-// rows per fragment, R fragments of rows per wave, K split over CPL waves
-// (workgroups of max(4, CPL) waves).
+// 16-byte chunks per lane per K tile.  For the matrix-core form (mfma): G rows
+// per fragment (16, or 8 for a half fragment), R fragments of rows per wave, K
+// split over CPL waves (workgroups of max(4, CPL) waves).
 struct SkinnyLayout {
     int g, r, cpl;
     bool mfma;

@@ -36,17 +36,20 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMPitch = 136;                      // LDS bytes per staged row of 4 blocks (128 + 8)
 
-// Workgroup of W waves: W / KS sets of 16 RGW rows, each set's K split over KS
-// waves.  NSC > 0: every wave has exactly NSC four-block steps, all issued
-// before the first is multiplied (the launch checks it); 0: any number, two in
-// flight.
-template <int M, int RGW, int KS, int NT, int W, int NSC = 0>
+// Workgroup of W waves: W / KS sets of 16 RGW rows (8 with HALF: the B
+// operand's columns 8..15 are zero, so short matrices get twice the
+// workgroups), each set's K split over KS waves.  NSC > 0: every wave has
+// exactly NSC four-block steps, all issued before the first is multiplied (the
+// launch checks it); 0: any number, two in flight.
+template <int M, int RGW, int KS, int NT, int W, int NSC = 0, int HALF = 0>
 __global__ __launch_bounds__(64 * W) void skinny_mfma_kernel(const int8_t* __restrict__ wq,
                                                           const uint16_t* __restrict__ wd, int64_t n, int nb,
                                                           const uint16_t* __restrict__ x, float* __restrict__ y) {
     static_assert(M >= 1 && M <= 16, "activation rows fill at most the 16 rows of the A operand");
+    static_assert(!HALF || RGW == 1, "a half fragment is one 8-row group");
     constexpr int RS = W / KS;                       // row sets per workgroup
-    constexpr int ROWS = 16 * RGW;                   // rows per wave
+    constexpr int ROWS = HALF ? 8 : 16 * RGW;        // rows per wave
+    static_assert(sizeof(float) * 4 * RGW * 64 <= ROWS * kMPitch, "the wave's partials fit its slice");
     constexpr int NLW = ROWS / 8;                    // 16-byte weight loads per lane per step
     __shared__ __attribute__((aligned(16))) unsigned char lds[W][ROWS * kMPitch];
     const int lane = threadIdx.x & 63;
@@ -97,7 +100,9 @@ __global__ __launch_bounds__(64 * W) void skinny_mfma_kernel(const int8_t* __res
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
             for (int r = 0; r < RGW; ++r) {
-                const i32x2 wv = *reinterpret_cast<const i32x2*>(sl + (16 * r + j) * kMPitch + 32 * u + 8 * g);
+                i32x2 wv = *reinterpret_cast<const i32x2*>(sl + (16 * r + (HALF ? (j & 7) : j)) * kMPitch +
+                                                           32 * u + 8 * g);
+                if (HALF && j >= 8) wv = (i32x2){0, 0};
                 uint32_t b[4];
                 i8x4_to_bf16x4((uint32_t)wv[0], b[0], b[1]);
                 i8x4_to_bf16x4((uint32_t)wv[1], b[2], b[3]);
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(64 * W) void skinny_mfma_kernel(const int8_t* __res
         for (int q = 0; q < 4; ++q) {
             const int m = 4 * g + q;
             const int64_t row = n0 + 16 * r + j;
-            if (m < M && row < n) y[(int64_t)m * n + row] = acc[r][q];
+            if (m < M && row < n && (!HALF || j < 8)) y[(int64_t)m * n + row] = acc[r][q];
         }
 }
 
@@ -172,13 +177,13 @@ __global__ __launch_bounds__(64 * W) void skinny_mfma_kernel(const int8_t* __res
 static_assert(sizeof(float) * 4 * 1 * 64 <= 16 * 1 * kMPitch, "partials fit the slices (RGW = 1)");
 static_assert(sizeof(float) * 4 * 2 * 64 <= 16 * 2 * kMPitch, "partials fit the slices (RGW = 2)");
 
-template <int M, int RGW, int KS, int NT, int W, int NSC = 0>
+template <int M, int RGW, int KS, int NT, int W, int NSC = 0, int HALF = 0>
 hipError_t launch_cfg(const int8_t* wq, const uint16_t* wd, int64_t n, int nb, const void* x, float* y,
                       hipStream_t stream) {
     if (NSC > 0 && nb != 4 * KS * NSC) return hipErrorInvalidValue;
-    const int64_t rows = 16 * RGW * (W / KS);
+    const int64_t rows = (HALF ? 8 : 16 * RGW) * (W / KS);
     const int64_t grid = (n + rows - 1) / rows;
-    skinny_mfma_kernel<M, RGW, KS, NT, W, NSC><<<(unsigned)grid, 64 * W, 0, stream>>>(
+    skinny_mfma_kernel<M, RGW, KS, NT, W, NSC, HALF><<<(unsigned)grid, 64 * W, 0, stream>>>(
         wq, wd, n, nb, static_cast<const uint16_t*>(x), y);
     return hipGetLastError();
 }
@@ -195,7 +200,7 @@ hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int nb, con
     if (L.cpl == 12)
         return nb == 48 ? launch_cfg<M, 1, 12, 0, 12, 1>(wq, wd, n, nb, x, y, stream)
                         : launch_cfg<M, 1, 12, 0, 12>(wq, wd, n, nb, x, y, stream);
-    if (L.cpl == 8) return launch_cfg<M, 1, 8, 0, 8>(wq, wd, n, nb, x, y, stream);
+    if (L.cpl == 8) return launch_cfg<M, 1, 8, 0, 8, 0, 1>(wq, wd, n, nb, x, y, stream);
     return launch_cfg<M, 1, 4, 0, 4>(wq, wd, n, nb, x, y, stream);
 }
 
@@ -215,7 +220,9 @@ hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int nb, con
 // of 48 (K = 1536: one four-block step per wave; qkv / o / gate_up at batch 8
 // 4.85 / 3.85 / 5.45 against 4.99 / 4.09 / 5.58 us with four), else eight
 // ways for K a multiple of 1024 below 32 rows per compute unit (the down
-// projection at batch 8: 6.5 against 7.4 us with four), else four.
+// projection, whose 1536 rows make few workgroups: 8-row half fragments
+// double them, and at batch 8 it takes 6.0 us against 6.5 with 16-row
+// fragments and 7.4 with a four-way split), else four.
 bool skinny_mfma_applies(int64_t n, int64_t k, int m, int cu_count) {
     if (m < 2 || m > 8 || k % 512 != 0) return false;
     if (m >= 5) return true;
@@ -224,7 +231,7 @@ bool skinny_mfma_applies(int64_t n, int64_t k, int m, int cu_count) {
 SkinnyLayout skinny_mfma_layout(int64_t n, int64_t k, int cu_count) {
     if ((n + 31) / 32 >= 4 * (int64_t)cu_count) return SkinnyLayout{16, 2, 4, true};
     if (k % 1536 == 0) return SkinnyLayout{16, 1, 12, true};
-    if (k % 1024 == 0 && (n + 31) / 32 < (int64_t)cu_count) return SkinnyLayout{16, 1, 8, true};
+    if (k % 1024 == 0 && (n + 31) / 32 < (int64_t)cu_count) return SkinnyLayout{8, 1, 8, true};
     return SkinnyLayout{16, 1, 4, true};
 }
 

@@ -232,7 +232,7 @@ int main() {
     call([&] { return q8_kernel_name(Q8_OP_SKINNY, 262144, 1536, 1, 0, name, sizeof name); }, Q8_OK, false);
     EXPECT(std::strcmp(name, "skinny_kernel<1,0,16,2,6>") == 0);
     call([&] { return q8_kernel_name(Q8_OP_SKINNY, 262144, 1536, 8, 0, name, sizeof name); }, Q8_OK, false);
-    EXPECT(std::strcmp(name, "skinny_mfma_kernel<8,1,4,0>") == 0);
+    EXPECT(std::strcmp(name, "skinny_mfma_kernel<8,16,1,4,0>") == 0);
     call([&] { return q8_kernel_name(Q8_OP_SKINNY, 262144, 1536, 8, 1, name, sizeof name); }, Q8_OK, false);
     EXPECT(std::strcmp(name, "skinny_kernel<8,1,16,2,6>") == 0);
     call([&] { return q8_kernel_name(Q8_OP_PREFILL, 4608, 1536, 256, 9, name, sizeof name); }, Q8_OK, false);

@@ -121,19 +121,20 @@ def expected_skinny(n, k, m, act, lay, c):
     activations at batch 5..8 (any shape) or 2..4 (at least 64 rows per compute
     unit), K a multiple of 512 -- two 16-row fragments per wave from 128 rows
     per compute unit on, else a twelve-way K split for K a multiple of 1536, an
-    eight-way one for K a multiple of 1024 below 32 rows per compute unit, a
-    four-way one otherwise; else the vector-ALU layout."""
+    eight-way one with 8-row half fragments for K a multiple of 1024 below 32
+    rows per compute unit, a four-way one otherwise; else the vector-ALU
+    layout.  Named <batch, rows per fragment, fragments, K split, non-temporal>."""
     a = q8.Q8_ACT_Q8 if act == "q8" else q8.Q8_ACT_BF16
     groups = (n + 31) // 32
     mfma = act == "bf16" and k % 512 == 0 and (m >= 5 or (m >= 2 and groups >= 2 * c))
     if mfma:
         if groups >= 4 * c:
-            return f"skinny_mfma_kernel<{m},2,4,1>"
+            return f"skinny_mfma_kernel<{m},16,2,4,1>"
         if k % 1536 == 0:
-            return f"skinny_mfma_kernel<{m},1,12,0>"
+            return f"skinny_mfma_kernel<{m},16,1,12,0>"
         if k % 1024 == 0 and groups < c:
-            return f"skinny_mfma_kernel<{m},1,8,0>"
-        return f"skinny_mfma_kernel<{m},1,4,0>"
+            return f"skinny_mfma_kernel<{m},8,1,8,0>"
+        return f"skinny_mfma_kernel<{m},16,1,4,0>"
     if act == "bf16" and m >= 3 and (n + 31) // 32 < 4 * c and lay == (16, 2, 6):
         lay = (32, 1, 3) if k // 32 <= 48 else (64, 1, 2)      # a middle matrix at batch 3-8
     return f"skinny_kernel<{m},{a},{lay[0]},{lay[1]},{lay[2]}>"
