@@ -412,6 +412,7 @@ hipError_t launch_q4_skinny(const uint8_t* wq, const uint16_t* wd, int64_t n, in
                             int act, const void* x, const uint16_t* xd, float* y,
                             const DeviceInfo& dev, hipStream_t stream) {
     const int nb = (int)(k / 32);
+    if (act == 0 && q4_mfma_applies(n, k, m, dev.cu_count)) return launch_q4_mfma(wq, wd, n, k, m, x, y, dev, stream);
     if (act == 0) return q4_launch_act<0>(wq, wd, n, nb, m, x, xd, y, dev, stream);
     return q4_launch_act<1>(wq, wd, n, nb, m, x, xd, y, dev, stream);
 }

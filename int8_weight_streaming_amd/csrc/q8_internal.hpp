@@ -35,6 +35,11 @@ bool skinny_mfma_applies(int64_t n, int64_t k, int m, int cu_count);
 SkinnyLayout skinny_mfma_layout(int64_t n, int64_t k, int cu_count);
 hipError_t launch_skinny_mfma(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int m, const void* x,
                               float* y, const DeviceInfo& dev, hipStream_t stream);
+// The same for int4 weights (q4_gemm_skinny with bf16 activations).
+bool q4_mfma_applies(int64_t n, int64_t k, int m, int cu_count);
+SkinnyLayout q4_mfma_layout(int64_t n, int64_t k, int cu_count);
+hipError_t launch_q4_mfma(const uint8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int m, const void* x,
+                          float* y, const DeviceInfo& dev, hipStream_t stream);
 
 hipError_t launch_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k, int m,
                          int act, const void* x, const uint16_t* xd, float* y,

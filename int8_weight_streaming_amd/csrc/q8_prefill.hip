@@ -222,6 +222,8 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kStreamSlice = 2 * 32 * kPitch;             // one wave's operand rows (scales stay in registers)
 constexpr int kStreamLds = 4 * kStreamSlice;              // 36,864 B per workgroup
+// three workgroups per CU: the kernel's 161 VGPRs leave room for three waves per
+// SIMD (LDS would hold four workgroups: 4 x 36,864 B)
 constexpr int kStreamWgPerCu = 3;
 constexpr int64_t kStreamMaxK = int64_t(1) << 24;         // 32-bit buffer offsets
 

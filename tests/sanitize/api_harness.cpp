@@ -104,6 +104,8 @@ hipError_t launch_skinny_mfma(const int8_t*, const uint16_t*, int64_t n, int64_t
     return rec(n, k, m);
 }
 Q4Layout q4_layout(int64_t, int64_t, int, int, int) { return {16, 2, 3, 0}; }
+bool q4_mfma_applies(int64_t, int64_t k, int m, int) { return m >= 5 && k % 512 == 0; }
+SkinnyLayout q4_mfma_layout(int64_t, int64_t, int) { return {16, 1, 4, true}; }
 // attention sizes: 64-row chunks up to 512 rows, 128 up to 2048, 256 above
 static int64_t chunk_rows(int64_t t) { return t <= 512 ? 64 : t <= 2048 ? 128 : 256; }
 int64_t attn_split_chunks(int64_t t) { return (t + chunk_rows(t) - 1) / chunk_rows(t); }

@@ -249,17 +249,41 @@ def q4_layout(m, act, n_kind):
 
 
 Q4_FORMS = [("very tall", lambda c: 256 * c + 70, 1536), ("tall", lambda c: 16 * c + 11, 1536),
-            ("short", lambda c: 200, 1536), ("long K", lambda c: 150, 4128)]
+            ("short", lambda c: 200, 1536), ("long K", lambda c: 150, 4128),
+            ("down shape", lambda c: 1536, 4096), ("K a multiple of 512 only", lambda c: 300, 2560)]
 Q4_CASES = [(kind, nf, k, m) for kind, nf, k in Q4_FORMS for m in (1, 2, 3, 8)]
+
+
+def expected_q4(n, k, m, a, kind, c):
+    """The int4 kernel the dispatch rule picks: the matrix-core form for bf16
+    activations at batch 2..8 with K a multiple of 512 -- two 16-row fragments
+    per wave from 128 rows per compute unit on, else a twelve-way K split for K
+    a multiple of 1536, an eight-way one for K a multiple of 1024 below 32 rows
+    per compute unit (from batch 5 only), a four-way one otherwise (the tall
+    form from batch 3); else the vector-ALU layout of the shape's kind."""
+    if a == q8.Q8_ACT_BF16 and 2 <= m <= 8 and k % 512 == 0:
+        groups = (n + 31) // 32
+        if groups >= 4 * c:
+            lay = (16, 2, 4, 1)
+        elif k % 1536 == 0:
+            lay = (16, 1, 12, 0)
+        elif k % 1024 == 0 and groups < c:
+            lay = (16, 1, 8, 0)
+        else:
+            lay = (16, 1, 4, 0)
+        if not (lay[2] == 8 and m <= 4) and not (lay[1] == 2 and m == 2):
+            return f"q4_skinny_mfma_kernel<{m},{lay[0]},{lay[1]},{lay[2]},{lay[3]}>"
+    lay = q4_layout(m, a, kind)
+    return f"q4_skinny_kernel<{m},{a},{lay[0]},{lay[1]},{lay[2]},{lay[3]}>"
 
 
 @pytest.mark.parametrize("kind,nf,k,m", Q4_CASES, ids=[f"{c[0]}-m{c[3]}" for c in Q4_CASES])
 @pytest.mark.parametrize("act", ["q8", "bf16"])
 def test_q4_block_sums_bitwise(kind, nf, k, m, act):
-    n = nf(cus())
+    c = cus()
+    n = nf(c)
     a = q8.Q8_ACT_Q8 if act == "q8" else q8.Q8_ACT_BF16
-    lay = q4_layout(m, a, kind)
-    want = f"q4_skinny_kernel<{m},{a},{lay[0]},{lay[1]},{lay[2]},{lay[3]}>"
+    want = expected_q4(n, k, m, a, kind, c)
     got_name = q8.kernel_name(q8.OP_Q4_SKINNY, n, k, m, a)
     log(f"int4 {kind} act={act} n={n} k={k} m={m}: {got_name}")
     assert got_name == want
