@@ -1,8 +1,9 @@
-// q8_skinny_mfma.hip -- batch 2..8 W8A16 products on the bf16 matrix cores.
+// q8_skinny_mfma.hip -- batch 2..8 W8A16 (and W4A16) products on the bf16
+// matrix cores.
 //
 //   y[m][j] = sum_b wd[j][b] * sum_{i<32} wq[j][32b+i] * x[m][32b+i]
 //
-// At batch 3..8 the vector-ALU form of the decode product spends about four
+// Above batch 2 the vector-ALU form of the decode product spends about four
 // dot instructions per weight on the activation rows, more than the weight
 // bytes cost at HBM speed [Frigg README, Finding 8: a batched kernel's cost
 // should stay nearly flat in the batch size].  Here the multiply-adds go to the
@@ -14,14 +15,16 @@
 // (lane (j, g) holds D[4g .. 4g + 3][j], one weight row, so one scale per lane
 // and block).
 //
-// Loads stay coalesced: a wave's 16 RGW weight rows arrive four blocks (128
-// bytes per row) at a time with full-line 16-byte loads, eight lanes per row,
-// are written to the wave's LDS slice (row pitch 136 bytes) and read back as
-// B fragments (8 bytes per lane: row j, bytes 8g .. 8g + 7 of the block; the
-// activation fragment uses the same k positions).  Loading fragments straight
+// Loads stay coalesced: a wave's 16 RGW (or 8) weight rows arrive four blocks
+// (128 bytes per row; 64 for int4) at a time with full-line 16-byte loads,
+// eight lanes per row (four for int4), are written to the wave's LDS slice
+// (row pitch 136 bytes; 80) and read back as B fragments (8 bytes per lane:
+// row j, bytes 8g .. 8g + 7 of the block; for int4 the nibbles of elements
+// 8g .. 8g + 7; the activation fragment uses the same k positions).  Loading fragments straight
 // from memory touches 16 rows x 32 bytes per instruction and streamed the
 // lm_head at under 2 TB/s.  The next four blocks are in flight while the
-// current ones are multiplied.  KS waves of a workgroup split K (contiguous
+// current ones are multiplied (or, with a step count fixed at compile time,
+// all of a wave's blocks).  KS waves of a workgroup split K (contiguous
 // block ranges) and add their partial results through LDS in a fixed order,
 // so results are bitwise reproducible; no atomics.
 #include "q8_device.hpp"
