@@ -812,6 +812,12 @@ def main() -> int:
                     help="run only the prefill products (for hardware-counter passes)")
     ap.add_argument("--prefill-p", type=int, nargs="*", default=[256],
                     help="P values of --prefill-only")
+    ap.add_argument("--lm-head-only", action="store_true",
+                    help="run only the lm_head products at the --lm-head-m batches, int4 and Q8_0, "
+                         "bf16 and Q8 activations, and the 1 GiB copy that scales byte counters "
+                         "(for hardware-counter passes)")
+    ap.add_argument("--lm-head-m", type=int, nargs="*", default=[1, 2, 4, 8],
+                    help="batches of --lm-head-only")
     ap.add_argument("--details", default=None, help="also write the full per-figure details (JSON) to this path")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -820,7 +826,7 @@ def main() -> int:
               "one; run with --gpus 1.", file=sys.stderr)
         return 2
 
-    want_cpu = not args.metric_only and not args.no_cpu_baseline and not args.prefill_only
+    want_cpu = not (args.metric_only or args.no_cpu_baseline or args.prefill_only or args.lm_head_only)
     if want_cpu:
         import oracle
         oracle.ensure_built()                 # before the GPU is touched: no compiler after that
@@ -845,6 +851,19 @@ def main() -> int:
                     q8, wl.normal_weights(wl.mimir_weight_seed(0, proj), n_, k_), dev)
         res = bench_prefill(q8, wl, dev, weights, sweep=tuple(args.prefill_p))
         print(json.dumps({"prefill": res}), flush=True)
+        return 0
+
+    if args.lm_head_only:
+        if any(m < 1 or m > 8 for m in args.lm_head_m):
+            print("--lm-head-m takes batches 1..8", file=sys.stderr)
+            return 2
+        cfg = wl.CONFIGS["lm_head_gemv_262144x1536_b1"]
+        w_dev = to_dev(wl.normal_weights(cfg["w_seed"], cfg["n"], cfg["k"]), dev)
+        wq, wd = q8.quantize_weights(w_dev)
+        copies = [(wq, wd), (wq.clone(), wd.clone())]
+        res = {"lm_head_batches": bench_lm_head_batches(q8, wl, dev, w_dev, copies, m_list=tuple(args.lm_head_m)),
+               "copy_probe": bench_copy_probe(dev)}
+        print(json.dumps(res), flush=True)
         return 0
 
     # ---- headline: lm_head-shaped GEMV, batch 1

@@ -319,8 +319,7 @@ q8_status q8_kernel_name(int op, int64_t n, int64_t k, int64_t rows, int act, ch
     } else if (op == Q8_OP_Q4_SKINNY && act == Q8_ACT_BF16 &&
                q8::q4_mfma_applies(n, k, (int)rows, dev->cu_count)) {
         const q8::SkinnyLayout L = q8::q4_mfma_layout(n, k, dev->cu_count);
-        std::snprintf(name, sizeof name, "q4_skinny_mfma_kernel<%d,%d,%d,%d,%d>", (int)rows, L.g, L.r, L.cpl,
-                      L.r == 2 ? 1 : 0);
+        std::snprintf(name, sizeof name, "q4_skinny_mfma_kernel<%d,%d,%d,%d,0>", (int)rows, L.g, L.r, L.cpl);
     } else if (op == Q8_OP_Q4_SKINNY) {
         const q8::Q4Layout L = q8::q4_layout(n, k, (int)rows, act, dev->cu_count);
         std::snprintf(name, sizeof name, "q4_skinny_kernel<%d,%d,%d,%d,%d,%d>", (int)rows, act, L.g, L.r, L.cpl,

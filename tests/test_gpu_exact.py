@@ -264,7 +264,7 @@ def expected_q4(n, k, m, a, kind, c):
     if a == q8.Q8_ACT_BF16 and 2 <= m <= 8 and k % 512 == 0:
         groups = (n + 31) // 32
         if groups >= 4 * c:
-            lay = (16, 2, 4, 1)
+            lay = (16, 2, 4, 0)                     # (int4: cached weight loads on the tall layout)
         elif k % 1536 == 0:
             lay = (16, 1, 12, 0)
         elif k % 1024 == 0 and groups < c:
