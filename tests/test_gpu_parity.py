@@ -270,6 +270,29 @@ def test_gemv_lm_head_config_full():
     assert_close(to_host(yq)[None, :], oracle.q8q8(oq, od, xq, xd), "lm_head gemv q8")
 
 
+@pytest.mark.parametrize("m", [2, 8])
+def test_skinny_lm_head_full_batches(m):
+    """The full 262144 x 1536 lm_head at batch 2 and 8 (the matrix-core form
+    with bf16 activations, the vector form with Q8 activations) against the
+    oracle on 4096 sampled rows."""
+    cfg = wl.CONFIGS["lm_head_gemv_262144x1536_b1"]
+    log(f"lm_head full m={m}: generating 262144 x 1536")
+    w = wl.normal_weights(cfg["w_seed"], cfg["n"], cfg["k"])
+    x = wl.normal_act_bf16(7600 + m, m, cfg["k"])
+    oq, od = oracle.quantize_f32(w)                   # the oracle's codes, uploaded
+    del w
+    wq, wd = to_dev(oq), to_dev(od)
+    rows = np.sort(wl.rng(7700 + m).choice(cfg["n"], size=4096, replace=False))
+    log(f"lm_head full m={m}: {q8.kernel_name(q8.OP_SKINNY, cfg['n'], cfg['k'], m, q8.Q8_ACT_BF16)}")
+    y = q8.gemm_skinny(wq, wd, to_dev(x))
+    torch.cuda.synchronize()
+    assert_close(to_host(y)[:, rows], oracle.w8a16(oq, od, x, rows=rows), f"lm_head bf16 m={m}")
+    xq, xd = oracle.quantize_bf16(x)
+    yq = q8.gemm_skinny(wq, wd, to_dev(xq), to_dev(xd))
+    torch.cuda.synchronize()
+    assert_close(to_host(yq)[:, rows], oracle.q8q8(oq, od, xq, xd, rows=rows), f"lm_head q8 m={m}")
+
+
 @pytest.mark.parametrize("m", [2, 4, 8])
 def test_skinny_mimir_shapes(m):
     for proj, (name, n, k) in enumerate(wl.BLOCK_SHAPES):
