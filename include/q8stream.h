@@ -124,7 +124,10 @@ q8_status q8_gemv(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k,
  * for all rows [Frigg README, Finding 8: looping the GEMV re-reads the weights
  * per row; a batched kernel costs nearly the same at every batch size].
  * x is bf16 [m][k] (act BF16) or int8 [m][k] with xd [m][k/32] (act Q8);
- * y is fp32 [m][n]. */
+ * y is fp32 [m][n].  Row t of y depends on row t of x only, bit for bit; for a
+ * given (n, k, m, act) results are bitwise reproducible, but a row's last bits
+ * may differ between batch sizes (each may take another kernel and fp32
+ * summation order; bf16 activations at batch 2-8 go to the matrix cores). */
 q8_status q8_gemm_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k,
                          int64_t m, int act, const void* x, const uint16_t* xd,
                          float* y, hipStream_t stream);
