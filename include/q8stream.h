@@ -354,7 +354,8 @@ q8_status q4_quantize_weights(const float* w, int64_t n, int64_t k,
  * c the unpacked codes.  act Q8_ACT_BF16: x is bf16 [m][k], xd NULL, fp32
  * accumulation.  act Q8_ACT_Q8: x is int8 codes [m][k] with binary16 xd
  * [m][k/32]; each block contributes wd * xd * (exact int32 sum of code
- * products).  y is fp32 [m][n]. */
+ * products).  y is fp32 [m][n].  Batch behaviour as q8_gemm_skinny (bf16
+ * activations at batch 2-8 go to the matrix cores on most shapes). */
 q8_status q4_gemm_skinny(const uint8_t* wq, const uint16_t* wd, int64_t n, int64_t k,
                          int64_t m, int act, const void* x, const uint16_t* xd,
                          float* y, hipStream_t stream);
