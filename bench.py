@@ -339,6 +339,40 @@ def bench_lm_head_batches(q8, wl, dev, w, q8_copies, m_list=(1, 2, 4, 8)) -> dic
     return out
 
 
+def bench_lm_head_shards(q8, wl, dev, q8_copies, ways=(2, 4, 8)) -> dict:
+    """One GPU's share of the lm_head when the vocabulary rows are split over
+    `ways` GPUs (262144 / ways rows x 1536, batch 1, bf16 activations): each GPU
+    would stream its own rows and write its own slice of y, with no reduction.
+    Timed here on one GPU, graph-replayed, rotating through every row slice of
+    both weight copies (858 MB between reuses, past the 256 MB Infinity
+    Cache)."""
+    import torch
+    cfg = wl.CONFIGS["lm_head_gemv_262144x1536_b1"]
+    n, k = cfg["n"], cfg["k"]
+    x = to_dev(wl.rms_unit_act_bf16(cfg["x_seed"], k)[0], dev)
+    out = {}
+    for g in ways:
+        rows = n // g
+        shards = [(cq[i * rows:(i + 1) * rows], cd[i * rows:(i + 1) * rows])
+                  for cq, cd in q8_copies for i in range(g)]
+        y = torch.empty(rows, dtype=torch.float32, device=dev)
+        cnt = [0]
+
+        def call():
+            wq, wd = shards[cnt[0] % len(shards)]
+            cnt[0] += 1
+            q8.gemv(wq, wd, x, out=y)
+
+        st = graph_us(call, 2 * len(shards))
+        nbytes = gemv_bytes(rows, k)
+        out[f"{g}_way"] = {"rows": rows, "us_per_call": st, "bytes_per_call": nbytes,
+                           "GBps": nbytes / st["median"] / 1e3,
+                           "frac_hbm_peak": nbytes / st["median"] / 1e3 / HBM_PEAK_GBPS,
+                           "kernel": q8.kernel_name(q8.OP_SKINNY, rows, k, 1)}
+        log(f"lm_head shard of {g}: {rows} x {k}: {st['median']:.2f} us, {nbytes / st['median'] / 1e3:.0f} GB/s")
+    return out
+
+
 def load_mimir(q8, wl, dev) -> tuple[dict, dict]:
     """The 128 block matrices and the lm_head in Q8_0, and the block matrices
     also in int4 (the "int4 core + int8 vocab" build), from one draw each."""
@@ -797,6 +831,11 @@ def summarize(extras: dict, cpu) -> dict:
     if lb:
         for m in (1, 2, 4, 8):
             s[f"lm_head_bf16_b{m}_us"] = r4(lb["q8_0"][f"bf16_b{m}"]["us_per_call"]["median"])
+    sh = extras.get("lm_head_row_shards")
+    if sh:
+        for key, v in sh.items():
+            s[f"lm_head_shard_{key}_us"] = r4(v["us_per_call"]["median"])
+            s[f"lm_head_shard_{key}_frac_hbm"] = r4(v["frac_hbm_peak"])
     if "read_probe" in extras:
         s["read_peak_GBps"] = r4(extras["read_probe"]["GBps"])
     if "copy_probe" in extras:
@@ -917,6 +956,7 @@ def main() -> int:
         log("lm_head products at batch 1-8, int4 and Q8_0")
         w_dev = to_dev(w_np, dev)
         extras["lm_head_batches"] = bench_lm_head_batches(q8, wl, dev, w_dev, copies)
+        extras["lm_head_row_shards"] = bench_lm_head_shards(q8, wl, dev, copies)
         extras["weight_quantize_262144x1536"], wq_sample = bench_quantize_weights(q8, w_dev)
         del w_dev
         torch.cuda.empty_cache()

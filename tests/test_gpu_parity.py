@@ -293,6 +293,46 @@ def test_skinny_lm_head_full_batches(m):
     assert_close(to_host(yq)[:, rows], oracle.q8q8(oq, od, xq, xd, rows=rows), f"lm_head q8 m={m}")
 
 
+def test_lm_head_row_shards_equal_rows_of_whole():
+    """Splitting the lm_head's rows over G GPUs (G = 2, 4, 8) is exact: one
+    GPU's share (262144 / G rows, its real shape) gives bit for bit the same
+    rows as the whole product when both take the same kernel form (asserted),
+    at batch 1 (bf16 and Q8 activations) and batch 8; the smallest share is
+    also checked against the oracle on sampled rows."""
+    cfg = wl.CONFIGS["lm_head_gemv_262144x1536_b1"]
+    n, k = cfg["n"], cfg["k"]
+    log("lm_head shards: generating 262144 x 1536")
+    w = wl.normal_weights(cfg["w_seed"], n, k)
+    oq, od = oracle.quantize_f32(w)
+    del w
+    wq, wd = to_dev(oq), to_dev(od)
+    x1 = wl.rms_unit_act_bf16(cfg["x_seed"], k)
+    x8 = wl.normal_act_bf16(7800, 8, k)
+    xq, xd = oracle.quantize_bf16(x1)
+    whole = {"b1 bf16": to_host(q8.gemm_skinny(wq, wd, to_dev(x1))),
+             "b1 q8": to_host(q8.gemm_skinny(wq, wd, to_dev(xq), to_dev(xd))),
+             "b8 bf16": to_host(q8.gemm_skinny(wq, wd, to_dev(x8)))}
+    for g in (2, 4, 8):
+        rows = n // g
+        for s in (0, g - 1):
+            sq, sd = wq[s * rows:(s + 1) * rows], wd[s * rows:(s + 1) * rows]
+            part = {"b1 bf16": q8.gemm_skinny(sq, sd, to_dev(x1)),
+                    "b1 q8": q8.gemm_skinny(sq, sd, to_dev(xq), to_dev(xd)),
+                    "b8 bf16": q8.gemm_skinny(sq, sd, to_dev(x8))}
+            torch.cuda.synchronize()
+            for key, y in part.items():
+                m, act = (8 if key.startswith("b8") else 1), (q8.Q8_ACT_Q8 if key.endswith("q8") else q8.Q8_ACT_BF16)
+                name = q8.kernel_name(q8.OP_SKINNY, rows, k, m, act)
+                log(f"shard {s} of {g} ({rows} rows) {key}: {name}")
+                assert name == q8.kernel_name(q8.OP_SKINNY, n, k, m, act)
+                assert np.array_equal(to_host(y).view(np.int32),
+                                      whole[key][:, s * rows:(s + 1) * rows].view(np.int32)), (g, s, key)
+    rows = n // 8
+    pick = np.sort(wl.rng(7801).choice(rows, size=512, replace=False))
+    y = to_host(q8.gemm_skinny(wq[:rows], wd[:rows], to_dev(x1)))
+    assert_close(y[:, pick], oracle.w8a16(oq[:rows], od[:rows], x1, rows=pick), "lm_head shard of 8")
+
+
 @pytest.mark.parametrize("m", [2, 4, 8])
 def test_skinny_mimir_shapes(m):
     for proj, (name, n, k) in enumerate(wl.BLOCK_SHAPES):
