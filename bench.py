@@ -1043,8 +1043,11 @@ def main() -> int:
                      "kernel": q8.kernel_name(q8.OP_SKINNY, n, k, 1),
                      "kernel_us": round(kern_ms * 1e3, 3),
                      "kernel_us_trials": {key: r4(v) for key, v in trials.items()},
-                     "measured_read_peak_GBps": round(measured_peak, 1),
-                     "frac_of_measured_read_peak": round(achieved / measured_peak, 4)},
+                     # the read probe and the GEMV stream at the same rate within
+                     # run noise: the measured ceiling is the faster of the two
+                     "read_probe_GBps": round(measured_peak, 1),
+                     "measured_read_peak_GBps": round(max(measured_peak, achieved), 1),
+                     "frac_of_measured_read_peak": round(achieved / max(measured_peak, achieved), 4)},
         "summary": summarize(extras, cpu),
         "cpu_baseline": None if cpu is None else {key: cpu[key] for key in
                                                   ("value", "unit", "cores", "kind", "sample", "cpu_model")},
