@@ -20,9 +20,9 @@
 // eight lanes per row (four for int4), are written to the wave's LDS slice
 // (row pitch 136 bytes; 80) and read back as B fragments (8 bytes per lane:
 // row j, bytes 8g .. 8g + 7 of the block; for int4 the nibbles of elements
-// 8g .. 8g + 7; the activation fragment uses the same k positions).  Loading fragments straight
-// from memory touches 16 rows x 32 bytes per instruction and streamed the
-// lm_head at under 2 TB/s.  The next four blocks are in flight while the
+// 8g .. 8g + 7; the activation fragment uses the same k positions).  Loading
+// fragments straight from memory touches 16 rows x 32 bytes per instruction
+// and streamed the lm_head at under 2 TB/s.  The next four blocks are in flight while the
 // current ones are multiplied (or, with a step count fixed at compile time,
 // all of a wave's blocks).  KS waves of a workgroup split K (contiguous
 // block ranges) and add their partial results through LDS in a fixed order,
@@ -229,14 +229,16 @@ hipError_t launch_m(const int8_t* wq, const uint16_t* wd, int64_t n, int nb, con
 
 }  // namespace
 
-// The matrix-core form is used for bf16 activations from batch 3 on where it
-// measured faster than the vector-ALU form (graph replay, weights rotated past
-// the caches): every Mimir shape and the lm_head at batch 5..8; at batch 2..4
-// only matrices of at least 64 rows per compute unit (the lm_head, batch 2:
-// 71.1 against 79.8 us), where the vector form's per-weight arithmetic shows
-// (qkv and gate_up at batch 2..4 measured faster alone on the matrix cores but
-// level or slower inside the decode step: 2.25 against 2.17 ms at batch 3).  It needs K a multiple of 512 (whole four-block
-// steps in each of the four K slices).  Tall matrices (4 or more 32-row
+// The matrix-core form is used for bf16 activations where it measured faster
+// than the vector-ALU form (graph replay, weights rotated past the caches):
+// every shape at batch 5..8, and at batch 2..4 only matrices of at least 64
+// rows per compute unit (the lm_head, batch 2: 71.1 against 79.8 us), where
+// the vector form's per-weight arithmetic shows (qkv and gate_up at batch 2..4
+// measured faster alone on the matrix cores but level or slower inside the
+// decode step: 2.25 against 2.17 ms at batch 3).  Q8 activations keep the
+// vector form (on the int8 matrix cores the step measured slower at every
+// batch).  It needs K a multiple of 512 (whole four-block steps in each of the
+// four K slices).  Tall matrices (4 or more 32-row
 // workgroups per compute unit) use two 16-row groups per wave and
 // non-temporal weight loads; shorter ones one group with K split over the
 // waves of a workgroup: twelve ways when the 32-element blocks are a multiple
@@ -284,8 +286,9 @@ hipError_t launch_skinny_mfma(const int8_t* wq, const uint16_t* wd, int64_t n, i
 // except on that down layout below batch 5 and on tall matrices at batch 2,
 // where the vector form is level or faster (int4 lm_head batch 2: 50.8 against
 // 56.4 us; the int4 decode step at batch 4: 2.18 against 2.33 ms with the
-// vector form below batch 5).  Batch 8 against the vector form: lm_head 60.8 / 97.5 us, qkv 4.65 /
-// 6.72, o 3.66 / 4.90, gate_up 4.85 / 7.01, down 6.15 / 8.35.
+// vector form below batch 5).  Batch 8 against the vector form: lm_head 60.8 /
+// 97.5 us, qkv 4.65 / 6.72, o 3.66 / 4.90, gate_up 4.85 / 7.01, down 6.15 /
+// 8.35.
 SkinnyLayout q4_mfma_layout(int64_t n, int64_t k, int cu_count) {
     if ((n + 31) / 32 >= 4 * (int64_t)cu_count) return SkinnyLayout{16, 2, 4, true};
     if (k % 1536 == 0) return SkinnyLayout{16, 1, 12, true};
