@@ -127,7 +127,8 @@ q8_status q8_gemv(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k,
  * y is fp32 [m][n].  Row t of y depends on row t of x only, bit for bit; for a
  * given (n, k, m, act) results are bitwise reproducible, but a row's last bits
  * may differ between batch sizes (each may take another kernel and fp32
- * summation order; bf16 activations at batch 2-8 go to the matrix cores). */
+ * summation order; bf16 activations take the matrix cores at batch 5-8, and
+ * at batch 2-4 on matrices of at least 64 rows per compute unit). */
 q8_status q8_gemm_skinny(const int8_t* wq, const uint16_t* wd, int64_t n, int64_t k,
                          int64_t m, int act, const void* x, const uint16_t* xd,
                          float* y, hipStream_t stream);
