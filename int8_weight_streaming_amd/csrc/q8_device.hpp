@@ -63,18 +63,35 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 // Exact int32 dot of one 32-element Q8 block split over a lane pair (lanes 2i
 // and 2i + 1): each lane holds one 16-byte half of the weight and activation
-// codes, takes its four signed v_dot4_i32_i8, and one DPP step adds the
-// partner's half; both lanes end with the block's sum
-// [fak MODEL-BASELINE-RESULTS, ACT 3 item 3: signed x signed int8 block dot].
-// |sum| <= 32 * 127 * 127 = 516,128, far inside int32.  Every lane of the
-// wave must execute it (the DPP step reads the partner's register).
-__device__ __forceinline__ int block_dot_halves(const u32x4& w, const u32x4& x) {
+// codes and takes its four signed v_dot4_i32_i8 (half_dot), and one DPP step
+// adds the partner's half [fak MODEL-BASELINE-RESULTS, ACT 3 item 3: signed x
+// signed int8 block dot].  |sum| <= 32 * 127 * 127 = 516,128, far inside
+// int32.  Every lane of the wave must execute these (the DPP step reads the
+// partner's register).
+__device__ __forceinline__ int half_dot(const u32x4& w, const u32x4& x) {
     int s = 0;
     s = __builtin_amdgcn_sdot4((int)w.x, (int)x.x, s, false);
     s = __builtin_amdgcn_sdot4((int)w.y, (int)x.y, s, false);
     s = __builtin_amdgcn_sdot4((int)w.z, (int)x.z, s, false);
     s = __builtin_amdgcn_sdot4((int)w.w, (int)x.w, s, false);
-    return s + __builtin_amdgcn_update_dpp(0, s, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+    return s;
+}
+__device__ __forceinline__ int pair_swap(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);        // quad_perm [1,0,3,2]
+}
+// One block sum, on both lanes of the pair.
+__device__ __forceinline__ int block_dot_halves(const u32x4& w, const u32x4& x) {
+    const int s = half_dot(w, x);
+    return s + pair_swap(s);
+}
+// Two block sums at once, one per lane: the even lane ends with block sum A
+// (wa . xa), the odd lane with block sum B (wb . xb).  Each lane sends its
+// partner its half of the product it does not keep, so one DPP add finishes
+// both and neither lane converts or folds a sum twice.
+__device__ __forceinline__ int block_dot_pair(const u32x4& wa, const u32x4& xa, const u32x4& wb,
+                                              const u32x4& xb, bool even) {
+    const int ha = half_dot(wa, xa), hb = half_dot(wb, xb);
+    return (even ? ha : hb) + pair_swap(even ? hb : ha);
 }
 
 // ---------------------------------------------------------------- buffer loads
@@ -153,6 +170,22 @@ __device__ __forceinline__ float xor32_value(float v) {
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
     v = row16_sum(v);
+    if (G >= 32) v = xor16_sum(v);
+    if (G >= 64) v = xor32_sum(v);
+    return v;
+}
+
+// Sum over the lanes of one parity in each group of G lanes (G = 16, 32 or
+// 64): a butterfly over lane ^ 2, lane ^ 4, lane ^ 8 (then the permlane
+// swaps), each step adding the same two values in both orders, so every lane
+// of a parity class ends with the same bits and equal inputs give equal sums
+// wherever they sit.  Lane ^ 4 is the half-row mirror (lane -> 7 - lane in
+// each 8) read back through a reversal of each quad.
+template <int G>
+__device__ __forceinline__ float group_sum_parity(float v) {
+    v += dpp_f<0x4E>(v);                   // quad_perm [2,3,0,1]: lane ^ 2
+    v += dpp_f<0x1B>(dpp_f<0x141>(v));     // quad_perm [3,2,1,0] of the half-row mirror: lane ^ 4
+    v += dpp_f<0x128>(v);                  // row_ror:8: lane ^ 8
     if (G >= 32) v = xor16_sum(v);
     if (G >= 64) v = xor32_sum(v);
     return v;

@@ -234,9 +234,11 @@ __device__ __forceinline__ void paired_epilogue(float a, float b, int64_t row, i
 // Activations of one K tile: registers or LDS.
 template <int M, int ACT, int CPL>
 struct XRegs {
-    // bf16: 8 dwords per chunk; Q8: 4 dwords of codes per chunk + block scale.
+    // bf16: 8 dwords per chunk; Q8: 4 dwords of codes per chunk + the block
+    // scale's binary16 bits (converted where it is used: a conversion next to
+    // the load would wait for it before the weight loads are issued).
     uint32_t v[M][CPL][ACT == 0 ? 8 : 4];
-    float s[M][CPL];
+    uint16_t s[M][CPL];
 };
 
 // Activations in registers at batch 1-2 (bf16 or Q8 input); fp32 input
@@ -301,6 +303,15 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
     if constexpr (AT) attn_parts_load<NC>(static_cast<const float*>(xv), k, (int)fa.attn_chunks, ao, aml);
     else if constexpr (RS) stage_load<M>(static_cast<const float*>(xv), k, sv);
 
+    // Q8 activations: the products (row r, activation row m), numbered
+    // c = m R + r, are taken two at a time; the even lane of a chunk pair
+    // accumulates product 2p of slot p, the odd lane product 2p + 1 (an odd
+    // last product: the even lane alone), so that one DPP add finishes both
+    // block sums (block_dot_pair) and each is converted and folded once.
+    static_assert(ACT == 0 || EPI == kEpiF32 || EPI == kEpiAdd, "Q8 activations store one value per lane");
+    constexpr int NPS = (R * M + 1) / 2;
+    const bool even = (gl & 1) == 0;
+
     const int8_t* wrow[R];
     const uint16_t* srow[R];
 #pragma unroll
@@ -314,6 +325,9 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+    float pacc[ACT == 1 ? NPS : 1];
+#pragma unroll
+    for (int p = 0; p < (ACT == 1 ? NPS : 1); ++p) pacc[p] = 0.0f;
 
     // staged activation pieces of a tile (batch 3-8), see below
     constexpr bool XPRE = !XREG && PRO == kProBf16;
@@ -338,7 +352,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
                         const uint4 a = *reinterpret_cast<const uint4*>(
                             static_cast<const int8_t*>(xv) + m * k + (int64_t)cc * 16);
                         xr.v[m][j][0] = a.x; xr.v[m][j][1] = a.y; xr.v[m][j][2] = a.z; xr.v[m][j][3] = a.w;
-                        xr.s[m][j] = half_bits_to_float(xdp[(int64_t)m * nb + (cc >> 1)]);
+                        xr.s[m][j] = xdp[(int64_t)m * nb + (cc >> 1)];
                     }
                 }
             }
@@ -471,6 +485,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
                         const int i0 = threadIdx.x + 256 * u;
                         const int i = i0 < nsc ? i0 : nsc - 1;
                         const int bl = i % (tch >> 1), m = i / (tch >> 1);
+                        pin(xsb[u]);      // converted here, not hoisted above the weight loads
                         sc[m * (TCH / 2) + bl] = half_bits_to_float(xsb[u]);
                     }
                 }
@@ -534,27 +549,35 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
                     }
                 }
             } else {
-                const bool even = (gl & 1) == 0;
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    uint32_t xc[4];
-                    float xs;
+                // exact int32 block sums: this lane's half and its neighbour's
+                auto xload = [&](int m, u32x4& xc, float& xs) {
                     if (XREG) {
-#pragma unroll
-                        for (int d = 0; d < 4; ++d) xc[d] = xr.v[m][j][d];
-                        xs = xr.s[m][j];
+                        xc = (u32x4){xr.v[m][j][0], xr.v[m][j][1], xr.v[m][j][2], xr.v[m][j][3]};
+                        xs = half_bits_to_float(xr.s[m][j]);
                     } else {
                         const uint4 a = *reinterpret_cast<const uint4*>(lds + (m * TCH + clc) * 16);
-                        xc[0] = a.x; xc[1] = a.y; xc[2] = a.z; xc[3] = a.w;
+                        xc = (u32x4){a.x, a.y, a.z, a.w};
                         xs = reinterpret_cast<const float*>(lds + M * TCH * 16)[m * (TCH / 2) + (clc >> 1)];
                     }
+                };
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        // exact int32 block sum: this lane's half and its neighbour's
-                        const u32x4 xv = {xc[0], xc[1], xc[2], xc[3]};
-                        const int s = block_dot_halves(w[j][r], xv);
-                        const float t = even ? ws[j][r] * xs : 0.0f;
-                        acc[r][m] = fmaf((float)s, t, acc[r][m]);
+                for (int p = 0; p < NPS; ++p) {
+                    const int ca = 2 * p, cb = 2 * p + 1;
+                    const int ma = ca / R, ra = ca % R;
+                    u32x4 xa;
+                    float sa;
+                    xload(ma, xa, sa);
+                    if (cb < R * M) {
+                        const int mb = cb / R, rb = cb % R;
+                        u32x4 xb = xa;
+                        float sb2 = sa;
+                        if (mb != ma) xload(mb, xb, sb2);
+                        const int s = block_dot_pair(w[j][ra], xa, w[j][rb], xb, even);
+                        const float t = (even ? ws[j][ra] : ws[j][rb]) * (even ? sa : sb2);
+                        pacc[p] = fmaf((float)s, t, pacc[p]);
+                    } else {
+                        const int s = block_dot_halves(w[j][ra], xa);
+                        pacc[p] = fmaf((float)s, even ? ws[j][ra] * sa : 0.0f, pacc[p]);
                     }
                 }
             }
@@ -562,11 +585,23 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t* __restrict__ 
     }
 
     // Combine the G partial sums of every (row, m); all lanes of the group end
-    // with the same value.
+    // with the same value.  Q8 activations: the sums over the lanes of one
+    // parity, so a lane of parity q holds product 2p + q of every slot p (the
+    // lane that stores a product has its parity, see the store below).
+    if constexpr (ACT == 1) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+        for (int p = 0; p < NPS; ++p) {
+            const float v = group_sum_parity<G>(pacc[p]);
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = group_sum<G>(acc[r][m]);
+            for (int q = 0; q < 2; ++q)
+                if (2 * p + q < R * M) acc[(2 * p + q) % R][(2 * p + q) / R] = v;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[r][m] = group_sum<G>(acc[r][m]);
+    }
 
     if constexpr (EPI == kEpiF32 || EPI == kEpiAdd) {
         // Lane g of the group stores value g (then g + G, ...): rows of one m
