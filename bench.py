@@ -582,18 +582,21 @@ PREFILL_SWEEP = (16, 64, 256, 1024, 4096)
 
 def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP, int8_peak_measured=None) -> dict:
     """Q8 x Q8 prefill: qkv and gate_up on [P, 1536] activations, down on
-    [P, 4096] (block-0 weights), each product graph-replayed.  P = 256 is the
-    configured workload (activations with the seeded special rows); the sweep
-    over P also fits time = fixed + P * slope for the three products, the
-    pages' prefill measure, and for the products with their activation side
-    (RMSNorm + quantizer fused for qkv and gate_up, the plain quantizer for
-    down)."""
+    [P, 4096] (block-0 weights), each product graph-replayed.  The headline
+    figures are those of the fragment-order product (weights packed once,
+    activations packed per call); the row-major product is timed beside it.
+    P = 256 is the configured workload (activations with the seeded special
+    rows); the sweep over P also fits time = fixed + P * slope for the three
+    products, the pages' prefill measure, and for the products with their
+    activation side (RMSNorm + quantizer fused for qkv and gate_up, the plain
+    quantizer for down, then the fragment packing of each activation matrix)."""
     import torch
     cfg = wl.CONFIGS["prefill_p256"]
     gemms = []
     for proj, (name, n, k) in enumerate(wl.BLOCK_SHAPES):
         if name != "o":
-            gemms.append((name, n, k, weights[(0, proj)]))
+            wq, wd = weights[(0, proj)]
+            gemms.append((name, n, k, (wq, wd), q8.pack_frag(wq, wd)))
     per_p = {}
     for P in sweep:
         if P == 256:
@@ -606,46 +609,60 @@ def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP, int8_peak_measured=
         for kk, xn in ((wl.HIDDEN, xa), (wl.INTER, xb)):
             xd_ = to_dev(xn, dev)
             q, d = q8.quantize_act(xd_)
-            xs[kk] = (xd_, q, d)
-        rows, tot_us, ops, nbytes = {}, 0.0, 0, 0
-        for name, n, k, (wq, wd) in gemms:
-            _, xq, xd = xs[k]
+            xs[kk] = (xd_, q, d, q8.pack_frag(q, d))
+        rows, rows_rm, tot_us, tot_rm, ops, nbytes = {}, {}, 0.0, 0.0, 0, 0
+        for name, n, k, (wq, wd), wf in gemms:
+            _, xq, xd, xf = xs[k]
             y = torch.empty((P, n), dtype=torch.float32, device=dev)
-            st = graph_us(lambda: q8.gemm_prefill(wq, wd, xq, xd, out=y), 10 if P >= 1024 else 20)
+            per_graph = 10 if P >= 1024 else 20
+            st = graph_us(lambda: q8.gemm_prefill_frag(wf, xf, out=y), per_graph)
+            st_rm = graph_us(lambda: q8.gemm_prefill(wq, wd, xq, xd, out=y), per_graph)
             o = 2 * P * n * k
-            rows[name] = {"us": st, "TOPS": o / st["median"] / 1e6, "kernel": q8.kernel_name(q8.OP_PREFILL, n, k, P)}
+            rows[name] = {"us": st, "TOPS": o / st["median"] / 1e6,
+                          "kernel": q8.kernel_name(q8.OP_PREFILL_FRAG, n, k, P)}
+            rows_rm[name] = {"us": st_rm, "TOPS": o / st_rm["median"] / 1e6,
+                             "kernel": q8.kernel_name(q8.OP_PREFILL, n, k, P)}
             tot_us += st["median"]
+            tot_rm += st_rm["median"]
             ops += o
             nbytes += prefill_bytes(n, k, P)
-        q_us = {}
-        for kk, (x_, q, d) in xs.items():
+        q_us, pack_us = {}, {}
+        for kk, (x_, q, d, xf) in xs.items():
             q_us[kk] = graph_us(lambda: q8.quantize_act(x_, out=(q, d)), 20)["median"]
+            pack_us[kk] = graph_us(lambda: q8.pack_frag(q, d, out=(xf.q, xf.d)), 20)["median"]
         # the activation side of qkv / gate_up: RMSNorm of the fp32 residual
         # rows, bf16, Q8_0 -- one fused launch, or norm then quantize
         h_ = to_dev(wl.bf16_bits_to_f32(xa), dev)
-        _, hq, hd = xs[wl.HIDDEN]
+        _, hq, hd, _ = xs[wl.HIDDEN]
         fused_us = graph_us(lambda: q8.quantize_act_fused(h_, q8.PRO_RMSNORM, out=(hq, hd)), 20)["median"]
         nrm = torch.empty_like(h_)
         chain_us = graph_us(lambda: (q8.rmsnorm(h_, out=nrm),
                                      q8.quantize_act_fused(nrm, q8.PRO_F32, out=(hq, hd))), 20)["median"]
         tops = ops / tot_us / 1e6
+        tops_rm = ops / tot_rm / 1e6
         per_p[P] = {"us_three_gemms": tot_us, "int_ops": ops, "TOPS": tops,
                     "frac_int8_peak": tops / INT8_PEAK_TOPS,
                     "frac_measured_int8_peak": tops / int8_peak_measured if int8_peak_measured else None,
                     "bytes": nbytes, "us_per_token": tot_us / P, "per_gemm": rows,
-                    "quantize_act_us": sum(q_us.values()),
+                    "row_major": {"us_three_gemms": tot_rm, "TOPS": tops_rm,
+                                  "frac_int8_peak": tops_rm / INT8_PEAK_TOPS, "per_gemm": rows_rm},
+                    "quantize_act_us": sum(q_us.values()), "pack_frag_act_us": sum(pack_us.values()),
                     "rmsnorm_quantize_fused_us": fused_us, "rmsnorm_then_quantize_us": chain_us,
-                    "us_products_with_activation_side": tot_us + 2 * fused_us + q_us[wl.INTER]}
+                    "us_products_with_activation_side": tot_us + 2 * fused_us + q_us[wl.INTER]
+                    + 2 * pack_us[wl.HIDDEN] + pack_us[wl.INTER]}
         log(f"prefill P={P}: {tot_us:.1f} us, {tops:.0f} TOPS ({100 * tops / INT8_PEAK_TOPS:.1f}% of int8 peak); "
-            + ", ".join(f"{nm} {r['us']['median']:.1f} us ({r['kernel']})" for nm, r in rows.items()))
+            + ", ".join(f"{nm} {r['us']['median']:.1f} us ({r['kernel']})" for nm, r in rows.items())
+            + f"; row-major {tot_rm:.1f} us ({100 * tops_rm / INT8_PEAK_TOPS:.1f}%)")
     ps = np.array(sorted(per_p), dtype=np.float64)
-    ts = np.array([per_p[int(P)]["us_three_gemms"] for P in ps])
     big = ps >= 256
     out = dict(per_p[256]) if 256 in per_p else {}
     out["p_sweep"] = {str(P): v for P, v in per_p.items()}
     if big.sum() >= 2:
+        ts = np.array([per_p[int(P)]["us_three_gemms"] for P in ps])
+        tr = np.array([per_p[int(P)]["row_major"]["us_three_gemms"] for P in ps])
         ta = np.array([per_p[int(P)]["us_products_with_activation_side"] for P in ps])
-        for key, tt in (("fit_p_ge_256", ts), ("fit_p_ge_256_with_activation_side", ta)):
+        for key, tt in (("fit_p_ge_256", ts), ("fit_p_ge_256_row_major", tr),
+                        ("fit_p_ge_256_with_activation_side", ta)):
             slope, fixed = np.polyfit(ps[big], tt[big], 1)
             out[key] = {"fixed_us": float(fixed), "slope_us_per_token": float(slope),
                         "slope_ms_per_token": float(slope) * 1e-3}
@@ -816,6 +833,7 @@ def summarize(extras: dict, cpu) -> dict:
         s["prefill_p256_TOPS"] = r4(pf["TOPS"])
         s["prefill_p256_frac_int8_peak"] = r4(pf["frac_int8_peak"])
         s["prefill_p256_frac_measured_int8_peak"] = r4(pf["frac_measured_int8_peak"])
+        s["prefill_p256_row_major_us"] = r4(pf["row_major"]["us_three_gemms"])
         p4 = pf.get("p_sweep", {}).get("4096")
         if p4:
             s["prefill_p4096_frac_int8_peak"] = r4(p4["frac_int8_peak"])

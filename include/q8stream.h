@@ -150,6 +150,48 @@ q8_status q8_gemm_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
                           int64_t p, const int8_t* xq, const uint16_t* xd,
                           float* y, hipStream_t stream);
 
+/* Fragment order: a second layout of a Q8_0 matrix, the one the int8 matrix
+ * core reads.  For a matrix of `rows` rows and K columns (nb = K/32 blocks) let
+ * rows64 = rows rounded up to a multiple of 64 and nbp = nb rounded up to a
+ * multiple of 4; then
+ *   codes  int8   [rows64 / 32][nbp][64][16]: entry (t, b, l, j) is code
+ *          32b + 16 (l / 32) + j of row 32t + l % 32;
+ *   scales uint16 [rows64 / 32][nbp / 4][32][4]: entry (t, g, i, u) is the
+ *          binary16 scale of row 32t + i, block 4g + u;
+ * rows >= `rows` and blocks >= nb hold zero codes and zero scales.  Every
+ * (32-row tile, block) is one contiguous kilobyte, loaded by a wave with one
+ * 16-byte load per lane into the registers the matrix core reads.  The byte
+ * counts are those of the row-major matrix plus the padding:
+ * q8_frag_code_bytes = rows64 * nbp * 32, q8_frag_scale_bytes = rows64 * nbp * 2
+ * (-1 for an invalid K or rows; host-only, no device needed). */
+int64_t q8_frag_code_bytes(int64_t rows, int64_t k);
+int64_t q8_frag_scale_bytes(int64_t rows, int64_t k);
+
+/* Rewrite a row-major Q8_0 matrix (codes q [rows][k], scales d [rows][k/32])
+ * into fragment order (qf, df of the sizes above, padding included).  Weights
+ * are packed once, next to their row-major copy; activation rows per call,
+ * after quantization.  rows = 0 is a no-op; pointers 16-byte aligned. */
+q8_status q8_pack_frag(const int8_t* q, const uint16_t* d, int64_t rows, int64_t k,
+                       int8_t* qf, uint16_t* df, hipStream_t stream);
+
+/* The Q8 x Q8 prefill product of q8_gemm_prefill on fragment-order operands:
+ * wf / wdf the n weight rows, xf / xdf the p activation rows (both as written
+ * by q8_pack_frag with the same K), 0 <= p <= 4,194,240; y fp32 [p][n]
+ * row-major.  The same arithmetic [fak MODEL-BASELINE-RESULTS, ACT 4, "How the
+ * GEMM was closed": every block's int32 sum taken exactly (here on the int8
+ * matrix cores) and folded once into an fp32 accumulator with the product of
+ * its two scales; register-blocked output tiles], with the operands loaded
+ * straight from memory into the matrix core's registers instead of through
+ * LDS.  fp32 summation order: blocks in order within each of up to 8 contiguous
+ * K ranges, the ranges' partial sums added in order; results are bitwise
+ * reproducible for a given (n, k, p) and exact whenever every partial sum is
+ * (e.g. power-of-two scales).  A grid beyond 2^31 - 1 workgroups (a product of
+ * more than ~2^35 32 x 32 output tiles) returns Q8_ERR_SHAPE after the device
+ * check. */
+q8_status q8_gemm_prefill_frag(const int8_t* wf, const uint16_t* wdf, int64_t n, int64_t k,
+                               int64_t p, const int8_t* xf, const uint16_t* xdf,
+                               float* y, hipStream_t stream);
+
 /* The exact int32 block sums of the Q8 x Q8 product, exported so that they can
  * be compared bit for bit: isum[t][j][b] = sum_{i<32} wq[j][32b+i] * xq[t][32b+i]
  * for t < m (m = 0..8), j < n, b < k/32 [fak MODEL-BASELINE-RESULTS, ACT 3
@@ -165,14 +207,16 @@ q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m,
  * with these extents launches on the current device, so that a test can show
  * which code path a shape exercises.  op Q8_OP_SKINNY: q8_gemm_skinny with
  * m = rows and activation type act (also q8_gemv at rows = 1); Q8_OP_PREFILL:
- * q8_gemm_prefill with p = rows (act ignored); Q8_OP_Q4_SKINNY: q4_gemm_skinny.
+ * q8_gemm_prefill with p = rows (act ignored); Q8_OP_Q4_SKINNY: q4_gemm_skinny;
+ * Q8_OP_PREFILL_FRAG: q8_gemm_prefill_frag with p = rows (act ignored).
  * Writes a NUL-terminated name such as "skinny_kernel<1,0,16,2,6>" (batch,
  * activation type, lanes per group, rows per group, chunks per lane) or
- * "prefill_tile64_kernel<2>" into buf, "none" for an empty call.  Extents are
+ * "prefill_tile64_kernel<2>" or "prefill_frag_kernel<2,4>" (weight tiles per wave,
+ * waves per K split) into buf, "none" for an empty call.  Extents are
  * validated as by those calls (Q8_ERR_ENUM, Q8_ERR_SHAPE, Q8_ERR_BATCH); buf
  * NULL gives Q8_ERR_NULL, a name longer than buf_len - 1 bytes Q8_ERR_SHAPE;
  * no device gives Q8_ERR_DEVICE.  Enqueues nothing. */
-typedef enum { Q8_OP_SKINNY = 0, Q8_OP_PREFILL = 1, Q8_OP_Q4_SKINNY = 2 } q8_op;
+typedef enum { Q8_OP_SKINNY = 0, Q8_OP_PREFILL = 1, Q8_OP_Q4_SKINNY = 2, Q8_OP_PREFILL_FRAG = 3 } q8_op;
 q8_status q8_kernel_name(int op, int64_t n, int64_t k, int64_t rows, int act, char* buf, int64_t buf_len);
 
 /* Decode attention over a Q8_0 key/value cache, one query row per head and no

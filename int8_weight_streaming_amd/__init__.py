@@ -28,6 +28,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+from typing import NamedTuple
 
 import torch
 
@@ -48,8 +49,9 @@ EXPORTED = (
     "q4_quantize_weights", "q4_gemm_skinny", "q8_gemm_fused", "q8_rmsnorm", "q8_attn_decode_append",
     "q8_quantize_act_fused", "q8_attn_partial_words", "q8_attn_decode_append_partials",
     "q8_gemm_attn_residual", "q8_attn_decode_noalloc", "q8_kernel_name",
+    "q8_frag_code_bytes", "q8_frag_scale_bytes", "q8_pack_frag", "q8_gemm_prefill_frag",
 )
-OP_SKINNY, OP_PREFILL, OP_Q4_SKINNY = 0, 1, 2
+OP_SKINNY, OP_PREFILL, OP_Q4_SKINNY, OP_PREFILL_FRAG = 0, 1, 2, 3
 ATTN_SCRATCH_WORDS = 262144
 
 
@@ -103,9 +105,16 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q8_gemm_attn_residual.restype = I
     L.q8_attn_decode_append.argtypes = [P, P, P, P, P, I64, I64, I64, I64, C.c_float, P, P, P, P, I64, P]
     L.q8_attn_decode_append.restype = I
+    L.q8_frag_code_bytes.argtypes = [I64, I64]
+    L.q8_frag_code_bytes.restype = I64
+    L.q8_frag_scale_bytes.argtypes = [I64, I64]
+    L.q8_frag_scale_bytes.restype = I64
+    L.q8_pack_frag.argtypes = [P, P, I64, I64, P, P, P]
+    L.q8_gemm_prefill_frag.argtypes = [P, P, I64, I64, I64, P, P, P, P]
     for name in ("q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
                  "q8_gemm_prefill", "q8_block_dots", "q4_quantize_weights", "q4_gemm_skinny",
-                 "q8_gemm_fused", "q8_rmsnorm", "q8_quantize_act_fused"):
+                 "q8_gemm_fused", "q8_rmsnorm", "q8_quantize_act_fused", "q8_pack_frag",
+                 "q8_gemm_prefill_frag"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -278,6 +287,63 @@ def gemm_prefill(wq, wd, xq, xd, out=None):
         torch.empty((p, n), dtype=torch.float32, device=wq.device)
     _check("q8_gemm_prefill", load_library().q8_gemm_prefill(
         _ptr(wq), _ptr(wd), n, k, p, _ptr(xq), _ptr(xd), _ptr(y), _stream()))
+    return y
+
+
+class Frag(NamedTuple):
+    """A Q8_0 matrix in the matrix core's fragment order (q8_pack_frag): flat
+    codes (int8) and scales (uint16) buffers in the layout include/q8stream.h
+    states, and the row count and K of the row-major matrix it came from."""
+    q: torch.Tensor
+    d: torch.Tensor
+    rows: int
+    k: int
+
+
+def frag_bytes(rows: int, k: int) -> tuple[int, int]:
+    """Bytes of the fragment-order codes and scales of a [rows][k] matrix."""
+    L = load_library()
+    qb, db = L.q8_frag_code_bytes(rows, k), L.q8_frag_scale_bytes(rows, k)
+    if qb < 0 or db < 0:
+        raise ValueError(f"invalid extents rows={rows} k={k}")
+    return qb, db
+
+
+def pack_frag(q, d, out=None) -> Frag:
+    """Rewrite a row-major Q8_0 matrix (codes [rows][k], scales [rows][k/32])
+    into fragment order; out = (codes, scales) tensors of the right sizes."""
+    wd, rows, k = _weights(q, d)
+    qb, db = frag_bytes(rows, k)
+    if out is not None:
+        qf = _out(out[0], "out[0]", torch.int8, qb)
+        df = _out(out[1], "out[1]", torch.uint16, db // 2)
+    else:
+        qf = torch.empty((qb,), dtype=torch.int8, device=q.device)
+        df = torch.empty((db // 2,), dtype=torch.uint16, device=q.device)
+    _check("q8_pack_frag", load_library().q8_pack_frag(
+        _ptr(q), _ptr(wd), rows, k, _ptr(qf), _ptr(df), _stream()))
+    return Frag(qf, df, rows, k)
+
+
+def gemm_prefill_frag(wf: Frag, xf: Frag, out=None):
+    """y fp32 [p][n] = Q8 x Q8 product of fragment-order weights (n rows) and
+    activations (p rows), as gemm_prefill on the row-major operands."""
+    for f, name in ((wf, "wf"), (xf, "xf")):
+        if not isinstance(f, Frag):
+            raise TypeError(f"{name} must be a Frag (pack_frag)")
+        qb, db = frag_bytes(f.rows, f.k)
+        if f.q.dtype != torch.int8 or f.q.numel() != qb or not f.q.is_contiguous() or not f.q.is_cuda:
+            raise ValueError(f"{name}.q must be contiguous device int8 of {qb} bytes")
+        d = _as_bits16(f.d)
+        if d.dtype != torch.uint16 or d.numel() * 2 != db or not d.is_contiguous() or not d.is_cuda:
+            raise ValueError(f"{name}.d must be contiguous device uint16 of {db} bytes")
+    if wf.k != xf.k:
+        raise ValueError("wf and xf must have the same k")
+    n, p, k = wf.rows, xf.rows, wf.k
+    y = _out(out, "out", torch.float32, p * n) if out is not None else \
+        torch.empty((p, n), dtype=torch.float32, device=wf.q.device)
+    _check("q8_gemm_prefill_frag", load_library().q8_gemm_prefill_frag(
+        _ptr(wf.q), _ptr(_as_bits16(wf.d)), n, k, p, _ptr(xf.q), _ptr(_as_bits16(xf.d)), _ptr(y), _stream()))
     return y
 
 

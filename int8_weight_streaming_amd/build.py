@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq8stream.so")
 
 SOURCES = ["q8_api.cpp", "q8_quantize.hip", "q8_skinny.hip", "q8_skinny_mfma.hip", "q8_prefill.hip", "q8_attn.hip",
-           "q4_skinny.hip", "q8_fused.hip"]
+           "q4_skinny.hip", "q8_fused.hip", "q8_prefill_frag.hip"]
 PROBE_SOURCES = ["q8_probe.hip"]
 PROBE_LIB = os.path.join(PKG, "libq8probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

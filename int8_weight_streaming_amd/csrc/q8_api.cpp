@@ -202,6 +202,44 @@ q8_status q8_gemm_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
     return finish(q8::launch_prefill(wq, wd, n, k, p, xq, xd, y, *dev, stream));
 }
 
+int64_t q8_frag_code_bytes(int64_t rows, int64_t k) {
+    if (check_k(k) != Q8_OK || check_rows(rows, k) != Q8_OK) return -1;
+    return q8::frag_rows(rows) * q8::frag_blocks(k) * 32;
+}
+
+int64_t q8_frag_scale_bytes(int64_t rows, int64_t k) {
+    if (check_k(k) != Q8_OK || check_rows(rows, k) != Q8_OK) return -1;
+    return q8::frag_rows(rows) * q8::frag_blocks(k) * 2;
+}
+
+q8_status q8_pack_frag(const int8_t* q, const uint16_t* d, int64_t rows, int64_t k, int8_t* qf, uint16_t* df,
+                       hipStream_t stream) {
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(rows, k));
+    if (rows == 0) return Q8_OK;
+    if (!q || !d || !qf || !df) return Q8_ERR_NULL;
+    if (!aligned16(q) || !aligned16(d) || !aligned16(qf) || !aligned16(df)) return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_pack_frag(q, d, rows, k, qf, df, *dev, stream));
+}
+
+q8_status q8_gemm_prefill_frag(const int8_t* wf, const uint16_t* wdf, int64_t n, int64_t k, int64_t p,
+                               const int8_t* xf, const uint16_t* xdf, float* y, hipStream_t stream) {
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(n, k));
+    Q8_TRY(check_rows(p, k));
+    if (p > kMaxPrefillRows) return Q8_ERR_SHAPE;
+    if (n == 0 || p == 0) return Q8_OK;
+    if (!wf || !wdf || !xf || !xdf || !y) return Q8_ERR_NULL;
+    if (!aligned16(wf) || !aligned16(wdf) || !aligned16(xf) || !aligned16(xdf) || !aligned16(y))
+        return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    if (q8::prefill_frag_layout(n, p, dev->cu_count).grid > (int64_t)INT32_MAX) return Q8_ERR_SHAPE;
+    return finish(q8::launch_prefill_frag(wf, wdf, n, k, p, xf, xdf, y, *dev, stream));
+}
+
 q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m, const int8_t* xq,
                         int32_t* isum, hipStream_t stream) {
     Q8_TRY(check_k(k));
@@ -291,11 +329,13 @@ q8_status q4_gemm_skinny(const uint8_t* wq, const uint16_t* wd, int64_t n, int64
 }
 
 q8_status q8_kernel_name(int op, int64_t n, int64_t k, int64_t rows, int act, char* buf, int64_t buf_len) {
-    if (op != Q8_OP_SKINNY && op != Q8_OP_PREFILL && op != Q8_OP_Q4_SKINNY) return Q8_ERR_ENUM;
-    if (op != Q8_OP_PREFILL && act != Q8_ACT_BF16 && act != Q8_ACT_Q8) return Q8_ERR_ENUM;
+    if (op != Q8_OP_SKINNY && op != Q8_OP_PREFILL && op != Q8_OP_Q4_SKINNY && op != Q8_OP_PREFILL_FRAG)
+        return Q8_ERR_ENUM;
+    const bool prefill = op == Q8_OP_PREFILL || op == Q8_OP_PREFILL_FRAG;
+    if (!prefill && act != Q8_ACT_BF16 && act != Q8_ACT_Q8) return Q8_ERR_ENUM;
     Q8_TRY(check_k(k));
     Q8_TRY(check_rows(n, k));
-    if (op == Q8_OP_PREFILL) {
+    if (prefill) {
         Q8_TRY(check_rows(rows, k));
         if (rows > kMaxPrefillRows) return Q8_ERR_SHAPE;
     } else if (rows < 0 || rows > Q8_MAX_BATCH) {
@@ -324,6 +364,9 @@ q8_status q8_kernel_name(int op, int64_t n, int64_t k, int64_t rows, int act, ch
         const q8::Q4Layout L = q8::q4_layout(n, k, (int)rows, act, dev->cu_count);
         std::snprintf(name, sizeof name, "q4_skinny_kernel<%d,%d,%d,%d,%d,%d>", (int)rows, act, L.g, L.r, L.cpl,
                       L.xl);
+    } else if (op == Q8_OP_PREFILL_FRAG) {
+        const q8::FragLayout L = q8::prefill_frag_layout(n, rows, dev->cu_count);
+        std::snprintf(name, sizeof name, "prefill_frag_kernel<%d,%d>", L.wn, L.ks);
     } else {
         static const char* const kinds[] = {"prefill_tile64_kernel<1>", "prefill_tile64_kernel<2>",
                                             "prefill_stream_kernel", "prefill_kernel"};

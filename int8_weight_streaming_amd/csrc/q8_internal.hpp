@@ -90,6 +90,24 @@ hipError_t launch_prefill(const int8_t* wq, const uint16_t* wd, int64_t n, int64
                           const int8_t* xq, const uint16_t* xd, float* y,
                           const DeviceInfo& dev, hipStream_t stream);
 
+// The prefill product on operands in the int8 matrix core's fragment order
+// (q8_prefill_frag.hip): rows rounded up to 64 and K/32 rounded up to 4 in
+// that layout; the tile shape (wn weight tiles of 32 rows per wave), K split
+// over ks waves and grid chosen for (n, p); the packing of a row-major Q8_0
+// matrix; the product.
+int64_t frag_rows(int64_t rows);
+int64_t frag_blocks(int64_t k);
+struct FragLayout {
+    int wn, ks;
+    int64_t grid;
+};
+FragLayout prefill_frag_layout(int64_t n, int64_t p, int cu_count);
+hipError_t launch_pack_frag(const int8_t* q, const uint16_t* d, int64_t rows, int64_t k, int8_t* qf,
+                            uint16_t* df, const DeviceInfo& dev, hipStream_t stream);
+hipError_t launch_prefill_frag(const int8_t* wf, const uint16_t* wsf, int64_t n, int64_t k, int64_t p,
+                               const int8_t* xf, const uint16_t* xsf, float* y, const DeviceInfo& dev,
+                               hipStream_t stream);
+
 // Decode attention over a Q8_0 key/value cache (head dimension 128): the
 // workspace floats the chunk partials of any context up to t need (0 when one
 // chunk covers every such context).

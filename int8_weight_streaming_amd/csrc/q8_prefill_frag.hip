@@ -1,0 +1,348 @@
+// q8_prefill_frag.hip -- Q8 x Q8 prefill product on operands stored in the
+// int8 matrix core's fragment order.
+//
+//   y[t][j] = sum_b wd[j][b] * xd[t][b] * isum[t][j][b],
+//   isum[t][j][b] = sum_{i<32} wq[j][32b+i] * xq[t][32b+i]  (exact int32)
+//
+// [fak MODEL-BASELINE-RESULTS, ACT 4, "How the GEMM was closed": keep each
+// block's int32 sum and fold it once into a float accumulator; register-block
+// the output so every loaded block serves several outputs.]
+//
+// Fragment order.  One v_mfma_i32_32x32x32_i8 takes, per lane (i, h) = (lane %
+// 32, lane / 32), the 16 bytes 16h .. 16h + 15 of one 32-element block of
+// operand row i.  A Q8_0 matrix is stored so that those 64 x 16 bytes are one
+// contiguous kilobyte per 32-row tile and block:
+//
+//   codes  [rows64 / 32][nbp][64 lanes][16 B]   lane (i, h) of (tile t, block b)
+//          holds codes 32b + 16h .. + 15 of row 32t + i,
+//   scales [rows64 / 32][nbp / 4][32 rows][4]   the binary16 scales of row
+//          32t + i, blocks 4g .. 4g + 3,
+//
+// rows64 = rows rounded up to 64 and nbp = K/32 rounded up to 4; padding rows
+// and blocks hold zero codes and zero scales.  A wave then loads each operand
+// fragment with one fully coalesced 16-byte load per lane straight into the
+// registers the matrix core reads, with no LDS round trip: the row-major
+// kernels stage every operand through LDS, and at the matrix core's rate that
+// staging alone would take the whole LDS bandwidth of a compute unit.  The
+// activation side is packed per call (q8_pack_frag on the quantized rows); the
+// weights once, next to their row-major copy.
+//
+// Kernel.  A wave owns a 32 (tokens) x 32*WN (weight rows) output tile over a
+// contiguous range of K steps (four blocks each); KS waves share a tile and
+// their partial tiles are added through LDS in wave order, so results are
+// bitwise reproducible.  Per block: the int8 product (exact int32 sums), the
+// scale outer product xd (x) wd on the f16 matrix core (exact: a product of two
+// binary16 numbers needs at most 22 bits), and the fold acc += float(isum) *
+// scale on the vector ALUs.  Only one product pair is in flight and the
+// operand registers of a block are refilled with the next step's block as
+// soon as its products are issued, which keeps the kernel at <= 128 VGPRs
+// (WN = 1: four waves per SIMD) or <= 168 (WN = 2: three); the matrix core and
+// the vector ALUs of a SIMD co-issue across those waves.  Workgroups are dealt
+// to the eight XCDs (workgroup id % 8) by column ranges of the weights and walk
+// their tiles token-major, so each XCD's L2 holds its weight columns and
+// fetches every activation tile once.
+#include "q8_device.hpp"
+#include "q8_internal.hpp"
+
+#include <type_traits>
+
+namespace q8 {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ packing
+
+// One thread per 16-byte code chunk of the fragment array, then one per
+// 8-byte scale group.  Rows and blocks past the matrix are written as zeros.
+__global__ __launch_bounds__(256) void pack_frag_kernel(const int8_t* __restrict__ q,
+                                                        const uint16_t* __restrict__ d, int64_t rows,
+                                                        int nb, int nbp, int64_t tiles,
+                                                        int8_t* __restrict__ qf, uint16_t* __restrict__ df) {
+    const int64_t nchunk = tiles * nbp * 64;
+    const int64_t ngroup = tiles * (nbp / 4) * 32;
+    const int64_t k = (int64_t)nb * 32;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < nchunk + ngroup;
+         e += (int64_t)gridDim.x * 256) {
+        if (e < nchunk) {
+            const int lane = (int)(e & 63);
+            const int64_t tb = e >> 6;
+            const int b = (int)(tb % nbp);
+            const int64_t row = (tb / nbp) * 32 + (lane & 31);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row < rows && b < nb)
+                v = *reinterpret_cast<const u32x4*>(q + row * k + (int64_t)b * 32 + 16 * (lane >> 5));
+            *reinterpret_cast<u32x4*>(qf + e * 16) = v;
+        } else {
+            const int64_t g = e - nchunk;
+            const int i = (int)(g & 31);
+            const int64_t tg = g >> 5;
+            const int grp = (int)(tg % (nbp / 4));
+            const int64_t row = (tg / (nbp / 4)) * 32 + i;
+            uint16_t s[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int b = 4 * grp + u;
+                s[u] = row < rows && b < nb ? d[row * nb + b] : (uint16_t)0;
+            }
+            const uint2 w = make_uint2((uint32_t)s[0] | ((uint32_t)s[1] << 16),
+                                       (uint32_t)s[2] | ((uint32_t)s[3] << 16));
+            *reinterpret_cast<uint2*>(df + g * 4) = w;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ product
+
+template <int KS>
+constexpr int frag_waves() { return KS > 4 ? KS : 4; }
+
+template <int WN, int KS>
+__global__ __launch_bounds__(64 * frag_waves<KS>())
+__attribute__((amdgpu_waves_per_eu(WN == 1 ? 4 : 3, WN == 1 ? 4 : 3)))
+void prefill_frag_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict__ wsf, int64_t n,
+                         int nbp, int64_t p, const i32x4* __restrict__ xf, const i32x2* __restrict__ xsf,
+                         float* __restrict__ y) {
+    constexpr int W = frag_waves<KS>();
+    constexpr int T = W / KS;                        // output tiles per workgroup
+    __shared__ __attribute__((aligned(16))) float red[KS > 1 ? W * WN * 16 * 64 : 4];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int ntn = (int)((n + 31) / 32), ntp = (int)((p + 31) / 32);
+    const int ntw = (ntn + WN - 1) / WN;             // wave columns of WN weight tiles
+    const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3;
+    const int c0 = (int)((int64_t)ntw * xcd / 8), nc = (int)((int64_t)ntw * (xcd + 1) / 8) - c0;
+    const int tile = jw * T + wave / KS;
+    const bool live = nc > 0 && tile < nc * ntp;
+    const int tp = live ? tile / nc : 0;
+    const int tn0 = live ? (c0 + tile % nc) * WN : 0;
+    const int kw = wave % KS;
+    const int SS = nbp / 4;                          // four-block steps over K
+    const int s_lo = (int)((int64_t)SS * kw / KS), S = (int)((int64_t)SS * (kw + 1) / KS) - s_lo;
+    const int i = lane & 31, h = lane >> 5;
+
+    const i32x4* pa = xf + ((int64_t)tp * nbp + 4 * s_lo) * 64 + lane;
+    const i32x4* pb[WN];
+    const i32x2* psb[WN];
+#pragma unroll
+    for (int b = 0; b < WN; ++b) {
+        pb[b] = wf + ((int64_t)(tn0 + b) * nbp + 4 * s_lo) * 64 + lane;
+        psb[b] = wsf + ((int64_t)(tn0 + b) * SS + s_lo) * 32 + i;
+    }
+    const i32x2* psa = xsf + ((int64_t)tp * SS + s_lo) * 32 + i;
+
+    float acc[WN][16];
+#pragma unroll
+    for (int b = 0; b < WN; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
+
+    if (live && S > 0) {
+        const i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        const f32x16 zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        i32x4 a[4], bw[WN][4];
+        i32x2 sa, sb[WN], sa_n = {0, 0}, sb_n[WN];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            a[u] = pa[u * 64];
+#pragma unroll
+            for (int b = 0; b < WN; ++b) bw[b][u] = pb[b][u * 64];
+        }
+        sa = psa[0];
+#pragma unroll
+        for (int b = 0; b < WN; ++b) {
+            sb[b] = psb[b][0];
+            sb_n[b] = (i32x2){0, 0};
+        }
+
+        // One four-block step; with REFILL the next step's scales are fetched
+        // first and each block's operand registers are reloaded with the next
+        // step's block as soon as its products are issued.
+        auto step = [&](int s, auto refill_tag) {
+            constexpr bool REFILL = decltype(refill_tag)::value;
+            if constexpr (REFILL) {
+                sa_n = psa[(s + 1) * 32];
+#pragma unroll
+                for (int b = 0; b < WN; ++b) sb_n[b] = psb[b][(s + 1) * 32];
+            }
+            // scale operands: the activation side holds the four blocks'
+            // scales in k = 0..3 (and again in k = 8..11 on lanes 32..63), the
+            // weight side block u's scale in k = u on lanes 0..31 only, so the
+            // single nonzero product is xd_u * wd_u
+            const i32x4 sta = {sa[0], sa[1], 0, 0};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int b = 0; b < WN; ++b) {
+                    const int wb = (u >> 1) ? sb[b][1] : sb[b][0];
+                    const int half = (u & 1) ? (wb & (int)0xFFFF0000u) : (wb & 0xFFFF);
+                    const int hv = h ? 0 : half;
+                    const i32x4 stb = {(u >> 1) ? 0 : hv, (u >> 1) ? hv : 0, 0, 0};
+                    const i32x16 c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[u], bw[b][u], zi, 0, 0, 0);
+                    const f32x16 t = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(f16x8, sta), __builtin_bit_cast(f16x8, stb), zf, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (REFILL) {
+                        if (b == WN - 1) {
+                            a[u] = pa[(4 * (s + 1) + u) * 64];
+#pragma unroll
+                            for (int b2 = 0; b2 < WN; ++b2) bw[b2][u] = pb[b2][(4 * (s + 1) + u) * 64];
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[b][r] = fmaf((float)c[r], t[r], acc[b][r]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if constexpr (REFILL) {
+                sa = sa_n;
+#pragma unroll
+                for (int b = 0; b < WN; ++b) sb[b] = sb_n[b];
+            }
+        };
+        for (int s = 0; s + 1 < S; ++s) step(s, std::true_type{});
+        step(S - 1, std::false_type{});
+    }
+
+    // Result r of lane (i, h) is row 8 (r / 4) + 4 h + r % 4 of the tile and
+    // column i of weight tile tn0 + b.  A quad q holds results 4q .. 4q + 3
+    // (rows 8q + 4h .. + 3).  Whole tiles store unguarded through one base
+    // pointer per lane; ragged ones check rows and columns.
+    const int64_t prow0 = (int64_t)tp * 32 + 4 * h;
+    const bool full = (int64_t)(tp + 1) * 32 <= p && (int64_t)(tn0 + WN) * 32 <= n;
+    float* const ybase = y + prow0 * n + (int64_t)tn0 * 32 + i;
+    auto store_quad = [&](int b, int q, const float4& v) {
+        float* yq = ybase + (int64_t)(8 * q) * n + 32 * b;
+        if (full) {
+            yq[0] = v.x;
+            yq[n] = v.y;
+            yq[2 * n] = v.z;
+            yq[3 * n] = v.w;
+        } else {
+            const int64_t row = prow0 + 8 * q, col = (int64_t)(tn0 + b) * 32 + i;
+            if (col < n) {
+                if (row < p) yq[0] = v.x;
+                if (row + 1 < p) yq[n] = v.y;
+                if (row + 2 < p) yq[2 * n] = v.z;
+                if (row + 3 < p) yq[3 * n] = v.w;
+            }
+        }
+    };
+    if constexpr (KS > 1) {
+        // every wave leaves its partial tile in LDS as 16-byte records
+        // [wave][b][q][lane]; the (b, q) items are dealt over the KS waves of
+        // the tile, and each sums its items' KS partials in wave order
+        float4* red4 = reinterpret_cast<float4*>(red);
+#pragma unroll
+        for (int b = 0; b < WN; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                red4[((wave * WN + b) * 4 + q) * 64 + lane] =
+                    make_float4(acc[b][4 * q], acc[b][4 * q + 1], acc[b][4 * q + 2], acc[b][4 * q + 3]);
+        __syncthreads();
+        if (live) {
+            const int w0 = wave - kw;                      // first wave of this tile
+            for (int item = kw; item < 4 * WN; item += KS) {
+                const int b = item >> 2, q = item & 3;
+                float4 v = red4[((w0 * WN + b) * 4 + q) * 64 + lane];
+                for (int w = 1; w < KS; ++w) {
+                    const float4 u = red4[(((w0 + w) * WN + b) * 4 + q) * 64 + lane];
+                    v.x += u.x;
+                    v.y += u.y;
+                    v.z += u.z;
+                    v.w += u.w;
+                }
+                store_quad(b, q, v);
+            }
+        }
+    } else if (live) {
+#pragma unroll
+        for (int b = 0; b < WN; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                store_quad(b, q, make_float4(acc[b][4 * q], acc[b][4 * q + 1], acc[b][4 * q + 2], acc[b][4 * q + 3]));
+    }
+}
+
+template <int WN, int KS>
+hipError_t launch_frag_cfg(const int8_t* wf, const uint16_t* wsf, int64_t n, int64_t k, int64_t p,
+                           const int8_t* xf, const uint16_t* xsf, float* y, int64_t grid, hipStream_t stream) {
+    constexpr int W = frag_waves<KS>();
+    const int nbp = (int)frag_blocks(k);
+    prefill_frag_kernel<WN, KS><<<(unsigned)grid, 64 * W, 0, stream>>>(
+        reinterpret_cast<const i32x4*>(wf), reinterpret_cast<const i32x2*>(wsf), n, nbp, p,
+        reinterpret_cast<const i32x4*>(xf), reinterpret_cast<const i32x2*>(xsf), y);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t frag_rows(int64_t rows) { return (rows + 63) / 64 * 64; }
+int64_t frag_blocks(int64_t k) { return (k / 32 + 3) / 4 * 4; }
+
+// Tile shape and K split, from a sweep of the Mimir shapes at P = 256, 1024
+// and 4096 (graph replay): two weight tiles per wave once that still leaves
+// two wave columns per compute unit, then the smallest split of K over 1, 2, 4
+// or 8 waves that puts at least eight waves of work on every compute unit.
+FragLayout prefill_frag_layout(int64_t n, int64_t p, int cu_count) {
+    const int64_t ntn = (n + 31) / 32, ntp = (p + 31) / 32;
+    const int wn = (ntn + 1) / 2 * ntp >= 2 * (int64_t)cu_count ? 2 : 1;
+    const int64_t tiles = (ntn + wn - 1) / wn * ntp;
+    int ks = 8;
+    for (int c : {1, 2, 4})
+        if (tiles * c >= 8 * (int64_t)cu_count) {
+            ks = c;
+            break;
+        }
+    const int waves = ks > 4 ? ks : 4;
+    const int per_wg = waves / ks;
+    const int64_t ntw = (ntn + wn - 1) / wn;
+    int64_t maxwg = 0;
+    for (int x = 0; x < 8; ++x) {
+        const int64_t nc = ntw * (x + 1) / 8 - ntw * x / 8;
+        const int64_t wgs = (nc * ntp + per_wg - 1) / per_wg;
+        maxwg = wgs > maxwg ? wgs : maxwg;
+    }
+    return FragLayout{wn, ks, 8 * maxwg};
+}
+
+hipError_t launch_pack_frag(const int8_t* q, const uint16_t* d, int64_t rows, int64_t k, int8_t* qf,
+                            uint16_t* df, const DeviceInfo& dev, hipStream_t stream) {
+    (void)hipGetLastError();
+    const int nb = (int)(k / 32), nbp = (int)frag_blocks(k);
+    const int64_t tiles = frag_rows(rows) / 32;
+    const int64_t work = tiles * nbp * 64 + tiles * (nbp / 4) * 32;
+    int64_t grid = (work + 255) / 256;
+    const int64_t cap = (int64_t)dev.cu_count * 16;
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    pack_frag_kernel<<<(unsigned)grid, 256, 0, stream>>>(q, d, rows, nb, nbp, tiles, qf, df);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_frag(const int8_t* wf, const uint16_t* wsf, int64_t n, int64_t k, int64_t p,
+                               const int8_t* xf, const uint16_t* xsf, float* y, const DeviceInfo& dev,
+                               hipStream_t stream) {
+    (void)hipGetLastError();
+    const FragLayout L = prefill_frag_layout(n, p, dev.cu_count);
+    if (L.wn == 2) {
+        switch (L.ks) {
+            case 1: return launch_frag_cfg<2, 1>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
+            case 2: return launch_frag_cfg<2, 2>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
+            case 4: return launch_frag_cfg<2, 4>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
+            default: return launch_frag_cfg<2, 8>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
+        }
+    }
+    switch (L.ks) {
+        case 1: return launch_frag_cfg<1, 1>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
+        case 2: return launch_frag_cfg<1, 2>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
+        case 4: return launch_frag_cfg<1, 4>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
+        default: return launch_frag_cfg<1, 8>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
+    }
+}
+
+}  // namespace q8

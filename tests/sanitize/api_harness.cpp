@@ -106,6 +106,20 @@ hipError_t launch_skinny_mfma(const int8_t*, const uint16_t*, int64_t n, int64_t
 Q4Layout q4_layout(int64_t, int64_t, int, int, int) { return {16, 2, 3, 0}; }
 bool q4_mfma_applies(int64_t, int64_t k, int m, int) { return m >= 5 && k % 512 == 0; }
 SkinnyLayout q4_mfma_layout(int64_t, int64_t, int) { return {16, 1, 4, true}; }
+int64_t frag_rows(int64_t rows) { return (rows + 63) / 64 * 64; }
+int64_t frag_blocks(int64_t k) { return (k / 32 + 3) / 4 * 4; }
+FragLayout prefill_frag_layout(int64_t n, int64_t p, int) {
+    const int64_t tiles = ((n + 31) / 32) * ((p + 31) / 32);
+    return FragLayout{1, 4, (tiles + 7) / 8 * 8};
+}
+hipError_t launch_pack_frag(const int8_t*, const uint16_t*, int64_t rows, int64_t k, int8_t*, uint16_t*,
+                            const DeviceInfo&, hipStream_t) {
+    return rec(0, k, rows);
+}
+hipError_t launch_prefill_frag(const int8_t*, const uint16_t*, int64_t n, int64_t k, int64_t p, const int8_t*,
+                               const uint16_t*, float*, const DeviceInfo&, hipStream_t) {
+    return rec(n, k, p);
+}
 // attention sizes: 64-row chunks up to 512 rows, 128 up to 2048, 256 above
 static int64_t chunk_rows(int64_t t) { return t <= 512 ? 64 : t <= 2048 ? 128 : 256; }
 int64_t attn_split_chunks(int64_t t) { return (t + chunk_rows(t) - 1) / chunk_rows(t); }
@@ -197,6 +211,19 @@ int main() {
     call([&] { return q8_gemm_prefill(i8(A), u16(B), 10, 64, 65535LL * 64 + 1, i8(A), u16(B), f32(A), nullptr); },
          Q8_ERR_SHAPE, false);
     call([&] { return q8_block_dots(i8(A), 7, 96, 3, i8(A), static_cast<int32_t*>(B), nullptr); }, Q8_OK, true);
+    EXPECT(q8_frag_code_bytes(65, 96) == 128 * 4 * 32 && q8_frag_scale_bytes(65, 96) == 128 * 4 * 2);
+    EXPECT(q8_frag_code_bytes(65, 95) == -1 && q8_frag_scale_bytes(-1, 96) == -1);
+    call([&] { return q8_pack_frag(i8(A), u16(B), 65, 96, i8(A), u16(B), nullptr); }, Q8_OK, true);
+    EXPECT(g_last_rows == 65 && g_last_k == 96);
+    call([&] { return q8_pack_frag(i8(A), u16(MIS), 65, 96, i8(A), u16(B), nullptr); }, Q8_ERR_ALIGN, false);
+    call([&] { return q8_pack_frag(nullptr, nullptr, 0, 96, nullptr, nullptr, nullptr); }, Q8_OK, false);
+    call([&] { return q8_gemm_prefill_frag(i8(A), u16(B), 4608, 1536, 256, i8(A), u16(B), f32(A), nullptr); },
+         Q8_OK, true);
+    EXPECT(g_last_n == 4608 && g_last_rows == 256);
+    call([&] { return q8_gemm_prefill_frag(i8(A), u16(B), (int64_t)1 << 30, 32, 65535LL * 64, i8(A), u16(B), f32(A),
+                                           nullptr); }, Q8_ERR_SHAPE, false);   // grid beyond 2^31 - 1
+    call([&] { return q8_gemm_prefill_frag(i8(A), nullptr, 46, 64, 3, i8(A), u16(B), f32(A), nullptr); },
+         Q8_ERR_NULL, false);
     call([&] { return q8_gemm_fused(i8(A), u16(B), 10, 64, 1, 0, A, 0, A, 0, 0, nullptr); }, Q8_ERR_ENUM, false);
     call([&] { return q8_gemm_fused(i8(A), u16(B), 11, 64, 1, 2, A, 3, A, 0, 0, nullptr); }, Q8_ERR_SHAPE, false);
     call([&] { return q8_gemm_fused(i8(A), u16(B), 256, 128, 1, 2, A, 3, A, 128, 7, nullptr); }, Q8_OK, true);
@@ -239,6 +266,8 @@ int main() {
     EXPECT(std::strcmp(name, "skinny_kernel<8,1,16,2,6>") == 0);
     call([&] { return q8_kernel_name(Q8_OP_PREFILL, 4608, 1536, 256, 9, name, sizeof name); }, Q8_OK, false);
     EXPECT(std::strcmp(name, "prefill_stream_kernel") == 0);
+    call([&] { return q8_kernel_name(Q8_OP_PREFILL_FRAG, 4608, 1536, 256, 0, name, sizeof name); }, Q8_OK, false);
+    EXPECT(std::strcmp(name, "prefill_frag_kernel<1,4>") == 0);
     call([&] { return q8_kernel_name(Q8_OP_SKINNY, 262144, 1536, 1, 0, name, 5); }, Q8_ERR_SHAPE, false);
 
     // without a device, valid calls are refused before any launch

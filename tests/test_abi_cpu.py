@@ -121,6 +121,42 @@ def test_prefill_and_block_dots_validation(lib):
     assert g(None, 0, 64, 1, None, None, None) == OK
 
 
+def test_frag_sizes_and_validation(lib):
+    """Fragment order: rows rounded up to 64, K/32 blocks rounded up to 4; 32
+    code bytes and 2 scale bytes per (row, block) of the padded matrix."""
+    cb, sb = lib.q8_frag_code_bytes, lib.q8_frag_scale_bytes
+    assert (cb(256, 1536), sb(256, 1536)) == (256 * 48 * 32, 256 * 48 * 2)
+    assert (cb(1, 32), sb(1, 32)) == (64 * 4 * 32, 64 * 4 * 2)
+    assert (cb(65, 96), sb(65, 96)) == (128 * 4 * 32, 128 * 4 * 2)
+    assert (cb(4608, 4128), sb(4608, 4128)) == (4608 * 132 * 32, 4608 * 132 * 2)
+    assert (cb(0, 64), sb(0, 64)) == (0, 0)
+    for rows, k in ((4, 48), (4, 0), (-1, 64), (1 << 31, 64)):
+        assert cb(rows, k) == -1 and sb(rows, k) == -1
+    f = lib.q8_pack_frag
+    assert f(A, B, 4, 48, A, B, None) == SHAPE
+    assert f(A, B, -1, 64, A, B, None) == SHAPE
+    assert f(None, B, 4, 64, A, B, None) == NULL
+    assert f(A, B, 4, 64, A, None, None) == NULL
+    assert f(A, B, 4, 64, MIS, B, None) == ALIGN
+    assert f(A, MIS, 4, 64, A, B, None) == ALIGN
+    assert f(None, None, 0, 64, None, None, None) == OK
+    g = lib.q8_gemm_prefill_frag
+    assert g(A, B, 8, 48, 4, A, B, A, None) == SHAPE
+    assert g(A, B, 8, 64, 65535 * 64 + 1, A, B, A, None) == SHAPE
+    assert g(A, B, -8, 64, 4, A, B, A, None) == SHAPE
+    assert g(A, B, 8, 64, 4, None, B, A, None) == NULL
+    assert g(A, None, 8, 64, 4, A, B, A, None) == NULL
+    assert g(A, B, 8, 64, 4, A, B, None, None) == NULL
+    assert g(A, B, 8, 64, 4, A, MIS, A, None) == ALIGN
+    assert g(A, B, 8, 64, 4, A, B, MIS, None) == ALIGN
+    assert g(None, None, 8, 64, 0, None, None, None, None) == OK
+    assert g(None, None, 0, 64, 9, None, None, None, None) == OK
+    import torch
+    if not torch.cuda.is_available():
+        assert f(A, B, 4, 64, A, B, None) == DEVICE
+        assert g(A, B, 8, 64, 4, A, B, A, None) == DEVICE
+
+
 def test_q4_validation(lib):
     f = lib.q4_quantize_weights
     assert f(A, 4, 48, A, B, None) == SHAPE
@@ -329,7 +365,8 @@ def test_kernel_name_validation(lib):
     import ctypes
     buf = ctypes.create_string_buffer(96)
     p = ctypes.cast(buf, ctypes.c_void_p)
-    assert f(3, 8, 64, 1, 0, p, 96) == ENUM                  # unknown op
+    assert f(4, 8, 64, 1, 0, p, 96) == ENUM                  # unknown op
+    assert f(-1, 8, 64, 1, 0, p, 96) == ENUM
     assert f(0, 8, 64, 1, 2, p, 96) == ENUM                  # unknown activation type
     assert f(0, 8, 48, 1, 0, p, 96) == SHAPE
     assert f(0, 8, 64, 9, 0, p, 96) == BATCH
@@ -342,3 +379,5 @@ def test_kernel_name_validation(lib):
     if not torch.cuda.is_available():
         assert f(0, 8, 64, 1, 0, p, 96) == DEVICE
         assert f(1, 8, 64, 5, 7, p, 96) == DEVICE            # act is ignored for prefill
+        assert f(3, 8, 64, 5, 7, p, 96) == DEVICE            # and for the fragment-order prefill
+    assert f(3, 8, 64, 65535 * 64 + 1, 0, p, 96) == SHAPE
