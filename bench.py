@@ -881,7 +881,8 @@ def main() -> int:
                     help="time only the headline GEMV (no other workloads, no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
-                    help="run only the prefill products (for hardware-counter passes)")
+                    help="run only the prefill products and the 1 GiB copy that scales byte "
+                         "counters (for hardware-counter passes)")
     ap.add_argument("--prefill-p", type=int, nargs="*", default=[256],
                     help="P values of --prefill-only")
     ap.add_argument("--lm-head-only", action="store_true",
@@ -922,7 +923,7 @@ def main() -> int:
                 weights[(0, proj)] = quantize_on_device(
                     q8, wl.normal_weights(wl.mimir_weight_seed(0, proj), n_, k_), dev)
         res = bench_prefill(q8, wl, dev, weights, sweep=tuple(args.prefill_p))
-        print(json.dumps({"prefill": res}), flush=True)
+        print(json.dumps({"prefill": res, "copy_probe": bench_copy_probe(dev)}), flush=True)
         return 0
 
     if args.lm_head_only:
