@@ -176,7 +176,7 @@ q8_status q8_pack_frag(const int8_t* q, const uint16_t* d, int64_t rows, int64_t
 
 /* The Q8 x Q8 prefill product of q8_gemm_prefill on fragment-order operands:
  * wf / wdf the n weight rows, xf / xdf the p activation rows (both as written
- * by q8_pack_frag with the same K), 0 <= p <= 4,194,240; y fp32 [p][n]
+ * by q8_pack_frag with the same K), 0 <= p <= 4,194,240, K <= 2^25; y fp32 [p][n]
  * row-major.  The same arithmetic [fak MODEL-BASELINE-RESULTS, ACT 4, "How the
  * GEMM was closed": every block's int32 sum taken exactly (here on the int8
  * matrix cores) and folded once into an fp32 accumulator with the product of

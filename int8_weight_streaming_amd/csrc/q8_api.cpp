@@ -28,6 +28,7 @@ q8::DeviceInfo g_dev_info[kMaxDevices];
 constexpr int64_t kMaxExtent = (int64_t)1 << 31;   // per-dimension limit
 constexpr int64_t kMaxElems = (int64_t)1 << 46;    // n * k limit (64 TiB of codes)
 constexpr int64_t kMaxPrefillRows = (int64_t)65535 * 64;
+constexpr int64_t kMaxFragK = (int64_t)1 << 25;            // a tile's K range fits 32-bit buffer offsets
 constexpr int64_t kMaxAttnHeads = (int64_t)1 << 16;
 constexpr int64_t kMaxAttnRows = ((int64_t)1 << 24) - 128;   // cache rows per head
 
@@ -229,7 +230,7 @@ q8_status q8_gemm_prefill_frag(const int8_t* wf, const uint16_t* wdf, int64_t n,
     Q8_TRY(check_k(k));
     Q8_TRY(check_rows(n, k));
     Q8_TRY(check_rows(p, k));
-    if (p > kMaxPrefillRows) return Q8_ERR_SHAPE;
+    if (p > kMaxPrefillRows || k > kMaxFragK) return Q8_ERR_SHAPE;
     if (n == 0 || p == 0) return Q8_OK;
     if (!wf || !wdf || !xf || !xdf || !y) return Q8_ERR_NULL;
     if (!aligned16(wf) || !aligned16(wdf) || !aligned16(xf) || !aligned16(xdf) || !aligned16(y))

@@ -124,16 +124,6 @@ void prefill_frag_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict__
     const int s_lo = (int)((int64_t)SS * kw / KS), S = (int)((int64_t)SS * (kw + 1) / KS) - s_lo;
     const int i = lane & 31, h = lane >> 5;
 
-    const i32x4* pa = xf + ((int64_t)tp * nbp + 4 * s_lo) * 64 + lane;
-    const i32x4* pb[WN];
-    const i32x2* psb[WN];
-#pragma unroll
-    for (int b = 0; b < WN; ++b) {
-        pb[b] = wf + ((int64_t)(tn0 + b) * nbp + 4 * s_lo) * 64 + lane;
-        psb[b] = wsf + ((int64_t)(tn0 + b) * SS + s_lo) * 32 + i;
-    }
-    const i32x2* psa = xsf + ((int64_t)tp * SS + s_lo) * 32 + i;
-
     float acc[WN][16];
 #pragma unroll
     for (int b = 0; b < WN; ++b)
@@ -141,20 +131,43 @@ void prefill_frag_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict__
         for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
 
     if (live && S > 0) {
+        // Buffer descriptors over this wave's tiles (all of K); a block is
+        // addressed by the scalar offset of its kilobyte, a step's scales by
+        // the scalar offset of their 256 bytes, so load addresses cost no
+        // vector instructions.
+        const char* xb = reinterpret_cast<const char*>(xf);
+        const char* wb = reinterpret_cast<const char*>(wf);
+        const char* xsb = reinterpret_cast<const char*>(xsf);
+        const char* wsb = reinterpret_cast<const char*>(wsf);
+        const __amdgpu_buffer_rsrc_t ra = range_rsrc32(xb + (int64_t)tp * nbp * 1024, nbp * 1024);
+        const __amdgpu_buffer_rsrc_t rsa = range_rsrc32(xsb + (int64_t)tp * SS * 256, SS * 256);
+        __amdgpu_buffer_rsrc_t rb[WN], rsb[WN];
+#pragma unroll
+        for (int b = 0; b < WN; ++b) {
+            rb[b] = range_rsrc32(wb + (int64_t)(tn0 + b) * nbp * 1024, nbp * 1024);
+            rsb[b] = range_rsrc32(wsb + (int64_t)(tn0 + b) * SS * 256, SS * 256);
+        }
+        const int vo = lane * 16, vs = i * 8;
+        auto ld_code = [&](__amdgpu_buffer_rsrc_t r, int blk) {
+            return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, blk * 1024, 0));
+        };
+        auto ld_scale = [&](__amdgpu_buffer_rsrc_t r, int st) {
+            return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, vs, st * 256, 0));
+        };
         const i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
         const f32x16 zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         i32x4 a[4], bw[WN][4];
         i32x2 sa, sb[WN], sa_n = {0, 0}, sb_n[WN];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            a[u] = pa[u * 64];
+            a[u] = ld_code(ra, 4 * s_lo + u);
 #pragma unroll
-            for (int b = 0; b < WN; ++b) bw[b][u] = pb[b][u * 64];
+            for (int b = 0; b < WN; ++b) bw[b][u] = ld_code(rb[b], 4 * s_lo + u);
         }
-        sa = psa[0];
+        sa = ld_scale(rsa, s_lo);
 #pragma unroll
         for (int b = 0; b < WN; ++b) {
-            sb[b] = psb[b][0];
+            sb[b] = ld_scale(rsb[b], s_lo);
             sb_n[b] = (i32x2){0, 0};
         }
 
@@ -163,33 +176,37 @@ void prefill_frag_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict__
         // step's block as soon as its products are issued.
         auto step = [&](int s, auto refill_tag) {
             constexpr bool REFILL = decltype(refill_tag)::value;
+            const int gs = s_lo + s;
             if constexpr (REFILL) {
-                sa_n = psa[(s + 1) * 32];
+                sa_n = ld_scale(rsa, gs + 1);
 #pragma unroll
-                for (int b = 0; b < WN; ++b) sb_n[b] = psb[b][(s + 1) * 32];
+                for (int b = 0; b < WN; ++b) sb_n[b] = ld_scale(rsb[b], gs + 1);
             }
-            // scale operands: the activation side holds the four blocks'
-            // scales in k = 0..3 (and again in k = 8..11 on lanes 32..63), the
-            // weight side block u's scale in k = u on lanes 0..31 only, so the
-            // single nonzero product is xd_u * wd_u
-            const i32x4 sta = {sa[0], sa[1], 0, 0};
+            // Scale operands: the weight side holds its four blocks' scales in
+            // k = 0..3 (lanes 32..63, k = 8..11, meet zeros); the activation
+            // side block u's scale in k = u on lanes 0..31 only, built once per
+            // block for all WN weight tiles; the single nonzero product is
+            // xd_u * wd_u.
+            i32x4 stb[WN];
+#pragma unroll
+            for (int b = 0; b < WN; ++b) stb[b] = (i32x4){sb[b][0], sb[b][1], 0, 0};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
+                const int xw = (u >> 1) ? sa[1] : sa[0];
+                const int half = (u & 1) ? (xw & (int)0xFFFF0000u) : (xw & 0xFFFF);
+                const int hv = h ? 0 : half;
+                const i32x4 sta = {(u >> 1) ? 0 : hv, (u >> 1) ? hv : 0, 0, 0};
 #pragma unroll
                 for (int b = 0; b < WN; ++b) {
-                    const int wb = (u >> 1) ? sb[b][1] : sb[b][0];
-                    const int half = (u & 1) ? (wb & (int)0xFFFF0000u) : (wb & 0xFFFF);
-                    const int hv = h ? 0 : half;
-                    const i32x4 stb = {(u >> 1) ? 0 : hv, (u >> 1) ? hv : 0, 0, 0};
                     const i32x16 c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[u], bw[b][u], zi, 0, 0, 0);
                     const f32x16 t = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        __builtin_bit_cast(f16x8, sta), __builtin_bit_cast(f16x8, stb), zf, 0, 0, 0);
+                        __builtin_bit_cast(f16x8, sta), __builtin_bit_cast(f16x8, stb[b]), zf, 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                     if constexpr (REFILL) {
                         if (b == WN - 1) {
-                            a[u] = pa[(4 * (s + 1) + u) * 64];
+                            a[u] = ld_code(ra, 4 * (gs + 1) + u);
 #pragma unroll
-                            for (int b2 = 0; b2 < WN; ++b2) bw[b2][u] = pb[b2][(4 * (s + 1) + u) * 64];
+                            for (int b2 = 0; b2 < WN; ++b2) bw[b2][u] = ld_code(rb[b2], 4 * (gs + 1) + u);
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);

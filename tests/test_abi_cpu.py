@@ -144,6 +144,7 @@ def test_frag_sizes_and_validation(lib):
     assert g(A, B, 8, 48, 4, A, B, A, None) == SHAPE
     assert g(A, B, 8, 64, 65535 * 64 + 1, A, B, A, None) == SHAPE
     assert g(A, B, -8, 64, 4, A, B, A, None) == SHAPE
+    assert g(A, B, 8, (1 << 25) + 32, 4, A, B, A, None) == SHAPE      # K beyond 32-bit tile offsets
     assert g(A, B, 8, 64, 4, None, B, A, None) == NULL
     assert g(A, None, 8, 64, 4, A, B, A, None) == NULL
     assert g(A, B, 8, 64, 4, A, B, None, None) == NULL
