@@ -588,8 +588,8 @@ def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP, int8_peak_measured=
     P = 256 is the configured workload (activations with the seeded special
     rows); the sweep over P also fits time = fixed + P * slope for the three
     products, the pages' prefill measure, and for the products with their
-    activation side (RMSNorm + quantizer fused for qkv and gate_up, the plain
-    quantizer for down, then the fragment packing of each activation matrix)."""
+    activation side (RMSNorm + quantizer in one launch for qkv and gate_up, the
+    quantizer alone for down, each writing fragment order)."""
     import torch
     cfg = wl.CONFIGS["prefill_p256"]
     gemms = []
@@ -631,10 +631,17 @@ def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP, int8_peak_measured=
             q_us[kk] = graph_us(lambda: q8.quantize_act(x_, out=(q, d)), 20)["median"]
             pack_us[kk] = graph_us(lambda: q8.pack_frag(q, d, out=(xf.q, xf.d)), 20)["median"]
         # the activation side of qkv / gate_up: RMSNorm of the fp32 residual
-        # rows, bf16, Q8_0 -- one fused launch, or norm then quantize
+        # rows, bf16, Q8_0 -- one fused launch (row-major, or straight into
+        # fragment order), or norm then quantize; of down: its bf16 input rows
+        # (here the seeded [P][4096] activations as fp32) into fragment order
         h_ = to_dev(wl.bf16_bits_to_f32(xa), dev)
-        _, hq, hd, _ = xs[wl.HIDDEN]
+        _, hq, hd, hf = xs[wl.HIDDEN]
         fused_us = graph_us(lambda: q8.quantize_act_fused(h_, q8.PRO_RMSNORM, out=(hq, hd)), 20)["median"]
+        fused_frag_us = graph_us(lambda: q8.quantize_act_fused_frag(h_, q8.PRO_RMSNORM, out=(hf.q, hf.d)),
+                                 20)["median"]
+        s_ = to_dev(wl.bf16_bits_to_f32(xb), dev)
+        sf = xs[wl.INTER][3]
+        down_frag_us = graph_us(lambda: q8.quantize_act_fused_frag(s_, q8.PRO_F32, out=(sf.q, sf.d)), 20)["median"]
         nrm = torch.empty_like(h_)
         chain_us = graph_us(lambda: (q8.rmsnorm(h_, out=nrm),
                                      q8.quantize_act_fused(nrm, q8.PRO_F32, out=(hq, hd))), 20)["median"]
@@ -648,8 +655,9 @@ def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP, int8_peak_measured=
                                   "frac_int8_peak": tops_rm / INT8_PEAK_TOPS, "per_gemm": rows_rm},
                     "quantize_act_us": sum(q_us.values()), "pack_frag_act_us": sum(pack_us.values()),
                     "rmsnorm_quantize_fused_us": fused_us, "rmsnorm_then_quantize_us": chain_us,
-                    "us_products_with_activation_side": tot_us + 2 * fused_us + q_us[wl.INTER]
-                    + 2 * pack_us[wl.HIDDEN] + pack_us[wl.INTER]}
+                    "rmsnorm_quantize_fused_frag_us": fused_frag_us, "quantize_frag_4096_us": down_frag_us,
+                    "us_products_with_activation_side": tot_us + 2 * fused_frag_us + down_frag_us,
+                    "row_major_us_products_with_activation_side": tot_rm + 2 * fused_us + q_us[wl.INTER]}
         log(f"prefill P={P}: {tot_us:.1f} us, {tops:.0f} TOPS ({100 * tops / INT8_PEAK_TOPS:.1f}% of int8 peak); "
             + ", ".join(f"{nm} {r['us']['median']:.1f} us ({r['kernel']})" for nm, r in rows.items())
             + f"; row-major {tot_rm:.1f} us ({100 * tops_rm / INT8_PEAK_TOPS:.1f}%)")

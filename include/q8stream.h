@@ -371,6 +371,15 @@ q8_status q8_rmsnorm(const float* x, int64_t m, int64_t k, float* y, hipStream_t
 q8_status q8_quantize_act_fused(const float* x, int64_t m, int64_t k, int prologue, int8_t* xq,
                                 uint16_t* xd, hipStream_t stream);
 
+/* q8_quantize_act_fused writing fragment order: the same codes and scales, in
+ * the layout of q8_pack_frag (xqf of q8_frag_code_bytes(m, k) bytes, xdf of
+ * q8_frag_scale_bytes(m, k)), padding rows and blocks written as zeros, so the
+ * activation side of q8_gemm_prefill_frag is one launch.  Bit-identical to
+ * q8_quantize_act_fused followed by q8_pack_frag.  0 <= m <= 4,194,240;
+ * otherwise as q8_quantize_act_fused. */
+q8_status q8_quantize_act_fused_frag(const float* x, int64_t m, int64_t k, int prologue, int8_t* xqf,
+                                     uint16_t* xdf, hipStream_t stream);
+
 /* ---- int4 weights ----------------------------------------------------------
  *
  * The pages price and measure an "int4 core + int8 vocab" build (Frigg README:

@@ -50,6 +50,7 @@ EXPORTED = (
     "q8_quantize_act_fused", "q8_attn_partial_words", "q8_attn_decode_append_partials",
     "q8_gemm_attn_residual", "q8_attn_decode_noalloc", "q8_kernel_name",
     "q8_frag_code_bytes", "q8_frag_scale_bytes", "q8_pack_frag", "q8_gemm_prefill_frag",
+    "q8_quantize_act_fused_frag",
 )
 OP_SKINNY, OP_PREFILL, OP_Q4_SKINNY, OP_PREFILL_FRAG = 0, 1, 2, 3
 ATTN_SCRATCH_WORDS = 262144
@@ -111,10 +112,11 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.q8_frag_scale_bytes.restype = I64
     L.q8_pack_frag.argtypes = [P, P, I64, I64, P, P, P]
     L.q8_gemm_prefill_frag.argtypes = [P, P, I64, I64, I64, P, P, P, P]
+    L.q8_quantize_act_fused_frag.argtypes = [P, I64, I64, I, P, P, P]
     for name in ("q8_quantize_weights", "q8_quantize_act", "q8_gemv", "q8_gemm_skinny",
                  "q8_gemm_prefill", "q8_block_dots", "q4_quantize_weights", "q4_gemm_skinny",
                  "q8_gemm_fused", "q8_rmsnorm", "q8_quantize_act_fused", "q8_pack_frag",
-                 "q8_gemm_prefill_frag"):
+                 "q8_gemm_prefill_frag", "q8_quantize_act_fused_frag"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -323,6 +325,23 @@ def pack_frag(q, d, out=None) -> Frag:
     _check("q8_pack_frag", load_library().q8_pack_frag(
         _ptr(q), _ptr(wd), rows, k, _ptr(qf), _ptr(df), _stream()))
     return Frag(qf, df, rows, k)
+
+
+def quantize_act_fused_frag(x, prologue, out=None) -> Frag:
+    """fp32 rows [m][k] -> (PRO_F32: bf16 | PRO_RMSNORM: RMSNorm, bf16) -> Q8_0
+    in fragment order, one launch; out = (codes, scales) of the frag sizes."""
+    _need(x, "x", torch.float32, 2)
+    m, k = x.shape
+    qb, db = frag_bytes(m, k)
+    if out is not None:
+        qf = _out(out[0], "out[0]", torch.int8, qb)
+        df = _out(out[1], "out[1]", torch.uint16, db // 2)
+    else:
+        qf = torch.empty((qb,), dtype=torch.int8, device=x.device)
+        df = torch.empty((db // 2,), dtype=torch.uint16, device=x.device)
+    _check("q8_quantize_act_fused_frag", load_library().q8_quantize_act_fused_frag(
+        _ptr(x), m, k, prologue, _ptr(qf), _ptr(df), _stream()))
+    return Frag(qf, df, m, k)
 
 
 def gemm_prefill_frag(wf: Frag, xf: Frag, out=None):

@@ -300,6 +300,20 @@ q8_status q8_quantize_act_fused(const float* x, int64_t m, int64_t k, int prolog
     return finish(q8::launch_act_prologue_quantize(x, m, k, prologue, xq, xd, stream));
 }
 
+q8_status q8_quantize_act_fused_frag(const float* x, int64_t m, int64_t k, int prologue, int8_t* xqf,
+                                     uint16_t* xdf, hipStream_t stream) {
+    if (prologue != Q8_PRO_F32 && prologue != Q8_PRO_RMSNORM) return Q8_ERR_ENUM;
+    Q8_TRY(check_k(k));
+    Q8_TRY(check_rows(m, k));
+    if (m > kMaxPrefillRows) return Q8_ERR_SHAPE;
+    if (m == 0) return Q8_OK;
+    if (!x || !xqf || !xdf) return Q8_ERR_NULL;
+    if (!aligned16(x) || !aligned16(xqf) || !aligned16(xdf)) return Q8_ERR_ALIGN;
+    const q8::DeviceInfo* dev = nullptr;
+    Q8_TRY(device_for(stream, &dev));
+    return finish(q8::launch_act_prologue_quantize_frag(x, m, k, prologue, xqf, xdf, stream));
+}
+
 q8_status q4_quantize_weights(const float* w, int64_t n, int64_t k, uint8_t* wq, uint16_t* wd,
                               hipStream_t stream) {
     Q8_TRY(check_k(k));

@@ -138,11 +138,30 @@ hipError_t launch_rmsnorm(const float* x, int64_t m, int64_t k, float* y, hipStr
 // eight-value groups t, t + 256, ... of the row, so a 32-value block is four
 // consecutive threads and its maximum is combined over the quad.  A row of
 // k <= 2048 is read once (the norm's registers are the values quantized).
-template <int PRO>
-__global__ __launch_bounds__(256) void act_prologue_quantize_kernel(const float* __restrict__ x, int64_t k,
-                                                                    int8_t* __restrict__ xq,
+// With FRAG the codes and scales go out in fragment order, one workgroup per
+// row of the padded array (rows past m write zeros).
+template <int PRO, bool FRAG>
+__global__ __launch_bounds__(256) void act_prologue_quantize_kernel(const float* __restrict__ x, int64_t m,
+                                                                    int64_t k, int8_t* __restrict__ xq,
                                                                     uint16_t* __restrict__ xd) {
     const int64_t row = blockIdx.x;
+    const int nb = (int)(k / 32);
+    // fragment order (the int8 matrix core's operand layout, see
+    // q8_prefill_frag.hip): 1 KB per (32-row tile, block), lane i + 32h holding
+    // bytes 16h .. 16h + 15 of row i; scales [tile][block / 4][32][4]; blocks
+    // up to nbp and the rows of the last 64-row group are written too, as zeros
+    const int nbp = (nb + 3) / 4 * 4;
+    const int64_t tile = row >> 5;
+    const int ri = (int)(row & 31);
+    if (FRAG && row >= m) {
+        for (int g = threadIdx.x; g < 4 * nbp; g += 256) {
+            const int b = g >> 2, hh = (g >> 1) & 1;
+            *reinterpret_cast<uint2*>(xq + ((tile * nbp + b) * 64 + hh * 32 + ri) * 16 + 8 * (g & 1)) =
+                make_uint2(0u, 0u);
+            if ((g & 3) == 0) xd[((tile * (nbp / 4) + b / 4) * 32 + ri) * 4 + (b & 3)] = 0;
+        }
+        return;
+    }
     const float* xr = x + row * k;
     const bool one = k <= kStageK;                 // uniform: the row in registers
     float4 sv[1][2];
@@ -181,8 +200,25 @@ __global__ __launch_bounds__(256) void act_prologue_quantize_kernel(const float*
             c[h] = ((uint32_t)block_code(v[4 * h], s) & 0xFFu) | (((uint32_t)block_code(v[4 * h + 1], s) & 0xFFu) << 8) |
                    (((uint32_t)block_code(v[4 * h + 2], s) & 0xFFu) << 16) |
                    ((uint32_t)block_code(v[4 * h + 3], s) << 24);
-        *reinterpret_cast<uint2*>(xq + row * k + 8 * g) = make_uint2(c[0], c[1]);
-        if ((threadIdx.x & 3) == 0) xd[row * (k / 32) + g / 4] = sb;
+        if constexpr (FRAG) {
+            const int64_t b = g >> 2;
+            const int hh = (int)((g >> 1) & 1);
+            *reinterpret_cast<uint2*>(xq + ((tile * nbp + b) * 64 + hh * 32 + ri) * 16 + 8 * (g & 1)) =
+                make_uint2(c[0], c[1]);
+            if ((threadIdx.x & 3) == 0) xd[((tile * (nbp / 4) + b / 4) * 32 + ri) * 4 + (b & 3)] = sb;
+        } else {
+            *reinterpret_cast<uint2*>(xq + row * k + 8 * g) = make_uint2(c[0], c[1]);
+            if ((threadIdx.x & 3) == 0) xd[row * nb + g / 4] = sb;
+        }
+    }
+    if constexpr (FRAG) {
+        // the padding blocks nb .. nbp - 1 of this row
+        for (int g = 4 * nb + threadIdx.x; g < 4 * nbp; g += 256) {
+            const int b = g >> 2, hh = (g >> 1) & 1;
+            *reinterpret_cast<uint2*>(xq + ((tile * nbp + b) * 64 + hh * 32 + ri) * 16 + 8 * (g & 1)) =
+                make_uint2(0u, 0u);
+            if ((g & 3) == 0) xd[((tile * (nbp / 4) + b / 4) * 32 + ri) * 4 + (b & 3)] = 0;
+        }
     }
 }
 
@@ -190,9 +226,20 @@ hipError_t launch_act_prologue_quantize(const float* x, int64_t m, int64_t k, in
                                         uint16_t* xd, hipStream_t stream) {
     (void)hipGetLastError();
     if (pro == kProNorm)
-        act_prologue_quantize_kernel<kProNorm><<<(unsigned)m, 256, 0, stream>>>(x, k, xq, xd);
+        act_prologue_quantize_kernel<kProNorm, false><<<(unsigned)m, 256, 0, stream>>>(x, m, k, xq, xd);
     else
-        act_prologue_quantize_kernel<kProF32><<<(unsigned)m, 256, 0, stream>>>(x, k, xq, xd);
+        act_prologue_quantize_kernel<kProF32, false><<<(unsigned)m, 256, 0, stream>>>(x, m, k, xq, xd);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_prologue_quantize_frag(const float* x, int64_t m, int64_t k, int pro, int8_t* xqf,
+                                             uint16_t* xdf, hipStream_t stream) {
+    (void)hipGetLastError();
+    const int64_t rows = (m + 63) / 64 * 64;       // every row of the fragment array, padding included
+    if (pro == kProNorm)
+        act_prologue_quantize_kernel<kProNorm, true><<<(unsigned)rows, 256, 0, stream>>>(x, m, k, xqf, xdf);
+    else
+        act_prologue_quantize_kernel<kProF32, true><<<(unsigned)rows, 256, 0, stream>>>(x, m, k, xqf, xdf);
     return hipGetLastError();
 }
 

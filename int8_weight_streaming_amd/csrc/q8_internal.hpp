@@ -61,6 +61,10 @@ hipError_t launch_attn_residual(const int8_t* wq, const uint16_t* wd, int64_t n,
                                 int nchunks, float* y, const DeviceInfo& dev, hipStream_t stream);
 hipError_t launch_act_prologue_quantize(const float* x, int64_t m, int64_t k, int pro, int8_t* xq,
                                         uint16_t* xd, hipStream_t stream);
+// The same writing fragment order (q8_prefill_frag.hip's layout), padding
+// rows and blocks included.
+hipError_t launch_act_prologue_quantize_frag(const float* x, int64_t m, int64_t k, int pro, int8_t* xqf,
+                                             uint16_t* xdf, hipStream_t stream);
 
 // int4 weights (two codes per byte, binary16 scale per 32-element block).
 hipError_t launch_q4_quantize(const float* w, int64_t nblocks, uint8_t* q, uint16_t* d,

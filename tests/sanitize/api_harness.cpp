@@ -79,6 +79,10 @@ hipError_t launch_act_prologue_quantize(const float*, int64_t m, int64_t k, int,
                                         hipStream_t) {
     return rec(0, k, m);
 }
+hipError_t launch_act_prologue_quantize_frag(const float*, int64_t m, int64_t k, int, int8_t*, uint16_t*,
+                                             hipStream_t) {
+    return rec(0, k, m);
+}
 hipError_t launch_q4_quantize(const float*, int64_t nblocks, uint8_t*, uint16_t*, const DeviceInfo&,
                               hipStream_t) {
     return rec(nblocks, 32, 0);
@@ -229,6 +233,11 @@ int main() {
     call([&] { return q8_gemm_fused(i8(A), u16(B), 256, 128, 1, 2, A, 3, A, 128, 7, nullptr); }, Q8_OK, true);
     call([&] { return q8_rmsnorm(f32(A), 2, 1536, f32(A), nullptr); }, Q8_OK, true);
     call([&] { return q8_quantize_act_fused(f32(A), 2, 1536, 0, i8(A), u16(B), nullptr); }, Q8_ERR_ENUM, false);
+    call([&] { return q8_quantize_act_fused_frag(f32(A), 37, 1536, 2, i8(A), u16(B), nullptr); }, Q8_OK, true);
+    EXPECT(g_last_rows == 37 && g_last_k == 1536);
+    call([&] { return q8_quantize_act_fused_frag(f32(A), 37, 1536, 3, i8(A), u16(B), nullptr); }, Q8_ERR_ENUM, false);
+    call([&] { return q8_quantize_act_fused_frag(f32(A), 65535LL * 64 + 1, 64, 1, i8(A), u16(B), nullptr); },
+         Q8_ERR_SHAPE, false);
     call([&] { return q4_quantize_weights(f32(A), 3, 64, static_cast<uint8_t*>(A), u16(B), nullptr); }, Q8_OK,
          true);
     call([&] { return q4_gemm_skinny(static_cast<uint8_t*>(A), u16(B), 3, 64, 9, 0, A, nullptr, f32(A), nullptr); },

@@ -140,6 +140,13 @@ def test_frag_sizes_and_validation(lib):
     assert f(A, B, 4, 64, MIS, B, None) == ALIGN
     assert f(A, MIS, 4, 64, A, B, None) == ALIGN
     assert f(None, None, 0, 64, None, None, None) == OK
+    h = lib.q8_quantize_act_fused_frag
+    assert h(A, 4, 64, 0, A, B, None) == ENUM                # the bf16 prologue is not a quantizer input
+    assert h(A, 4, 48, 1, A, B, None) == SHAPE
+    assert h(A, 65535 * 64 + 1, 64, 1, A, B, None) == SHAPE
+    assert h(None, 4, 64, 2, A, B, None) == NULL
+    assert h(A, 4, 64, 2, A, MIS, None) == ALIGN
+    assert h(None, 0, 64, 2, None, None, None) == OK
     g = lib.q8_gemm_prefill_frag
     assert g(A, B, 8, 48, 4, A, B, A, None) == SHAPE
     assert g(A, B, 8, 64, 65535 * 64 + 1, A, B, A, None) == SHAPE

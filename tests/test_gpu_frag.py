@@ -150,6 +150,34 @@ def test_frag_block_sums_bitwise(name, n, k, p, form):
     assert_bitwise(to_host(y), oracle.q8q8(wq, wd, xq, xd), got)
 
 
+@pytest.mark.parametrize("m,k,pro", [(1, 32, q8.PRO_F32), (37, 1536, q8.PRO_RMSNORM), (256, 1536, q8.PRO_RMSNORM),
+                                      (256, 4096, q8.PRO_F32), (65, 2080, q8.PRO_RMSNORM), (64, 96, q8.PRO_F32),
+                                      (130, 8224, q8.PRO_RMSNORM)])
+def test_quantize_act_fused_frag(m, k, pro):
+    """The fused activation quantizer writing fragment order: the oracle's codes
+    and scales of the rows its prologue produces, in the layout of frag_layout,
+    padding rows and blocks zero (k = 8224 is past the one-read row staging).
+    The prologue's rows are the GPU norm's (checked against the oracle in
+    test_gpu_fused) rounded to bf16, or the fp32 rows rounded to bf16."""
+    g = wl.rng(7600 + m + k)
+    h = (g.standard_normal((m, k), dtype=np.float32) * np.float32(3.0)).astype(np.float32)
+    dh = to_dev(h)
+    qf = torch.full((q8.frag_bytes(m, k)[0],), 3, dtype=torch.int8, device="cuda:0")
+    df = torch.full((q8.frag_bytes(m, k)[1] // 2,), 5, dtype=torch.int16, device="cuda:0").view(torch.uint16)
+    f = q8.quantize_act_fused_frag(dh, pro, out=(qf, df))
+    rows = to_host(q8.rmsnorm(dh)) if pro == q8.PRO_RMSNORM else h
+    torch.cuda.synchronize()
+    xq, xd = oracle.quantize_bf16(wl.f32_to_bf16_bits(rows))
+    eq, ed = frag_layout(xq, xd)
+    assert np.array_equal(to_host(f.q), eq), "codes"
+    assert np.array_equal(to_host(f.d), ed), "scales"
+    # the same bytes as the row-major fused quantizer followed by the packing
+    rq, rd = q8.quantize_act_fused(dh, pro)
+    p2 = q8.pack_frag(rq, rd)
+    torch.cuda.synchronize()
+    assert torch.equal(p2.q, f.q) and torch.equal(p2.d.view(torch.int16), f.d.view(torch.int16))
+
+
 def test_frag_reproducible_and_graph_replay():
     n, k, p = 1536, 4096, 256
     wq, wd, xq, xd = _case(7400, n, k, p)
