@@ -144,7 +144,12 @@ template <int PRO, bool FRAG>
 __global__ __launch_bounds__(256) void act_prologue_quantize_kernel(const float* __restrict__ x, int64_t m,
                                                                     int64_t k, int8_t* __restrict__ xq,
                                                                     uint16_t* __restrict__ xd) {
-    const int64_t row = blockIdx.x;
+    // Fragment order: workgroups are dealt round-robin to the eight XCDs, so
+    // rows are mapped to make the 32 rows of a tile (which share every
+    // kilobyte of the fragment array) run on one XCD and meet in its L2:
+    // workgroup j of XCD x takes row 32 (8 (j / 32) + x) + j % 32.
+    const int64_t row = FRAG ? ((int64_t)((blockIdx.x >> 8) * 8 + (blockIdx.x & 7)) * 32 + ((blockIdx.x >> 3) & 31))
+                             : (int64_t)blockIdx.x;
     const int nb = (int)(k / 32);
     // fragment order (the int8 matrix core's operand layout, see
     // q8_prefill_frag.hip): 1 KB per (32-row tile, block), lane i + 32h holding
@@ -153,6 +158,7 @@ __global__ __launch_bounds__(256) void act_prologue_quantize_kernel(const float*
     const int nbp = (nb + 3) / 4 * 4;
     const int64_t tile = row >> 5;
     const int ri = (int)(row & 31);
+    if (FRAG && row >= (m + 63) / 64 * 64) return;     // past the padded array (grid rounded to 256)
     if (FRAG && row >= m) {
         for (int g = threadIdx.x; g < 4 * nbp; g += 256) {
             const int b = g >> 2, hh = (g >> 1) & 1;
@@ -235,7 +241,8 @@ hipError_t launch_act_prologue_quantize(const float* x, int64_t m, int64_t k, in
 hipError_t launch_act_prologue_quantize_frag(const float* x, int64_t m, int64_t k, int pro, int8_t* xqf,
                                              uint16_t* xdf, hipStream_t stream) {
     (void)hipGetLastError();
-    const int64_t rows = (m + 63) / 64 * 64;       // every row of the fragment array, padding included
+    const int64_t rows = (m + 255) / 256 * 256;    // every row of the fragment array, padding included, in
+                                                   // groups of eight tiles (one per XCD)
     if (pro == kProNorm)
         act_prologue_quantize_kernel<kProNorm, true><<<(unsigned)rows, 256, 0, stream>>>(x, m, k, xqf, xdf);
     else
