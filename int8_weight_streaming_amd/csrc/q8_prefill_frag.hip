@@ -303,18 +303,20 @@ int64_t frag_blocks(int64_t k) { return (k / 32 + 3) / 4 * 4; }
 
 // Tile shape and K split, from a sweep of the Mimir shapes at P = 256, 1024
 // and 4096 (graph replay): two weight tiles per wave once that still leaves
-// two wave columns per compute unit, then the smallest split of K over 1, 2, 4
-// or 8 waves that puts at least eight waves of work on every compute unit.
+// two wave columns per compute unit, then the smallest split of K that puts
+// at least eight waves of work on every compute unit.  With one tile per wave
+// there are fewer than four tiles per compute unit, so the split is 4 or 8;
+// with two there are at least two, so it is 1, 2 or 4 -- the five forms
+// compiled below, whatever the compute-unit count.
 FragLayout prefill_frag_layout(int64_t n, int64_t p, int cu_count) {
-    const int64_t ntn = (n + 31) / 32, ntp = (p + 31) / 32;
-    const int wn = (ntn + 1) / 2 * ntp >= 2 * (int64_t)cu_count ? 2 : 1;
+    const int64_t ntn = (n + 31) / 32, ntp = (p + 31) / 32, cus = cu_count;
+    const int wn = (ntn + 1) / 2 * ntp >= 2 * cus ? 2 : 1;
     const int64_t tiles = (ntn + wn - 1) / wn * ntp;
-    int ks = 8;
-    for (int c : {1, 2, 4})
-        if (tiles * c >= 8 * (int64_t)cu_count) {
-            ks = c;
-            break;
-        }
+    int ks;
+    if (wn == 2)
+        ks = tiles >= 8 * cus ? 1 : tiles >= 4 * cus ? 2 : 4;
+    else
+        ks = tiles >= 2 * cus ? 4 : 8;
     const int waves = ks > 4 ? ks : 4;
     const int per_wg = waves / ks;
     const int64_t ntw = (ntn + wn - 1) / wn;
@@ -350,16 +352,11 @@ hipError_t launch_prefill_frag(const int8_t* wf, const uint16_t* wsf, int64_t n,
         switch (L.ks) {
             case 1: return launch_frag_cfg<2, 1>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
             case 2: return launch_frag_cfg<2, 2>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
-            case 4: return launch_frag_cfg<2, 4>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
-            default: return launch_frag_cfg<2, 8>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
+            default: return launch_frag_cfg<2, 4>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
         }
     }
-    switch (L.ks) {
-        case 1: return launch_frag_cfg<1, 1>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
-        case 2: return launch_frag_cfg<1, 2>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
-        case 4: return launch_frag_cfg<1, 4>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
-        default: return launch_frag_cfg<1, 8>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
-    }
+    if (L.ks == 4) return launch_frag_cfg<1, 4>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
+    return launch_frag_cfg<1, 8>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
 }
 
 }  // namespace q8

@@ -6,8 +6,9 @@ q8_gemm_prefill_frag) against the oracle.
   blocks zero).
 * Parity with the fp64 oracle (max-abs 2e-3, relative L2 1e-5) on ragged
   shapes, edge-case weights and the P = 256 workload shapes.
-* The int32 block sums bitwise on every kernel form the dispatch rule reaches
-  on this device, by the power-of-two construction of test_gpu_exact [fak
+* The int32 block sums bitwise on every compiled kernel form (the five the
+  dispatch rule can reach at any compute-unit count), by the power-of-two
+  construction of test_gpu_exact [fak
   MODEL-BASELINE-RESULTS, ACT 4 "Correctness": the tile kernel must equal the
   scalar reference bit for bit, remainder paths included]; each case asserts the
   form its shape selects.
