@@ -227,6 +227,29 @@ def bench_mfma_probe(dev) -> dict:
     return {"TOPS": best, "frac_of_published": best / INT8_PEAK_TOPS, "variants": res}
 
 
+def bench_fold_probe(dev) -> dict:
+    """The exact-fold probe (int8 block sums, scale outer product and fp32 fold
+    of Q8 x Q8 block-tiles, no memory traffic) at one to four waves per SIMD;
+    the fastest median is the measured ceiling of an exact per-block prefill,
+    in the int8 product's operations per second."""
+    import torch
+    from int8_weight_streaming_amd import probe
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = probe.sink(dev)
+    res = {}
+    for wpc in (1, 2, 3, 4):
+        iters = 2000
+        ramp(lambda: probe.fold(cus * wpc, iters, sink))
+        ops = probe.fold(cus * wpc, iters, sink)
+        torch.cuda.synchronize()
+        st = stats(ops / (time_region(lambda i: probe.fold(cus * wpc, iters, sink), 2)[0] * 1e9)
+                   for _ in range(TRIALS))
+        res[f"{wpc}_waves_per_simd_TOPS"] = st
+        log(f"exact-fold probe, {wpc} waves per SIMD: {st['median']:.0f} TOPS")
+    best = max(v["median"] for v in res.values())
+    return {"TOPS": best, "frac_of_published_int8_peak": best / INT8_PEAK_TOPS, "variants": res}
+
+
 def bench_sync_probe(dev) -> dict:
     """What one dependency edge of a decode step costs on this GPU: the
     per-launch cost of an empty kernel under graph replay, and one grid-wide
@@ -580,7 +603,7 @@ def bench_fused_step(q8, wl, dev, weights, t: int) -> dict:
 PREFILL_SWEEP = (16, 64, 256, 1024, 4096)
 
 
-def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP, int8_peak_measured=None) -> dict:
+def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP, int8_peak_measured=None, fold_ceiling=None) -> dict:
     """Q8 x Q8 prefill: qkv and gate_up on [P, 1536] activations, down on
     [P, 4096] (block-0 weights), each product graph-replayed.  The headline
     figures are those of the fragment-order product (weights packed once,
@@ -650,6 +673,7 @@ def bench_prefill(q8, wl, dev, weights, sweep=PREFILL_SWEEP, int8_peak_measured=
         per_p[P] = {"us_three_gemms": tot_us, "int_ops": ops, "TOPS": tops,
                     "frac_int8_peak": tops / INT8_PEAK_TOPS,
                     "frac_measured_int8_peak": tops / int8_peak_measured if int8_peak_measured else None,
+                    "frac_fold_ceiling": tops / fold_ceiling if fold_ceiling else None,
                     "bytes": nbytes, "us_per_token": tot_us / P, "per_gemm": rows,
                     "row_major": {"us_three_gemms": tot_rm, "TOPS": tops_rm,
                                   "frac_int8_peak": tops_rm / INT8_PEAK_TOPS, "per_gemm": rows_rm},
@@ -842,9 +866,13 @@ def summarize(extras: dict, cpu) -> dict:
         s["prefill_p256_frac_int8_peak"] = r4(pf["frac_int8_peak"])
         s["prefill_p256_frac_measured_int8_peak"] = r4(pf["frac_measured_int8_peak"])
         s["prefill_p256_row_major_us"] = r4(pf["row_major"]["us_three_gemms"])
+        if pf.get("frac_fold_ceiling"):
+            s["prefill_p256_frac_fold_ceiling"] = r4(pf["frac_fold_ceiling"])
         p4 = pf.get("p_sweep", {}).get("4096")
         if p4:
             s["prefill_p4096_frac_int8_peak"] = r4(p4["frac_int8_peak"])
+            if p4.get("frac_fold_ceiling"):
+                s["prefill_p4096_frac_fold_ceiling"] = r4(p4["frac_fold_ceiling"])
         if "fit_p_ge_256" in pf:
             s["prefill_fit_fixed_us"] = r4(pf["fit_p_ge_256"]["fixed_us"])
             s["prefill_fit_slope_us_per_token"] = r4(pf["fit_p_ge_256"]["slope_us_per_token"])
@@ -868,6 +896,8 @@ def summarize(extras: dict, cpu) -> dict:
         s["copy_GBps_read_plus_write"] = r4(extras["copy_probe"]["GBps_read_plus_write"])
     if "mfma_i8_probe" in extras:
         s["int8_mfma_measured_TOPS"] = r4(extras["mfma_i8_probe"]["TOPS"])
+    if "fold_probe" in extras:
+        s["exact_fold_ceiling_TOPS"] = r4(extras["fold_probe"]["TOPS"])
     if cpu:
         one = cpu["per_threads"]["1"]
         s["cpu_oracle_1t_lm_head_GBps"] = r4(one["lm_head_gemv_GBps"])
@@ -930,8 +960,9 @@ def main() -> int:
             if name != "o":
                 weights[(0, proj)] = quantize_on_device(
                     q8, wl.normal_weights(wl.mimir_weight_seed(0, proj), n_, k_), dev)
-        res = bench_prefill(q8, wl, dev, weights, sweep=tuple(args.prefill_p))
-        print(json.dumps({"prefill": res, "copy_probe": bench_copy_probe(dev)}), flush=True)
+        fold = bench_fold_probe(dev)
+        res = bench_prefill(q8, wl, dev, weights, sweep=tuple(args.prefill_p), fold_ceiling=fold["TOPS"])
+        print(json.dumps({"prefill": res, "fold_probe": fold, "copy_probe": bench_copy_probe(dev)}), flush=True)
         return 0
 
     if args.lm_head_only:
@@ -993,6 +1024,7 @@ def main() -> int:
     extras["copy_probe"] = bench_copy_probe(dev)
     log(f"copy probe: {extras['copy_probe']['GBps_read_plus_write']:.1f} GB/s (read + write)")
     extras["mfma_i8_probe"] = bench_mfma_probe(dev)
+    extras["fold_probe"] = bench_fold_probe(dev)
 
     if not args.metric_only:
         log("gemv 1536x1536")
@@ -1020,7 +1052,8 @@ def main() -> int:
             extras[f"fused_step_b1_ctx{t}"] = bench_fused_step(q8, wl, dev, weights, t)
         log("prefill P sweep")
         extras["prefill_p256"] = bench_prefill(q8, wl, dev, weights,
-                                               int8_peak_measured=extras["mfma_i8_probe"]["TOPS"])
+                                               int8_peak_measured=extras["mfma_i8_probe"]["TOPS"],
+                                               fold_ceiling=extras["fold_probe"]["TOPS"])
         del weights
         log("decode synchronization probe")
         extras["sync_probe"] = bench_sync_probe(dev)

@@ -62,6 +62,18 @@ int64_t q8_probe_barrier_words(void);
  * operands never produce.  1 <= workgroups <= 2^20, 1 <= iters <= 2^24. */
 q8_status q8_probe_mfma_i8(int workgroups, int iters, int32_t* sink, hipStream_t stream);
 
+/* Exact-fold probe: `workgroups` workgroups of four waves, each wave retiring
+ * `iters` rounds of four Q8 x Q8 block-tiles with no memory traffic -- per
+ * block-tile one v_mfma_i32_32x32x32_i8 (the exact int32 block sums of a
+ * 32 x 32 output tile), one v_mfma_f32_32x32x16_f16 (the tile's scale outer
+ * product) and the fp32 fold (16 converts + 16 FMAs per lane) [fak
+ * MODEL-BASELINE-RESULTS, ACT 4, "How the GEMM was closed": the per-block
+ * fold is what bounds the prefill product].  Counted as the int8 product's
+ * workgroups * 4 * iters * 4 * 65,536 operations, the timed rate is the
+ * ceiling of any prefill kernel that folds exact block sums one block at a
+ * time.  sink and limits as q8_probe_mfma_i8. */
+q8_status q8_probe_fold(int workgroups, int iters, int32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

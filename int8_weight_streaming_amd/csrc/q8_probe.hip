@@ -14,6 +14,9 @@
 //  * int8 matrix-core probe: independent chains of v_mfma_i32_32x32x32_i8 per
 //    wave, so the sustained int8 rate of the chip (at whatever clock it holds
 //    under that load) can be quoted beside the published peak.
+//  * Exact-fold probe: the arithmetic of a Q8 x Q8 block-tile (int8 block
+//    sums, scale outer product, fp32 fold) with no memory traffic, the rate
+//    any exact per-block prefill kernel is bounded by.
 #include "q8probe.h"
 #include "q8_device.hpp"
 
@@ -101,6 +104,62 @@ __global__ __launch_bounds__(256) void probe_mfma_i8_kernel(int iters, int* __re
     if (s == 0x7FEDCBA9 && l == 0) sink[0] = s;
 }
 
+// ---- exact-fold probe
+
+typedef float f32x16p __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8p __attribute__((ext_vector_type(8)));
+
+// The arithmetic of one Q8 x Q8 prefill block-tile with nothing else: the
+// exact int32 block sums (v_mfma_i32_32x32x32_i8), the scale outer product
+// (v_mfma_f32_32x32x16_f16) and the fp32 fold (16 converts + 16 FMAs per
+// lane), the products of block u + 1 issued before block u is folded.  Each
+// wave retires `iters` rounds of four block-tiles; the operands are made
+// opaque every round so nothing is hoisted, and the result is written only in
+// a case the operands never produce.  Timed with one to four workgroups per
+// compute unit it gives the rate at which the chip can retire exact
+// per-block folds -- the ceiling of any prefill kernel that keeps exact int32
+// block sums and folds them in fp32 one block at a time.
+__global__ __launch_bounds__(256) void probe_fold_kernel(int iters, int* __restrict__ sink) {
+    const int l = threadIdx.x & 63;
+    q8::i32x4 a = {l, l + 1, l + 2, l + 3}, b = {l ^ 5, l + 7, 3, l};
+    f16x8p ha, hb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        ha[j] = (_Float16)(l + j);
+        hb[j] = (_Float16)(j - l);
+    }
+    const q8::i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const f32x16p zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    q8::i32x16 c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zi, 0, 0, 0), c1;
+    f32x16p t0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha, hb, zf, 0, 0, 0), t1;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            asm volatile("" : "+v"(a), "+v"(b), "+v"(ha));
+            c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zi, 0, 0, 0);
+            t1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha, hb, zf, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = fmaf((float)c0[r], t0[r], acc[r]);
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" : "+v"(a), "+v"(b), "+v"(hb));
+            c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zi, 0, 0, 0);
+            t0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha, hb, zf, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = fmaf((float)c1[r], t1[r], acc[r]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[r];
+    if (__float_as_int(s) == 0x7FEDCBA9 && l == 0) sink[0] = c0[0];
+}
+
 int cu_count_current() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -150,6 +209,16 @@ extern "C" q8_status q8_probe_barrier(uint32_t* flags, int workgroups, int round
     if (workgroups < 1 || workgroups > cus || workgroups > kBarStride || rounds < 0) return Q8_ERR_SHAPE;
     (void)hipGetLastError();
     probe_barrier_kernel<<<workgroups, 64, 0, stream>>>(flags, rounds);
+    return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ERR_HIP;
+}
+
+extern "C" q8_status q8_probe_fold(int workgroups, int iters, int32_t* sink, hipStream_t stream) {
+    if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24)) return Q8_ERR_SHAPE;
+    if (!sink) return Q8_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(sink) & 3u) return Q8_ERR_ALIGN;
+    if (cu_count_current() <= 0) return Q8_ERR_DEVICE;
+    (void)hipGetLastError();
+    probe_fold_kernel<<<workgroups, 256, 0, stream>>>(iters, sink);
     return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ERR_HIP;
 }
 

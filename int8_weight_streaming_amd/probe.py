@@ -1,6 +1,6 @@
 """ctypes binding of the benchmark's measurement probes (``libq8probe.so``,
-``include/q8probe.h``): the HBM read probe, the grid-barrier probe and the int8
-matrix-core rate probe.  Not part of the computation; only ``bench.py`` and the
+``include/q8probe.h``): the HBM read probe, the grid-barrier probe, the int8
+matrix-core rate probe and the exact-fold probe.  Not part of the computation; only ``bench.py`` and the
 tests load it."""
 from __future__ import annotations
 
@@ -13,7 +13,7 @@ from . import Q8Error, _ptr, _stream, status_str
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 PROBE_LIB_PATH = os.path.join(_HERE, "libq8probe.so")
-EXPORTED = ("q8_probe_read", "q8_probe_barrier", "q8_probe_barrier_words", "q8_probe_mfma_i8")
+EXPORTED = ("q8_probe_read", "q8_probe_barrier", "q8_probe_barrier_words", "q8_probe_mfma_i8", "q8_probe_fold")
 READ_LOADS_PER_THREAD = (4, 8, 12, 16)
 MFMA_I8_OPS = 32 * 32 * 32 * 2           # integer operations of one v_mfma_i32_32x32x32_i8
 
@@ -35,6 +35,8 @@ def load() -> C.CDLL:
     L.q8_probe_barrier_words.restype = I64
     L.q8_probe_mfma_i8.argtypes = [I, I, P, P]
     L.q8_probe_mfma_i8.restype = I
+    L.q8_probe_fold.argtypes = [I, I, P, P]
+    L.q8_probe_fold.restype = I
     _lib = L
     return L
 
@@ -76,3 +78,10 @@ def mfma_i8(workgroups: int, iters: int, sink_t: torch.Tensor) -> int:
     """Enqueue the int8 matrix-core probe; returns its integer operation count."""
     _check("q8_probe_mfma_i8", load().q8_probe_mfma_i8(int(workgroups), int(iters), _ptr(sink_t), _stream()))
     return int(workgroups) * 4 * int(iters) * 8 * MFMA_I8_OPS
+
+
+def fold(workgroups: int, iters: int, sink_t: torch.Tensor) -> int:
+    """Enqueue the exact-fold probe; returns the int8 operation count of the
+    block-tiles it retires."""
+    _check("q8_probe_fold", load().q8_probe_fold(int(workgroups), int(iters), _ptr(sink_t), _stream()))
+    return int(workgroups) * 4 * int(iters) * 4 * MFMA_I8_OPS

@@ -1,6 +1,6 @@
 """The benchmark's measurement probes (libq8probe.so) run to completion: the
 read probe over a buffer for every offered load depth (it writes nothing for
-these buffers), the int8 matrix-core probe, and the grid-barrier probe, whose
+these buffers), the int8 matrix-core and exact-fold probes, and the grid-barrier probe, whose
 rounds all complete on every workgroup (no timeout flagged) and whose
 consecutive calls continue from the epochs the previous call left."""
 import numpy as np
@@ -37,6 +37,14 @@ def test_mfma_probe_runs(probe):
     ops = probe.mfma_i8(16, 100, s)
     torch.cuda.synchronize()
     assert ops == 16 * 4 * 100 * 8 * 65536
+    assert int(s.abs().sum().item()) == 0
+
+
+def test_fold_probe_runs(probe):
+    s = probe.sink(DEV)
+    ops = probe.fold(16, 100, s)
+    torch.cuda.synchronize()
+    assert ops == 16 * 4 * 100 * 4 * 65536
     assert int(s.abs().sum().item()) == 0
 
 
