@@ -66,7 +66,9 @@ q8_status q8_probe_mfma_i8(int workgroups, int iters, int32_t* sink, hipStream_t
  * `iters` rounds of four Q8 x Q8 block-tiles with no memory traffic -- per
  * block-tile one v_mfma_i32_32x32x32_i8 (the exact int32 block sums of a
  * 32 x 32 output tile), one v_mfma_f32_32x32x16_f16 (the tile's scale outer
- * product) and the fp32 fold (16 converts + 16 FMAs per lane) [fak
+ * product) and the fp32 fold (16 exact int-to-float steps + 16 FMAs per lane),
+ * issued as the prefill kernel issues them, on operands that switch like real
+ * data [fak
  * MODEL-BASELINE-RESULTS, ACT 4, "How the GEMM was closed": the per-block
  * fold is what bounds the prefill product].  Counted as the int8 product's
  * workgroups * 4 * iters * 4 * 65,536 operations, the timed rate is the

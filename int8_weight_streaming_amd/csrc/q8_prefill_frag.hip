@@ -100,6 +100,9 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(const int8_t* __restrict
 template <int KS>
 constexpr int frag_waves() { return KS > 4 ? KS : 4; }
 
+constexpr int kFoldBias = 0x4B400000;        // binary32 bits of 1.5 * 2^23
+constexpr float kFoldBiasF = 12582912.0f;    // 1.5 * 2^23
+
 template <int WN, int KS>
 __global__ __launch_bounds__(64 * frag_waves<KS>())
 __attribute__((amdgpu_waves_per_eu(WN == 1 ? 4 : 3, WN == 1 ? 4 : 3)))
@@ -154,21 +157,33 @@ void prefill_frag_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict__
         auto ld_scale = [&](__amdgpu_buffer_rsrc_t r, int st) {
             return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, vs, st * 256, 0));
         };
-        const i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        // The int8 product accumulates onto the bit pattern of 1.5 * 2^23: a
+        // block sum S has |S| <= 32 * 128 * 128 < 2^22, so the int32 result's
+        // bits read as a binary32 number are exactly 1.5 * 2^23 + S, and one
+        // exact subtraction gives float(S) -- an add issues faster than the
+        // int-to-float conversion it replaces, and the fold is bit for bit
+        // the same.
+        i32x16 cb;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cb[r] = kFoldBias;
+        asm volatile("" : "+v"(cb));
         const f32x16 zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        // The scales go out before the codes, in the order a step issues its
+        // loads, so the wait for them at the head of the step loop leaves the
+        // code loads of the step in flight.
         i32x4 a[4], bw[WN][4];
         i32x2 sa, sb[WN], sa_n = {0, 0}, sb_n[WN];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a[u] = ld_code(ra, 4 * s_lo + u);
-#pragma unroll
-            for (int b = 0; b < WN; ++b) bw[b][u] = ld_code(rb[b], 4 * s_lo + u);
-        }
         sa = ld_scale(rsa, s_lo);
 #pragma unroll
         for (int b = 0; b < WN; ++b) {
             sb[b] = ld_scale(rsb[b], s_lo);
             sb_n[b] = (i32x2){0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            a[u] = ld_code(ra, 4 * s_lo + u);
+#pragma unroll
+            for (int b = 0; b < WN; ++b) bw[b][u] = ld_code(rb[b], 4 * s_lo + u);
         }
 
         // One four-block step; with REFILL the next step's scales are fetched
@@ -198,7 +213,7 @@ void prefill_frag_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict__
                 const i32x4 sta = {(u >> 1) ? 0 : hv, (u >> 1) ? hv : 0, 0, 0};
 #pragma unroll
                 for (int b = 0; b < WN; ++b) {
-                    const i32x16 c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[u], bw[b][u], zi, 0, 0, 0);
+                    const i32x16 c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[u], bw[b][u], cb, 0, 0, 0);
                     const f32x16 t = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                         __builtin_bit_cast(f16x8, sta), __builtin_bit_cast(f16x8, stb[b]), zf, 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
@@ -211,7 +226,8 @@ void prefill_frag_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict__
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[b][r] = fmaf((float)c[r], t[r], acc[b][r]);
+                    for (int r = 0; r < 16; ++r)
+                        acc[b][r] = fmaf(__int_as_float(c[r]) - kFoldBiasF, t[r], acc[b][r]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }

@@ -109,48 +109,87 @@ __global__ __launch_bounds__(256) void probe_mfma_i8_kernel(int iters, int* __re
 typedef float f32x16p __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8p __attribute__((ext_vector_type(8)));
 
-// The arithmetic of one Q8 x Q8 prefill block-tile with nothing else: the
-// exact int32 block sums (v_mfma_i32_32x32x32_i8), the scale outer product
-// (v_mfma_f32_32x32x16_f16) and the fp32 fold (16 converts + 16 FMAs per
-// lane), the products of block u + 1 issued before block u is folded.  Each
-// wave retires `iters` rounds of four block-tiles; the operands are made
-// opaque every round so nothing is hoisted, and the result is written only in
-// a case the operands never produce.  Timed with one to four workgroups per
-// compute unit it gives the rate at which the chip can retire exact
-// per-block folds -- the ceiling of any prefill kernel that keeps exact int32
-// block sums and folds them in fp32 one block at a time.
+// A hash of 32-bit words for the probe's operands (an integer finalizer:
+// xor-shift, multiply, xor-shift, multiply, xor-shift).
+__device__ __forceinline__ uint32_t probe_mix(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7feb352dU;
+    x ^= x >> 15;
+    x *= 0x846ca68bU;
+    x ^= x >> 16;
+    return x;
+}
+
+// Four int8 codes in [-127, 127] from one hash.
+__device__ __forceinline__ int probe_codes(uint32_t seed) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) w |= (((probe_mix(seed * 4u + (uint32_t)y) % 255u) - 127u) & 0xFFu) << (8 * y);
+    return (int)w;
+}
+
+// The arithmetic of one Q8 x Q8 prefill block-tile with nothing else, as the
+// prefill kernel issues it: the exact int32 block sums (v_mfma_i32_32x32x32_i8,
+// accumulating onto the bits of 1.5 * 2^23), the scale outer product
+// (v_mfma_f32_32x32x16_f16, one nonzero k slot as in the kernel) and the fp32
+// fold (16 exact subtractions + 16 FMAs per lane), the products of block u + 1
+// issued before block u is folded.  Two operand sets of uniformly distributed
+// codes and positive binary16 scales alternate, so successive products switch
+// like real data (the matrix cores' power, and with it the clock, depends on
+// the operand bits).  Each wave retires `iters` rounds of four block-tiles; the
+// operands are made opaque every round so nothing is hoisted, and the result
+// is written only in a case the operands never produce.  Timed with one to
+// four workgroups per compute unit it gives the rate at which the chip can
+// retire exact per-block folds -- the ceiling of any prefill kernel that keeps
+// exact int32 block sums and folds them in fp32 one block at a time.
 __global__ __launch_bounds__(256) void probe_fold_kernel(int iters, int* __restrict__ sink) {
     const int l = threadIdx.x & 63;
-    q8::i32x4 a = {l, l + 1, l + 2, l + 3}, b = {l ^ 5, l + 7, 3, l};
-    f16x8p ha, hb;
+    const uint32_t g = (uint32_t)(blockIdx.x * 256 + threadIdx.x);
+    q8::i32x4 a[2], b[2];
+    f16x8p ha[2], hb;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        ha[j] = (_Float16)(l + j);
-        hb[j] = (_Float16)(j - l);
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[q][j] = probe_codes(g * 16u + (uint32_t)(q * 4 + j));
+            b[q][j] = probe_codes(0x9E3779B9u ^ (g * 16u + (uint32_t)(q * 4 + j)));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ha[q][j] = (_Float16)0.0f;
+        if (l < 32) ha[q][q] = (_Float16)(1.0f / (float)(1u + probe_mix(g * 2u + (uint32_t)q) % 1000u));
     }
-    const q8::i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        hb[j] = j < 4 ? (_Float16)(1.0f / (float)(1u + probe_mix(0x85EBCA6Bu ^ (g * 8u + (uint32_t)j)) % 1000u))
+                      : (_Float16)0.0f;
+    q8::i32x16 cb;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cb[r] = 0x4B400000;
+    asm volatile("" : "+v"(cb));
     const f32x16p zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float acc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    q8::i32x16 c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zi, 0, 0, 0), c1;
-    f32x16p t0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha, hb, zf, 0, 0, 0), t1;
+    auto fold = [&](const q8::i32x16& c, const f32x16p& t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = fmaf(__int_as_float(c[r]) - 12582912.0f, t[r], acc[r]);
+    };
+    q8::i32x16 c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], b[0], cb, 0, 0, 0), c1;
+    f32x16p t0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[0], hb, zf, 0, 0, 0), t1;
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            asm volatile("" : "+v"(a), "+v"(b), "+v"(ha));
-            c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zi, 0, 0, 0);
-            t1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha, hb, zf, 0, 0, 0);
+            asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(ha[1]));
+            c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[1], b[1], cb, 0, 0, 0);
+            t1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[1], hb, zf, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = fmaf((float)c0[r], t0[r], acc[r]);
+            fold(c0, t0);
             __builtin_amdgcn_sched_barrier(0);
-            asm volatile("" : "+v"(a), "+v"(b), "+v"(hb));
-            c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zi, 0, 0, 0);
-            t0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha, hb, zf, 0, 0, 0);
+            asm volatile("" : "+v"(b[0]), "+v"(b[1]), "+v"(ha[0]));
+            c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], b[0], cb, 0, 0, 0);
+            t0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[0], hb, zf, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = fmaf((float)c1[r], t1[r], acc[r]);
+            fold(c1, t1);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
