@@ -524,7 +524,7 @@ def bench_attn(q8, wl, dev, slabs) -> dict:
     work = torch.empty((q8.attn_work_words(ATTN_HEADS, ATTN_CAP),), dtype=torch.float32, device=dev)
     scale = 1.0 / float(np.sqrt(ATTN_D))
     res = {}
-    for t in (512, 2048, 4096):
+    for t in (256, 512, 2048, 4096):
         cnt = [0]
 
         def call():
@@ -878,7 +878,7 @@ def summarize(extras: dict, cpu) -> dict:
             s["prefill_fit_slope_us_per_token"] = r4(pf["fit_p_ge_256"]["slope_us_per_token"])
     at = extras.get("attn_decode_int8kv")
     if at:
-        for t in ("512", "4096"):
+        for t in ("256", "512", "4096"):
             s[f"attn_t{t}_us"] = r4(at[t]["us_per_call"]["median"])
             s[f"attn_t{t}_frac_hbm"] = r4(at[t]["frac_hbm"])
     lb = extras.get("lm_head_batches")

@@ -236,7 +236,7 @@ q8_status q8_kernel_name(int op, int64_t n, int64_t k, int64_t rows, int act, ch
  * [heads][128].  head_dim must be 128 (Q8_ERR_SHAPE otherwise); 1 <= t <= t_cap
  * <= 2^24 - 128; heads <= 65536 (0 is a no-op); scale finite.
  * `work`: caller-owned fp32 workspace of at least q8_attn_work_words(heads, t)
- * words (0 when t <= 64, and then `work` may be NULL); its contents on entry
+ * words (0 when t <= 256, and then `work` may be NULL); its contents on entry
  * do not matter and are overwritten.  Rows past t are never read.  fp32
  * accumulation; results are bitwise reproducible for a given (heads, t). */
 q8_status q8_attn_decode(const uint16_t* q, const int8_t* kq, const uint16_t* kd,

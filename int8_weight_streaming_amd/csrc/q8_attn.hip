@@ -12,9 +12,11 @@
 // (an int8 KV read per decoded token)].
 //
 // The cache read is the cost (2 x 136 bytes per row and head), so the kernel
-// streams it once: a workgroup takes a chunk of 64 rows of one head up to 512
-// rows of context, 128 up to 2048 and 256 above (more, smaller workgroups
-// measured faster at short contexts, fewer partials to combine at long ones);
+// streams it once: up to 256 rows of context one workgroup takes all rows of a
+// head (64, 128 or 256 of them) and writes the result itself; longer contexts
+// are split into chunks of 64 rows of one head up to 512 rows, 128 up to 2048
+// and 256 above (more, smaller workgroups measured faster at short contexts,
+// fewer partials to combine at long ones);
 // each of its four waves a quarter, lane l the 16-byte segment l % 8
 // (dimensions 16 (l % 8) .. + 15, inside one Q8 block) of rows 8j + l / 8,
 // j < RPL = 2, 4 or 8, for K and V alike, all loads issued before the first
@@ -35,16 +37,20 @@
 namespace q8 {
 
 constexpr int kAttnD = 128;                    // head dimension
+constexpr int64_t kAttnWholeTo = 256;          // contexts up to here: one chunk per head (64, 128 or 256 rows)
 constexpr int64_t kAttnNarrowTo = 512;         // contexts up to here: 64-row chunks (two rows per lane)
 constexpr int64_t kAttnWideFrom = 2048;        // above: 256-row chunks (eight); between: 128 (four)
 constexpr int kAttnPart = kAttnPartFloats;      // floats per (head, chunk): o[128], m, l, 2 pad (16-byte records)
 static_assert(kAttnPartFloats == kAttnD + 4, "partial record layout");
 
-static int64_t attn_chunk_rows(int64_t t) { return t <= kAttnNarrowTo ? 64 : t <= kAttnWideFrom ? 128 : 256; }
+static int64_t attn_chunk_rows(int64_t t) {
+    if (t <= kAttnWholeTo) return t <= 64 ? 64 : t <= 128 ? 128 : 256;
+    return t <= kAttnNarrowTo ? 64 : t <= kAttnWideFrom ? 128 : 256;
+}
 // chunks the split uses for context t
 int64_t attn_split_chunks(int64_t t) { return (t + attn_chunk_rows(t) - 1) / attn_chunk_rows(t); }
-// the most chunks of any context up to t (8 at 512 rows, 16 at 2048), so a
-// workspace sized for the longest context serves every shorter one
+// the most chunks of any context up to t (1 up to 256 rows, 8 at 512, 16 at
+// 2048), so a workspace sized for the longest context serves every shorter one
 static int64_t attn_max_chunks(int64_t t) {
     int64_t c = attn_split_chunks(t);
     if (t > kAttnNarrowTo && c < attn_split_chunks(kAttnNarrowTo)) c = attn_split_chunks(kAttnNarrowTo);

@@ -260,8 +260,9 @@ def test_attn_partials_and_residual_validation(lib):
 
 def test_attn_append_validation(lib):
     f = lib.q8_attn_decode_append
-    need = lib.q8_attn_work_words(2, 200)
-    base = [A, B, A, B, A, 2, 200, 256, 128, 0.088, A, B, A, B, need, None]
+    need = lib.q8_attn_work_words(2, 300)
+    assert need > 0
+    base = [A, B, A, B, A, 2, 300, 400, 128, 0.088, A, B, A, B, need, None]
 
     def call(**kw):
         a = list(base)
@@ -269,7 +270,7 @@ def test_attn_append_validation(lib):
             a[int(i[1:])] = v
         return f(*a)
     assert call(a8=64) == SHAPE                        # head_dim
-    assert call(a6=300) == SHAPE                       # t > t_cap
+    assert call(a6=500) == SHAPE                       # t > t_cap
     assert call(a6=0) == SHAPE
     assert call(a10=None) == NULL                      # knew
     assert call(a11=None) == NULL                      # vnew
@@ -308,19 +309,19 @@ def test_probe_validation():
 
 def test_attn_validation(lib):
     f = lib.q8_attn_decode                                 # prototype set by load_library()
-    need = lib.q8_attn_work_words(2, 200)
-    assert need == 2 * 4 * 132
-    assert lib.q8_attn_work_words(12, 64) == 0 and lib.q8_attn_work_words(12, 65) == 12 * 2 * 132
+    need = lib.q8_attn_work_words(2, 300)
+    assert need == 2 * 5 * 132                             # 64-row chunks above 256 rows
+    assert lib.q8_attn_work_words(12, 256) == 0 and lib.q8_attn_work_words(12, 257) == 12 * 5 * 132
     assert lib.q8_attn_work_words(12, 4096) == 12 * 16 * 132
     assert all(lib.q8_attn_work_words(3, t) <= lib.q8_attn_work_words(3, t + 1) for t in range(1, 4200))
     assert lib.q8_attn_work_words(1, 0) == -1
-    args = lambda **kw: dict(dict(q=A, kq=B, kd=A, vq=B, vd=A, heads=2, t=200, t_cap=256, d=128,
+    args = lambda **kw: dict(dict(q=A, kq=B, kd=A, vq=B, vd=A, heads=2, t=300, t_cap=400, d=128,
                                   scale=0.088, out=A, work=B, words=need), **kw)
     call = lambda a: f(a["q"], a["kq"], a["kd"], a["vq"], a["vd"], a["heads"], a["t"], a["t_cap"],
                        a["d"], a["scale"], a["out"], a["work"], a["words"], None)
     assert call(args(d=64)) == SHAPE
     assert call(args(t=0)) == SHAPE
-    assert call(args(t=300)) == SHAPE                      # t > t_cap
+    assert call(args(t=500)) == SHAPE                      # t > t_cap
     assert call(args(t_cap=1 << 24)) == SHAPE
     assert call(args(scale=float("nan"))) == SHAPE
     assert call(args(scale=float("inf"))) == SHAPE
@@ -329,9 +330,9 @@ def test_attn_validation(lib):
     assert call(args(work=None)) == NULL
     assert call(args(kd=MIS)) == ALIGN
     assert call(args(heads=0, q=None, kq=None, kd=None, vq=None, vd=None, out=None, work=None)) == OK
-    # one chunk: no workspace needed
-    assert call(args(t=64, work=None, words=0)) in (DEVICE, OK)   # one chunk: no workspace
-    assert call(args(t=65, work=None, words=0)) == SHAPE
+    # one chunk (up to 256 rows): no workspace needed
+    assert call(args(t=256, work=None, words=0)) in (DEVICE, OK)
+    assert call(args(t=257, work=None, words=0)) == SHAPE
     import torch
     if not torch.cuda.is_available():
         assert call(args()) == DEVICE
