@@ -381,7 +381,10 @@ q8_status q8_kernel_name(int op, int64_t n, int64_t k, int64_t rows, int act, ch
                       L.xl);
     } else if (op == Q8_OP_PREFILL_FRAG) {
         const q8::FragLayout L = q8::prefill_frag_layout(n, rows, dev->cu_count);
-        std::snprintf(name, sizeof name, "prefill_frag_kernel<%d,%d>", L.wn, L.ks);
+        if (L.wp == 2)
+            std::snprintf(name, sizeof name, "prefill_frag64_kernel");
+        else
+            std::snprintf(name, sizeof name, "prefill_frag_kernel<%d,%d>", L.wn, L.ks);
     } else {
         static const char* const kinds[] = {"prefill_tile64_kernel<1>", "prefill_tile64_kernel<2>",
                                             "prefill_stream_kernel", "prefill_kernel"};

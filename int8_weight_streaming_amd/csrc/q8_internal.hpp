@@ -104,6 +104,7 @@ int64_t frag_blocks(int64_t k);
 struct FragLayout {
     int wn, ks;
     int64_t grid;
+    int wp;        // token tiles per wave: 2 selects the 64 x 64 kernel (wn = 2, ks = 1)
 };
 FragLayout prefill_frag_layout(int64_t n, int64_t p, int cu_count);
 hipError_t launch_pack_frag(const int8_t* q, const uint16_t* d, int64_t rows, int64_t k, int8_t* qf,

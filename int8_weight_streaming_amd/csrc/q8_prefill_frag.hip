@@ -40,7 +40,8 @@
 // the vector ALUs of a SIMD co-issue across those waves.  Workgroups are dealt
 // to the eight XCDs (workgroup id % 8) by column ranges of the weights and walk
 // their tiles token-major, so each XCD's L2 holds its weight columns and
-// fetches every activation tile once.
+// fetches every activation tile once.  Long prompts take a 64 x 64 form of the
+// same loop (prefill_frag64_kernel: two token tiles per wave).
 #include "q8_device.hpp"
 #include "q8_internal.hpp"
 
@@ -301,6 +302,170 @@ void prefill_frag_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict__
     }
 }
 
+
+// The 64 x 64 form for long prompts: a wave owns two token tiles x two weight
+// tiles over all of K, so each block's four operand loads serve four
+// block-tiles (one load per block-tile against 1.5 for the 32 x 64 tile).  The
+// operand registers hold two blocks (a block's registers are reloaded with the
+// block two ahead as soon as its last product pair is issued) and the fold
+// converts the int32 sums directly (the biased accumulator's 16 registers would
+// push the kernel past three waves per SIMD); per output the fold order is the
+// 32 x 64 kernel's with K whole, so the results are the same bits.  Workgroups
+// of four waves, one 64 x 64 tile each, dealt to XCDs by weight columns as
+// above.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void prefill_frag64_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict__ wsf, int64_t n, int nbp,
+                           int64_t p, const i32x4* __restrict__ xf, const i32x2* __restrict__ xsf,
+                           float* __restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int ntn = (int)((n + 31) / 32), ntp = (int)((p + 31) / 32);
+    const int ntw = (ntn + 1) / 2, ntq = (ntp + 1) / 2;   // wave columns and rows of tile pairs
+    const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3;
+    const int c0 = (int)((int64_t)ntw * xcd / 8), nc = (int)((int64_t)ntw * (xcd + 1) / 8) - c0;
+    const int tile = jw * 4 + wave;
+    const bool live = nc > 0 && tile < nc * ntq;
+    // the second tile of a pair exists in the padded fragment arrays (rows64)
+    const int tp0 = live ? (tile / nc) * 2 : 0;
+    const int tn0 = live ? (c0 + tile % nc) * 2 : 0;
+    const int SS = nbp / 4;
+    const int i = lane & 31, h = lane >> 5;
+
+    float acc[2][2][16];                                  // [token tile][weight tile]
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[pp][b][r] = 0.0f;
+
+    if (live && SS > 0) {
+        const char* xb = reinterpret_cast<const char*>(xf);
+        const char* wb = reinterpret_cast<const char*>(wf);
+        const char* xsb = reinterpret_cast<const char*>(xsf);
+        const char* wsb = reinterpret_cast<const char*>(wsf);
+        __amdgpu_buffer_rsrc_t ra[2], rsa[2], rb[2], rsb[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            ra[q] = range_rsrc32(xb + (int64_t)(tp0 + q) * nbp * 1024, nbp * 1024);
+            rsa[q] = range_rsrc32(xsb + (int64_t)(tp0 + q) * SS * 256, SS * 256);
+            rb[q] = range_rsrc32(wb + (int64_t)(tn0 + q) * nbp * 1024, nbp * 1024);
+            rsb[q] = range_rsrc32(wsb + (int64_t)(tn0 + q) * SS * 256, SS * 256);
+        }
+        const int vo = lane * 16, vs = i * 8;
+        auto ld_code = [&](__amdgpu_buffer_rsrc_t r, int blk) {
+            return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, blk * 1024, 0));
+        };
+        auto ld_scale = [&](__amdgpu_buffer_rsrc_t r, int st) {
+            return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, vs, st * 256, 0));
+        };
+        const i32x16 zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        const f32x16 zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        // operand registers of two blocks (slot = block % 2), scales of one step;
+        // the scales go out first
+        i32x4 a[2][2], bw[2][2];
+        i32x2 sa[2], sb[2], sa_n[2], sb_n[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            sa[q] = ld_scale(rsa[q], 0);
+            sb[q] = ld_scale(rsb[q], 0);
+            sa_n[q] = (i32x2){0, 0};
+            sb_n[q] = (i32x2){0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                a[q][u] = ld_code(ra[q], u);
+                bw[q][u] = ld_code(rb[q], u);
+            }
+        auto step = [&](int gs, auto refill_tag) {
+            constexpr bool REFILL = decltype(refill_tag)::value;
+            if constexpr (REFILL) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    sa_n[q] = ld_scale(rsa[q], gs + 1);
+                    sb_n[q] = ld_scale(rsb[q], gs + 1);
+                }
+            }
+            // scale operands as in prefill_frag_kernel
+            i32x4 stb[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) stb[b] = (i32x4){sb[b][0], sb[b][1], 0, 0};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const int xw = (u >> 1) ? sa[pp][1] : sa[pp][0];
+                    const int half = (u & 1) ? (xw & (int)0xFFFF0000u) : (xw & 0xFFFF);
+                    const int hv = h ? 0 : half;
+                    const i32x4 sta = {(u >> 1) ? 0 : hv, (u >> 1) ? hv : 0, 0, 0};
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        const i32x16 c =
+                            __builtin_amdgcn_mfma_i32_32x32x32_i8(a[pp][u & 1], bw[b][u & 1], zi, 0, 0, 0);
+                        const f32x16 t = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(f16x8, sta), __builtin_bit_cast(f16x8, stb[b]), zf, 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (pp == 1 && b == 1 && (REFILL || u < 2)) {     // the block two ahead
+#pragma unroll
+                            for (int q = 0; q < 2; ++q) {
+                                a[q][u & 1] = ld_code(ra[q], 4 * gs + u + 2);
+                                bw[q][u & 1] = ld_code(rb[q], 4 * gs + u + 2);
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[pp][b][r] = fmaf((float)c[r], t[r], acc[pp][b][r]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+            if constexpr (REFILL) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    sa[q] = sa_n[q];
+                    sb[q] = sb_n[q];
+                }
+            }
+        };
+        for (int s = 0; s + 1 < SS; ++s) step(s, std::true_type{});
+        step(SS - 1, std::false_type{});
+    }
+
+    // stores as in prefill_frag_kernel, per token tile
+    if (live) {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            const int64_t prow0 = (int64_t)(tp0 + pp) * 32 + 4 * h;
+            const bool full = (int64_t)(tp0 + pp + 1) * 32 <= p && (int64_t)(tn0 + 2) * 32 <= n;
+            float* const ybase = y + prow0 * n + (int64_t)tn0 * 32 + i;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float* yq = ybase + (int64_t)(8 * q) * n + 32 * b;
+                    const float v0 = acc[pp][b][4 * q], v1 = acc[pp][b][4 * q + 1];
+                    const float v2 = acc[pp][b][4 * q + 2], v3 = acc[pp][b][4 * q + 3];
+                    if (full) {
+                        yq[0] = v0;
+                        yq[n] = v1;
+                        yq[2 * n] = v2;
+                        yq[3 * n] = v3;
+                    } else {
+                        const int64_t row = prow0 + 8 * q, col = (int64_t)(tn0 + b) * 32 + i;
+                        if (col < n) {
+                            if (row < p) yq[0] = v0;
+                            if (row + 1 < p) yq[n] = v1;
+                            if (row + 2 < p) yq[2 * n] = v2;
+                            if (row + 3 < p) yq[3 * n] = v3;
+                        }
+                    }
+                }
+        }
+    }
+}
+
 template <int WN, int KS>
 hipError_t launch_frag_cfg(const int8_t* wf, const uint16_t* wsf, int64_t n, int64_t k, int64_t p,
                            const int8_t* xf, const uint16_t* xsf, float* y, int64_t grid, hipStream_t stream) {
@@ -323,7 +488,9 @@ int64_t frag_blocks(int64_t k) { return (k / 32 + 3) / 4 * 4; }
 // at least eight waves of work on every compute unit.  With one tile per wave
 // there are fewer than four tiles per compute unit, so the split is 4 or 8;
 // with two there are at least two, so it is 1, 2 or 4 -- the five forms
-// compiled below, whatever the compute-unit count.
+// compiled below, whatever the compute-unit count.  With K whole and at least
+// three 64 x 64 tiles per SIMD the two-token-tile kernel takes over (measured
+// at P = 4096: gate_up 138-140 against 149 us, qkv 89-90 against 91-94).
 FragLayout prefill_frag_layout(int64_t n, int64_t p, int cu_count) {
     const int64_t ntn = (n + 31) / 32, ntp = (p + 31) / 32, cus = cu_count;
     const int wn = (ntn + 1) / 2 * ntp >= 2 * cus ? 2 : 1;
@@ -333,16 +500,20 @@ FragLayout prefill_frag_layout(int64_t n, int64_t p, int cu_count) {
         ks = tiles >= 8 * cus ? 1 : tiles >= 4 * cus ? 2 : 4;
     else
         ks = tiles >= 2 * cus ? 4 : 8;
+    const int64_t ntw = (ntn + wn - 1) / wn;
+    // 64 x 64 per wave once that still leaves three waves of work per SIMD
+    const int64_t ntq = (ntp + 1) / 2;
+    const int wp = wn == 2 && ks == 1 && ntw * ntq >= 12 * cus ? 2 : 1;
     const int waves = ks > 4 ? ks : 4;
     const int per_wg = waves / ks;
-    const int64_t ntw = (ntn + wn - 1) / wn;
+    const int64_t rows_w = wp == 2 ? ntq : ntp;
     int64_t maxwg = 0;
     for (int x = 0; x < 8; ++x) {
         const int64_t nc = ntw * (x + 1) / 8 - ntw * x / 8;
-        const int64_t wgs = (nc * ntp + per_wg - 1) / per_wg;
+        const int64_t wgs = (nc * rows_w + per_wg - 1) / per_wg;
         maxwg = wgs > maxwg ? wgs : maxwg;
     }
-    return FragLayout{wn, ks, 8 * maxwg};
+    return FragLayout{wn, ks, 8 * maxwg, wp};
 }
 
 hipError_t launch_pack_frag(const int8_t* q, const uint16_t* d, int64_t rows, int64_t k, int8_t* qf,
@@ -364,6 +535,12 @@ hipError_t launch_prefill_frag(const int8_t* wf, const uint16_t* wsf, int64_t n,
                                hipStream_t stream) {
     (void)hipGetLastError();
     const FragLayout L = prefill_frag_layout(n, p, dev.cu_count);
+    if (L.wp == 2) {
+        prefill_frag64_kernel<<<(unsigned)L.grid, 256, 0, stream>>>(
+            reinterpret_cast<const i32x4*>(wf), reinterpret_cast<const i32x2*>(wsf), n, (int)frag_blocks(k), p,
+            reinterpret_cast<const i32x4*>(xf), reinterpret_cast<const i32x2*>(xsf), y);
+        return hipGetLastError();
+    }
     if (L.wn == 2) {
         switch (L.ks) {
             case 1: return launch_frag_cfg<2, 1>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);

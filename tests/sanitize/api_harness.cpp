@@ -114,7 +114,7 @@ int64_t frag_rows(int64_t rows) { return (rows + 63) / 64 * 64; }
 int64_t frag_blocks(int64_t k) { return (k / 32 + 3) / 4 * 4; }
 FragLayout prefill_frag_layout(int64_t n, int64_t p, int) {
     const int64_t tiles = ((n + 31) / 32) * ((p + 31) / 32);
-    return FragLayout{1, 4, (tiles + 7) / 8 * 8};
+    return FragLayout{1, 4, (tiles + 7) / 8 * 8, 1};
 }
 hipError_t launch_pack_frag(const int8_t*, const uint16_t*, int64_t rows, int64_t k, int8_t*, uint16_t*,
                             const DeviceInfo&, hipStream_t) {

@@ -121,9 +121,10 @@ def test_frag_prefill_p256_config():
 
 def _forms():
     """(name, n, k, p) cases that reach the kernel forms of the dispatch rule
-    (weight tiles per wave, waves per K split) on a 256-CU device, with ragged
-    rows and K: K = 256 splits two steps over four waves (two waves get
-    none); K = 4128 pads 129 blocks to 132."""
+    (weight tiles per wave, waves per K split, and the 64 x 64 kernel for long
+    prompts) on a 256-CU device, with ragged rows and K: K = 256 splits two
+    steps over four waves (two waves get none); K = 4128 pads 129 blocks to
+    132."""
     return [
         ("1 tile, K over 8 waves", 100, 1536, 40, (1, 8)),
         ("1 tile, K over 8 waves, K padded", 70, 4128, 20, (1, 8)),
@@ -134,6 +135,8 @@ def _forms():
         ("2 tiles, K over 2 waves", 2048, 1536, 1024, (2, 2)),
         ("2 tiles, whole K", 2048, 512, 2048, (2, 1)),
         ("2 tiles, whole K, ragged", 2047, 160, 2040, (2, 1)),
+        ("64 x 64 per wave", 2048, 160, 6144, "prefill_frag64_kernel"),
+        ("64 x 64 per wave, ragged", 2043, 96, 6140, "prefill_frag64_kernel"),
     ]
 
 
@@ -143,7 +146,7 @@ def test_frag_block_sums_bitwise(name, n, k, p, form):
     log(f"frag {name} n={n} k={k} p={p}: {got}")
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the shapes are chosen for 256 compute units")
-    assert got == "prefill_frag_kernel<%d,%d>" % form
+    assert got == (form if isinstance(form, str) else "prefill_frag_kernel<%d,%d>" % form)
     wq, wd, xq, xd = q8_pair(7300 + k % 97 + p, n, k, p)
     assert_exact_regime(abs_term_bound(wq, wd, xq, xd), 0.25)
     y = q8.gemm_prefill_frag(pack(wq, wd), pack(xq, xd))
