@@ -212,8 +212,9 @@ q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m,
  * Writes a NUL-terminated name such as "skinny_kernel<1,0,16,2,6>" (batch,
  * activation type, lanes per group, rows per group, chunks per lane) or
  * "prefill_tile64_kernel<2>" or "prefill_frag_kernel<2,4>" (weight tiles per wave,
- * waves per K split) or "prefill_frag64_kernel" (two token tiles and two weight
- * tiles per wave, long prompts) into buf, "none" for an empty call.  Extents are
+ * waves per K split) or "prefill_frag64_kernel<1>" (two token tiles and two
+ * weight tiles per wave, long prompts; waves per K split) into buf, "none" for
+ * an empty call.  Extents are
  * validated as by those calls (Q8_ERR_ENUM, Q8_ERR_SHAPE, Q8_ERR_BATCH); buf
  * NULL gives Q8_ERR_NULL, a name longer than buf_len - 1 bytes Q8_ERR_SHAPE;
  * no device gives Q8_ERR_DEVICE.  Enqueues nothing. */

@@ -382,7 +382,7 @@ q8_status q8_kernel_name(int op, int64_t n, int64_t k, int64_t rows, int act, ch
     } else if (op == Q8_OP_PREFILL_FRAG) {
         const q8::FragLayout L = q8::prefill_frag_layout(n, rows, dev->cu_count);
         if (L.wp == 2)
-            std::snprintf(name, sizeof name, "prefill_frag64_kernel");
+            std::snprintf(name, sizeof name, "prefill_frag64_kernel<%d>", L.ks);
         else
             std::snprintf(name, sizeof name, "prefill_frag_kernel<%d,%d>", L.wn, L.ks);
     } else {

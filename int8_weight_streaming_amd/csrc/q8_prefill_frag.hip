@@ -311,8 +311,11 @@ void prefill_frag_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict__
 // converts the int32 sums directly (the biased accumulator's 16 registers would
 // push the kernel past three waves per SIMD); per output the fold order is the
 // 32 x 64 kernel's with K whole, so the results are the same bits.  Workgroups
-// of four waves, one 64 x 64 tile each, dealt to XCDs by weight columns as
-// above.
+// of four waves, 4 / KS tiles of 64 x 64, dealt to XCDs by weight columns as
+// above.  With KS = 2 the two waves of a tile take half of K each; wave kw
+// stores token tile kw, taking the other wave's partial sums of it through LDS
+// and adding the two in wave order.
+template <int KS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void prefill_frag64_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict__ wsf, int64_t n, int nbp,
                            int64_t p, const i32x4* __restrict__ xf, const i32x2* __restrict__ xsf,
@@ -323,12 +326,14 @@ void prefill_frag64_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict
     const int ntw = (ntn + 1) / 2, ntq = (ntp + 1) / 2;   // wave columns and rows of tile pairs
     const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3;
     const int c0 = (int)((int64_t)ntw * xcd / 8), nc = (int)((int64_t)ntw * (xcd + 1) / 8) - c0;
-    const int tile = jw * 4 + wave;
+    const int tile = jw * (4 / KS) + wave / KS;
     const bool live = nc > 0 && tile < nc * ntq;
     // the second tile of a pair exists in the padded fragment arrays (rows64)
     const int tp0 = live ? (tile / nc) * 2 : 0;
     const int tn0 = live ? (c0 + tile % nc) * 2 : 0;
-    const int SS = nbp / 4;
+    const int kw = wave % KS;
+    const int SS = nbp / 4;                          // four-block steps over K
+    const int s_lo = SS * kw / KS, S = SS * (kw + 1) / KS - s_lo;
     const int i = lane & 31, h = lane >> 5;
 
     float acc[2][2][16];                                  // [token tile][weight tile]
@@ -339,7 +344,7 @@ void prefill_frag64_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[pp][b][r] = 0.0f;
 
-    if (live && SS > 0) {
+    if (live && S > 0) {
         const char* xb = reinterpret_cast<const char*>(xf);
         const char* wb = reinterpret_cast<const char*>(wf);
         const char* xsb = reinterpret_cast<const char*>(xsf);
@@ -367,8 +372,8 @@ void prefill_frag64_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict
         i32x2 sa[2], sb[2], sa_n[2], sb_n[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            sa[q] = ld_scale(rsa[q], 0);
-            sb[q] = ld_scale(rsb[q], 0);
+            sa[q] = ld_scale(rsa[q], s_lo);
+            sb[q] = ld_scale(rsb[q], s_lo);
             sa_n[q] = (i32x2){0, 0};
             sb_n[q] = (i32x2){0, 0};
         }
@@ -376,8 +381,8 @@ void prefill_frag64_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                a[q][u] = ld_code(ra[q], u);
-                bw[q][u] = ld_code(rb[q], u);
+                a[q][u] = ld_code(ra[q], 4 * s_lo + u);
+                bw[q][u] = ld_code(rb[q], 4 * s_lo + u);
             }
         auto step = [&](int gs, auto refill_tag) {
             constexpr bool REFILL = decltype(refill_tag)::value;
@@ -429,14 +434,50 @@ void prefill_frag64_kernel(const i32x4* __restrict__ wf, const i32x2* __restrict
                 }
             }
         };
-        for (int s = 0; s + 1 < SS; ++s) step(s, std::true_type{});
-        step(SS - 1, std::false_type{});
+        for (int s = s_lo; s + 1 < s_lo + S; ++s) step(s, std::true_type{});
+        step(s_lo + S - 1, std::false_type{});
     }
 
-    // stores as in prefill_frag_kernel, per token tile
+    if constexpr (KS == 2) {
+        // wave kw hands its partial sums of token tile 1 - kw to the other wave
+        __shared__ __attribute__((aligned(16))) float4 part[4][2][4][64];   // [wave][b][q][lane]
+        auto put = [&](const float (&t)[2][16]) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    part[wave][b][q][lane] = make_float4(t[b][4 * q], t[b][4 * q + 1], t[b][4 * q + 2], t[b][4 * q + 3]);
+        };
+        if (kw == 0)
+            put(acc[1]);
+        else
+            put(acc[0]);
+        __syncthreads();
+        // token tile kw: the partial of wave 0 first, then that of wave 1
+        auto add = [&](float (&t)[2][16], bool first) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 o = part[wave ^ 1][b][q][lane];
+                    const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        t[b][4 * q + e] = first ? t[b][4 * q + e] + ov[e] : ov[e] + t[b][4 * q + e];
+                }
+        };
+        if (kw == 0)
+            add(acc[0], true);
+        else
+            add(acc[1], false);
+    }
+
+    // stores as in prefill_frag_kernel, per token tile (wave kw of a split
+    // stores token tile kw)
     if (live) {
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
+            if (KS == 2 && pp != kw) continue;
             const int64_t prow0 = (int64_t)(tp0 + pp) * 32 + 4 * h;
             const bool full = (int64_t)(tp0 + pp + 1) * 32 <= p && (int64_t)(tn0 + 2) * 32 <= n;
             float* const ybase = y + prow0 * n + (int64_t)tn0 * 32 + i;
@@ -501,9 +542,19 @@ FragLayout prefill_frag_layout(int64_t n, int64_t p, int cu_count) {
     else
         ks = tiles >= 2 * cus ? 4 : 8;
     const int64_t ntw = (ntn + wn - 1) / wn;
-    // 64 x 64 per wave once that still leaves three waves of work per SIMD
+    // 64 x 64 per wave once that still leaves three waves of work per SIMD,
+    // with K whole or split over two waves
     const int64_t ntq = (ntp + 1) / 2;
-    const int wp = wn == 2 && ks == 1 && ntw * ntq >= 12 * cus ? 2 : 1;
+    int wp = 1;
+    if (wn == 2 && ks <= 2) {
+        if (ntw * ntq >= 12 * cus) {
+            wp = 2;
+            ks = 1;
+        } else if (2 * ntw * ntq >= 12 * cus) {
+            wp = 2;
+            ks = 2;
+        }
+    }
     const int waves = ks > 4 ? ks : 4;
     const int per_wg = waves / ks;
     const int64_t rows_w = wp == 2 ? ntq : ntp;
@@ -536,9 +587,15 @@ hipError_t launch_prefill_frag(const int8_t* wf, const uint16_t* wsf, int64_t n,
     (void)hipGetLastError();
     const FragLayout L = prefill_frag_layout(n, p, dev.cu_count);
     if (L.wp == 2) {
-        prefill_frag64_kernel<<<(unsigned)L.grid, 256, 0, stream>>>(
-            reinterpret_cast<const i32x4*>(wf), reinterpret_cast<const i32x2*>(wsf), n, (int)frag_blocks(k), p,
-            reinterpret_cast<const i32x4*>(xf), reinterpret_cast<const i32x2*>(xsf), y);
+        const auto wa = reinterpret_cast<const i32x4*>(wf);
+        const auto ws = reinterpret_cast<const i32x2*>(wsf);
+        const auto xa = reinterpret_cast<const i32x4*>(xf);
+        const auto xs = reinterpret_cast<const i32x2*>(xsf);
+        const int nbp = (int)frag_blocks(k);
+        if (L.ks == 2)
+            prefill_frag64_kernel<2><<<(unsigned)L.grid, 256, 0, stream>>>(wa, ws, n, nbp, p, xa, xs, y);
+        else
+            prefill_frag64_kernel<1><<<(unsigned)L.grid, 256, 0, stream>>>(wa, ws, n, nbp, p, xa, xs, y);
         return hipGetLastError();
     }
     if (L.wn == 2) {

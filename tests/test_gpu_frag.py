@@ -124,7 +124,7 @@ def _forms():
     (weight tiles per wave, waves per K split, and the 64 x 64 kernel for long
     prompts) on a 256-CU device, with ragged rows and K: K = 256 splits two
     steps over four waves (two waves get none); K = 4128 pads 129 blocks to
-    132."""
+    132; K = 96 is one step, which a two-way split gives to one wave."""
     return [
         ("1 tile, K over 8 waves", 100, 1536, 40, (1, 8)),
         ("1 tile, K over 8 waves, K padded", 70, 4128, 20, (1, 8)),
@@ -135,8 +135,10 @@ def _forms():
         ("2 tiles, K over 2 waves", 2048, 1536, 1024, (2, 2)),
         ("2 tiles, whole K", 2048, 512, 2048, (2, 1)),
         ("2 tiles, whole K, ragged", 2047, 160, 2040, (2, 1)),
-        ("64 x 64 per wave", 2048, 160, 6144, "prefill_frag64_kernel"),
-        ("64 x 64 per wave, ragged", 2043, 96, 6140, "prefill_frag64_kernel"),
+        ("64 x 64 per wave", 2048, 160, 6144, "prefill_frag64_kernel<1>"),
+        ("64 x 64 per wave, ragged", 2043, 96, 6140, "prefill_frag64_kernel<1>"),
+        ("64 x 64 per wave, K over 2 waves", 1536, 160, 4096, "prefill_frag64_kernel<2>"),
+        ("64 x 64 per wave, K over 2 waves, one step", 1530, 96, 4090, "prefill_frag64_kernel<2>"),
     ]
 
 
