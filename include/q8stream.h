@@ -211,7 +211,7 @@ q8_status q8_block_dots(const int8_t* wq, int64_t n, int64_t k, int64_t m,
  * Q8_OP_PREFILL_FRAG: q8_gemm_prefill_frag with p = rows (act ignored).
  * Writes a NUL-terminated name such as "skinny_kernel<1,0,16,2,6>" (batch,
  * activation type, lanes per group, rows per group, chunks per lane) or
- * "prefill_tile64_kernel<2>" or "prefill_frag_kernel<2,4>" (weight tiles per wave,
+ * "prefill_tile64_kernel<2>" or "prefill_frag_kernel<2,2>" (weight tiles per wave,
  * waves per K split) or "prefill_frag64_kernel<1>" (two token tiles and two
  * weight tiles per wave, long prompts; waves per K split) into buf, "none" for
  * an empty call.  Extents are

@@ -523,30 +523,33 @@ hipError_t launch_frag_cfg(const int8_t* wf, const uint16_t* wsf, int64_t n, int
 int64_t frag_rows(int64_t rows) { return (rows + 63) / 64 * 64; }
 int64_t frag_blocks(int64_t k) { return (k / 32 + 3) / 4 * 4; }
 
-// Tile shape and K split, from a sweep of the Mimir shapes at P = 256, 1024
-// and 4096 (graph replay): two weight tiles per wave once that still leaves
-// two wave columns per compute unit, then the smallest split of K that puts
-// at least eight waves of work on every compute unit.  With one tile per wave
-// there are fewer than four tiles per compute unit, so the split is 4 or 8;
-// with two there are at least two, so it is 1, 2 or 4 -- the five forms
-// compiled below, whatever the compute-unit count.  With K whole and at least
-// three 64 x 64 tiles per SIMD the two-token-tile kernel takes over (measured
-// at P = 4096: gate_up 138-140 against 149 us, qkv 89-90 against 91-94).
+// Tile shape and K split, from sweeps of the Mimir shapes at P = 128 .. 4096
+// (graph replay, every form forced on the same box): two weight tiles per wave
+// once that leaves four wave columns of tiles per compute unit, then the
+// smallest split of K that puts enough waves on every compute unit.  With two
+// tiles per wave there are then at least four tiles per compute unit, so the
+// split is 1 or 2; with one, 4 from 1.5 tiles per compute unit, else 8 -- the
+// four forms compiled below, whatever the compute-unit count (at P = 256 qkv
+// 9.75 us with <1,4> against 10.5 with two tiles per wave, down 8.8 against
+// 9.1 with <1,8>).  With at least three 64 x 64 tiles per SIMD the
+// two-token-tile kernel takes over (measured at P = 4096: gate_up 138-140
+// against 149 us, qkv 89-90 against 91-94), also with K split over two waves
+// where whole K would leave fewer.
 FragLayout prefill_frag_layout(int64_t n, int64_t p, int cu_count) {
     const int64_t ntn = (n + 31) / 32, ntp = (p + 31) / 32, cus = cu_count;
-    const int wn = (ntn + 1) / 2 * ntp >= 2 * cus ? 2 : 1;
+    const int wn = (ntn + 1) / 2 * ntp >= 4 * cus ? 2 : 1;
     const int64_t tiles = (ntn + wn - 1) / wn * ntp;
     int ks;
     if (wn == 2)
-        ks = tiles >= 8 * cus ? 1 : tiles >= 4 * cus ? 2 : 4;
+        ks = tiles >= 8 * cus ? 1 : 2;
     else
-        ks = tiles >= 2 * cus ? 4 : 8;
+        ks = 2 * tiles >= 3 * cus ? 4 : 8;
     const int64_t ntw = (ntn + wn - 1) / wn;
     // 64 x 64 per wave once that still leaves three waves of work per SIMD,
     // with K whole or split over two waves
     const int64_t ntq = (ntp + 1) / 2;
     int wp = 1;
-    if (wn == 2 && ks <= 2) {
+    if (wn == 2) {
         if (ntw * ntq >= 12 * cus) {
             wp = 2;
             ks = 1;
@@ -599,11 +602,8 @@ hipError_t launch_prefill_frag(const int8_t* wf, const uint16_t* wsf, int64_t n,
         return hipGetLastError();
     }
     if (L.wn == 2) {
-        switch (L.ks) {
-            case 1: return launch_frag_cfg<2, 1>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
-            case 2: return launch_frag_cfg<2, 2>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
-            default: return launch_frag_cfg<2, 4>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
-        }
+        if (L.ks == 1) return launch_frag_cfg<2, 1>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
+        return launch_frag_cfg<2, 2>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
     }
     if (L.ks == 4) return launch_frag_cfg<1, 4>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);
     return launch_frag_cfg<1, 8>(wf, wsf, n, k, p, xf, xsf, y, L.grid, stream);

@@ -130,8 +130,9 @@ def _forms():
         ("1 tile, K over 8 waves, K padded", 70, 4128, 20, (1, 8)),
         ("1 tile, K over 4 waves", 1536, 256, 384, (1, 4)),
         ("1 tile, K over 4 waves, ragged", 1530, 1536, 370, (1, 4)),
-        ("2 tiles, K over 4 waves", 2048, 256, 512, (2, 4)),
-        ("2 tiles, K over 4 waves, ragged", 2043, 4128, 500, (2, 4)),
+        ("1 tile, K over 4 waves, two steps", 2048, 256, 512, (1, 4)),
+        ("1 tile, K over 4 waves, ragged, K padded", 2043, 4128, 500, (1, 4)),
+        ("2 tiles, K over 2 waves, ragged", 2043, 1056, 1000, (2, 2)),
         ("2 tiles, K over 2 waves", 2048, 1536, 1024, (2, 2)),
         ("2 tiles, whole K", 2048, 512, 2048, (2, 1)),
         ("2 tiles, whole K, ragged", 2047, 160, 2040, (2, 1)),
